@@ -1,0 +1,27 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: long CPU checks (still part of the default run)")
+
+
+@pytest.fixture(scope="session")
+def ora():
+    import oracle
+    oracle.build(force=False)
+    oracle.lib()
+    return oracle
+
+
+@pytest.fixture(scope="session")
+def pins():
+    from tests.pins import load
+    return load()
