@@ -1,0 +1,266 @@
+// The C ABI of libr9k.so: argument checks, the M-based dispatcher and the
+// launches.  Declarations, argument meanings and error behaviour: r9k.h.
+//
+// The dispatcher follows the r9700-stack release v0.3.2 notes ("What changed
+// for someone running it"): the decode (skinny) kernels take up to 255 rows,
+// the tiled fp8 GEMMs everything above; the boundary is a setting, as it is on
+// the pages (R9K_HC_FP8_DECODE_MAXM there, R9K_FP8_SKINNY_MAXM here).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "r9k.h"
+#include "r9k_internal.h"
+
+using namespace r9k;
+
+namespace {
+
+std::atomic<int> g_skinny_max_m{255};
+std::atomic<int> g_engine{R9K_ENGINE_AUTO};
+std::atomic<int> g_qa_inload_max_m{64};
+std::once_flag g_env_once;
+
+void read_env() {
+    std::call_once(g_env_once, [] {
+        if (const char *e = getenv("R9K_FP8_SKINNY_MAXM")) {
+            int v = atoi(e);
+            if (v >= 0) g_skinny_max_m = v;
+        }
+        if (const char *e = getenv("R9K_FP8_ENGINE")) {
+            if (!strcmp(e, "skinny")) g_engine = R9K_ENGINE_SKINNY;
+            else if (!strcmp(e, "tiled")) g_engine = R9K_ENGINE_TILED;
+            else g_engine = R9K_ENGINE_AUTO;
+        }
+        if (const char *e = getenv("R9K_QA_INLOAD_MAXM")) {
+            int v = atoi(e);
+            if (v >= 0) g_qa_inload_max_m = v;
+        }
+    });
+}
+
+// Device check, cached per device id: 1 = gfx950, 2 = not usable.
+constexpr int MAX_DEV = 64;
+std::atomic<int> g_dev_ok[MAX_DEV];
+
+int check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return R9K_ERR_DEVICE;
+    }
+    if (dev < MAX_DEV) {
+        const int st = g_dev_ok[dev].load();
+        if (st == 1) return R9K_OK;
+        if (st == 2) return R9K_ERR_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    int ok = 0;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess) ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    (void)hipGetLastError();
+    if (dev < MAX_DEV) g_dev_ok[dev] = ok ? 1 : 2;
+    return ok ? R9K_OK : R9K_ERR_DEVICE;
+}
+
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+constexpr int64_t MAX_DIM = int64_t(1) << 24;
+
+int check_gemm_shape(int64_t M, int64_t K, int64_t N) {
+    if (M < 0 || K <= 0 || N <= 0 || K % 128 || N % 128) return R9K_ERR_SHAPE;
+    if (M > MAX_DIM || K > MAX_DIM || N > MAX_DIM) return R9K_ERR_SHAPE;
+    return R9K_OK;
+}
+
+int engine_for(int64_t M) {
+    read_env();
+    const int e = g_engine.load();
+    if (e != R9K_ENGINE_AUTO) return e;
+    return M <= g_skinny_max_m.load() ? R9K_ENGINE_SKINNY : R9K_ENGINE_TILED;
+}
+
+// GEMM workspace: [skinny tile counters][skinny split-K partials][A codes][A scales]
+struct GemmWs {
+    size_t counters, part, aq, as, total;
+};
+GemmWs gemm_ws(int64_t M, int64_t K, int64_t N) {
+    GemmWs w;
+    const SkinnyCfg c = skinny_config(M, K, N);
+    w.counters = 0;
+    w.part = skinny_counter_bytes(c, N);
+    w.aq = w.part + skinny_partial_bytes(c, N);
+    w.as = w.aq + align_up((size_t)(M * K), 256);
+    w.total = w.as + align_up((size_t)(M * (K / 128)) * sizeof(float), 256);
+    return w;
+}
+
+int launch_result(hipError_t e) { return e == hipSuccess ? R9K_OK : R9K_ERR_LAUNCH; }
+
+int run_gemm(const uint16_t *a, const uint8_t *aq, const float *as, int64_t M, int64_t K, const uint8_t *w,
+             const float *ws, int64_t N, uint16_t *c, void *workspace, size_t ws_bytes, hipStream_t s) {
+    if (M == 0) return R9K_OK;
+    const GemmWs L = gemm_ws(M, K, N);
+    if (ws_bytes < L.total) return R9K_ERR_WORKSPACE;
+    int rc = check_device();
+    if (rc) return rc;
+    uint8_t *base = (uint8_t *)workspace;
+    const int engine = engine_for(M);
+    if (a && (engine == R9K_ENGINE_TILED || M > g_qa_inload_max_m.load())) {
+        // quantise A once per call into the workspace, then run on codes
+        uint8_t *wq_a = base + L.aq;
+        float *ws_a = (float *)(base + L.as);
+        rc = launch_result(launch_quant_act(a, M, K, wq_a, ws_a, s));
+        if (rc) return rc;
+        a = nullptr;
+        aq = wq_a;
+        as = ws_a;
+    }
+    if (engine == R9K_ENGINE_TILED) {
+        TiledArgs t{aq, as, w, ws, c, M, K, N};
+        return launch_result(launch_gemm_tiled(t, s));
+    }
+    const SkinnyCfg cfg = skinny_config(M, K, N);
+    SkinnyArgs sa{a, aq, as, w, ws, c, (float *)(base + L.part), (uint32_t *)(base + L.counters), M, K, N};
+    return launch_result(launch_gemm_skinny(sa, cfg, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int r9k_abi_version(void) { return R9K_ABI_VERSION; }
+
+const char *r9k_strerror(int code) {
+    switch (code) {
+        case R9K_OK: return "success";
+        case R9K_ERR_NULLPTR: return "a required pointer is NULL";
+        case R9K_ERR_SHAPE: return "a size is out of range";
+        case R9K_ERR_ALIGN: return "a base pointer is not 16-byte aligned";
+        case R9K_ERR_DEVICE: return "no HIP device, or the current device is not gfx950";
+        case R9K_ERR_LAUNCH: return "a kernel launch failed";
+        case R9K_ERR_WORKSPACE: return "the workspace is smaller than required";
+        case R9K_ERR_ARG: return "an enumerated argument has an unknown value";
+        default: return "unknown r9k error code";
+    }
+}
+
+int r9k_quant_act(const uint16_t *a, int64_t M, int64_t K, uint8_t *aq, float *as, void *stream) {
+    if (!a || !aq || !as) return R9K_ERR_NULLPTR;
+    if (M < 0 || K <= 0 || K % 128 || M > MAX_DIM || K > MAX_DIM) return R9K_ERR_SHAPE;
+    if (!aligned16(a) || !aligned16(aq) || !aligned16(as)) return R9K_ERR_ALIGN;
+    if (M == 0) return R9K_OK;
+    if (int rc = check_device()) return rc;
+    return launch_result(launch_quant_act(a, M, K, aq, as, (hipStream_t)stream));
+}
+
+int r9k_quant_weight(const uint16_t *w, int64_t N, int64_t K, uint8_t *wq, float *ws, void *stream) {
+    if (!w || !wq || !ws) return R9K_ERR_NULLPTR;
+    if (N <= 0 || K <= 0 || N % 128 || K % 128 || N > MAX_DIM || K > MAX_DIM) return R9K_ERR_SHAPE;
+    if (!aligned16(w) || !aligned16(wq) || !aligned16(ws)) return R9K_ERR_ALIGN;
+    if (int rc = check_device()) return rc;
+    return launch_result(launch_quant_weight(w, N, K, wq, ws, (hipStream_t)stream));
+}
+
+int r9k_encode_e4m3(const float *x, int64_t n, uint8_t *codes, void *stream) {
+    if (!x || !codes) return R9K_ERR_NULLPTR;
+    if (n < 0 || n > (int64_t(1) << 40)) return R9K_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(codes)) return R9K_ERR_ALIGN;
+    if (n == 0) return R9K_OK;
+    if (int rc = check_device()) return rc;
+    return launch_result(launch_encode_e4m3(x, n, codes, (hipStream_t)stream));
+}
+
+int r9k_gemm_fp8_block_workspace(int64_t M, int64_t K, int64_t N, size_t *bytes) {
+    if (!bytes) return R9K_ERR_NULLPTR;
+    if (int rc = check_gemm_shape(M, K, N)) return rc;
+    *bytes = gemm_ws(M, K, N).total;
+    return R9K_OK;
+}
+
+int r9k_gemm_fp8_block(const uint8_t *aq, const float *as, int64_t M, int64_t K, const uint8_t *w,
+                       const float *ws, int64_t N, uint16_t *c, void *workspace, size_t ws_bytes, void *stream) {
+    if (!aq || !as || !w || !ws || !c || !workspace) return R9K_ERR_NULLPTR;
+    if (int rc = check_gemm_shape(M, K, N)) return rc;
+    if (!aligned16(aq) || !aligned16(as) || !aligned16(w) || !aligned16(ws) || !aligned16(c) || !aligned16(workspace))
+        return R9K_ERR_ALIGN;
+    return run_gemm(nullptr, aq, as, M, K, w, ws, N, c, workspace, ws_bytes, (hipStream_t)stream);
+}
+
+int r9k_gemm_fp8_block_qa(const uint16_t *a, int64_t M, int64_t K, const uint8_t *w, const float *ws, int64_t N,
+                          uint16_t *c, void *workspace, size_t ws_bytes, void *stream) {
+    if (!a || !w || !ws || !c || !workspace) return R9K_ERR_NULLPTR;
+    if (int rc = check_gemm_shape(M, K, N)) return rc;
+    if (!aligned16(a) || !aligned16(w) || !aligned16(ws) || !aligned16(c) || !aligned16(workspace))
+        return R9K_ERR_ALIGN;
+    return run_gemm(a, nullptr, nullptr, M, K, w, ws, N, c, workspace, ws_bytes, (hipStream_t)stream);
+}
+
+int r9k_set_dispatch(int skinny_max_m, int engine) {
+    read_env();
+    if (skinny_max_m < 0) return R9K_ERR_SHAPE;
+    if (engine != R9K_ENGINE_AUTO && engine != R9K_ENGINE_SKINNY && engine != R9K_ENGINE_TILED) return R9K_ERR_ARG;
+    g_skinny_max_m = skinny_max_m;
+    g_engine = engine;
+    return R9K_OK;
+}
+
+int r9k_get_dispatch(int *skinny_max_m, int *engine) {
+    if (!skinny_max_m || !engine) return R9K_ERR_NULLPTR;
+    read_env();
+    *skinny_max_m = g_skinny_max_m.load();
+    *engine = g_engine.load();
+    return R9K_OK;
+}
+
+static int check_moe_shape(int64_t T, int64_t H, int64_t E, int64_t I, int64_t topk) {
+    if (T < 0 || T > 256 || H <= 0 || I <= 0 || H % 128 || I % 128 || E <= 0 || topk < 1 || topk > E)
+        return R9K_ERR_SHAPE;
+    if (T * topk > 4096 || H > MAX_DIM || I > MAX_DIM || E > 65536) return R9K_ERR_SHAPE;
+    return R9K_OK;
+}
+
+int r9k_moe_fp8_decode_workspace(int64_t T, int64_t H, int64_t E, int64_t I, int64_t topk, size_t *bytes) {
+    if (!bytes) return R9K_ERR_NULLPTR;
+    if (int rc = check_moe_shape(T, H, E, I, topk)) return rc;
+    *bytes = moe_layout(T, H, E, I, topk).total;
+    return R9K_OK;
+}
+
+int r9k_moe_ws_offset(int64_t T, int64_t H, int64_t E, int64_t I, int64_t topk, int which, size_t *offset) {
+    if (!offset) return R9K_ERR_NULLPTR;
+    if (int rc = check_moe_shape(T, H, E, I, topk)) return rc;
+    const MoeLayout L = moe_layout(T, H, E, I, topk);
+    switch (which) {
+        case 0: *offset = L.gu; return R9K_OK;
+        case 1: *offset = L.h; return R9K_OK;
+        case 2: *offset = L.y; return R9K_OK;
+        case 3: *offset = L.hq; return R9K_OK;
+        case 4: *offset = L.hs; return R9K_OK;
+    }
+    return R9K_ERR_ARG;
+}
+
+int r9k_moe_fp8_decode(const uint16_t *x, int64_t T, int64_t H, const int32_t *topk_ids, const float *topk_w,
+                       int64_t topk, const uint8_t *w13, const float *w13_s, const uint8_t *w2, const float *w2_s,
+                       int64_t E, int64_t I, uint16_t *out, void *workspace, size_t ws_bytes, int fused,
+                       void *stream) {
+    if (!x || !topk_ids || !topk_w || !w13 || !w13_s || !w2 || !w2_s || !out || !workspace) return R9K_ERR_NULLPTR;
+    if (int rc = check_moe_shape(T, H, E, I, topk)) return rc;
+    if (fused != 0 && fused != 1) return R9K_ERR_ARG;
+    if (!aligned16(x) || !aligned16(topk_ids) || !aligned16(topk_w) || !aligned16(w13) || !aligned16(w13_s) ||
+        !aligned16(w2) || !aligned16(w2_s) || !aligned16(out) || !aligned16(workspace))
+        return R9K_ERR_ALIGN;
+    if (T == 0) return R9K_OK;
+    const MoeLayout L = moe_layout(T, H, E, I, topk);
+    if (ws_bytes < L.total) return R9K_ERR_WORKSPACE;
+    if (int rc = check_device()) return rc;
+    uint8_t *b = (uint8_t *)workspace;
+    MoeArgs a{x, topk_ids, topk_w, w13, w13_s, w2, w2_s, out, (uint16_t *)(b + L.gu), (uint16_t *)(b + L.h),
+              b + L.hq, (float *)(b + L.hs), (float *)(b + L.y), T, H, E, I, topk};
+    return launch_result(launch_moe_decode(a, fused == 1, (hipStream_t)stream));
+}
+
+}  // extern "C"

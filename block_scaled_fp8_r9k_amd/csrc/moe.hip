@@ -1,0 +1,332 @@
+// Engine (c): routed MoE decode with block-scaled fp8 experts.
+//
+// The r9700-stack release v0.3.3 notes ("What changed for someone running it")
+// describe the fused MoE decode path: silu(gate) * up in the gate_up GEMM's
+// epilogue and the fp8 row quant inside the down GEMM's A-load, bit-identical
+// to the three-launch path (gate_up GEMM, silu*up with the quant, down GEMM).
+// Both paths are here; both end with the weighted combine over the top-k.
+//
+// Decode MoE is a weight stream over the experts the tokens touch.  Every
+// kernel's grid covers all E experts (it never depends on routing data); a
+// CTA first collects, in ascending order, the (token, slot) pairs routed to its
+// expert, and leaves at once if there are none.  The pairs are the rows of a
+// skinny GEMM against that expert's weights, organised like the dense skinny
+// engine: weight bytes straight into MFMA registers with 16-byte loads, the
+// pairs' activation codes in LDS, one e4m3 16x16x128 MFMA per 16x16 tile and
+// K-group, promotion acc += P * as * ws per group.
+//   gate_up: CTA = (expert, 128-column tile j); each wave holds gate columns
+//            [128 j + 32 w, +32) and the matching up columns I + the same, so
+//            its lanes own gate and up of the same (pair, column).
+//   down:    CTA = (expert, 128-column tile of H).
+// A pair p = t * topk + j is a row everywhere; intermediates are indexed by p.
+#include "r9k_device.h"
+#include "r9k_internal.h"
+
+namespace r9k {
+
+namespace {
+
+enum Mode { GATEUP_STORE = 0, GATEUP_SILU = 1, DOWN_QUANT = 2, DOWN_CODES = 3 };
+
+constexpr int MAX_PAIRS = 4096;
+
+// silu(g) * u in fp32, rounded to bf16: the single definition both paths use.
+__device__ __forceinline__ uint32_t silu_mul_bf16(float g, float u) {
+    const float sg = g / (1.0f + expf(-g));
+    return bf16_rne(sg * u);
+}
+
+// Collect the pairs routed to expert e, ascending, into list[]; returns count.
+__device__ int gather_pairs(const int32_t *ids, int P, int e, int *list, int *wave_cnt) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int base = 0;
+    for (int c0 = 0; c0 < P; c0 += 256) {
+        const int idx = c0 + tid;
+        const bool hit = idx < P && ids[idx] == e;
+        const unsigned long long bal = __ballot(hit);
+        if (lane == 0) wave_cnt[wave] = __popcll(bal);
+        __syncthreads();
+        int off = base;
+        for (int w = 0; w < wave; ++w) off += wave_cnt[w];
+        if (hit) {
+            off += __popcll(bal & ((1ull << lane) - 1ull));
+            list[off] = idx;
+        }
+        int tot = 0;
+        for (int w = 0; w < 4; ++w) tot += wave_cnt[w];
+        base += tot;
+        __syncthreads();
+    }
+    return base;
+}
+
+template <int KC, int NCT>
+struct MoeSmem {
+    static constexpr int PITCH = KC * 128 + 16;
+    uint8_t codes[16 * PITCH];
+    float scales[KC * 16];
+};
+
+}  // namespace
+
+// One expert GEMM pass.  NCT = column tiles of 16 per wave (4 for gate_up:
+// 2 gate + 2 up, 2 for down).  Rows are the expert's pairs in tiles of 16.
+template <int MODE, int KC>
+__global__ __launch_bounds__(256) void k_moe_gemm(MoeArgs p) {
+    constexpr bool GATEUP = MODE == GATEUP_STORE || MODE == GATEUP_SILU;
+    constexpr int NCT = GATEUP ? 4 : 2;
+    constexpr int PITCH = MoeSmem<KC, NCT>::PITCH;
+    __shared__ MoeSmem<KC, NCT> sm;
+    __shared__ int list[MAX_PAIRS];
+    __shared__ int wave_cnt[4];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, q = lane >> 4;
+    const int64_t H = p.H, I = p.I, topk = p.topk;
+    const int P = (int)(p.T * topk);
+    const int64_t K = GATEUP ? H : I;          // contraction length
+    const int64_t G = K / 128;
+    const int64_t ntile = GATEUP ? I / 128 : H / 128;
+    const int e = (int)(blockIdx.x / ntile);
+    const int64_t j = blockIdx.x % ntile;
+
+    const int cnt = gather_pairs(p.ids, P, e, list, wave_cnt);
+    if (cnt == 0) return;
+
+    // weight rows this lane streams, per column tile c
+    const uint8_t *wbase;
+    const float *wsbase;
+    int64_t wrow[NCT];
+    if (GATEUP) {
+        wbase = p.w13 + (int64_t)e * 2 * I * H;
+        wsbase = p.w13s + (int64_t)e * (2 * I / 128) * G;
+#pragma unroll
+        for (int c = 0; c < NCT; ++c)
+            wrow[c] = (c < 2 ? 128 * j : I + 128 * j) + wave * 32 + 16 * (c & 1) + l16;
+    } else {
+        wbase = p.w2 + (int64_t)e * H * I;
+        wsbase = p.w2s + (int64_t)e * (H / 128) * G;
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) wrow[c] = 128 * j + wave * 32 + 16 * c + l16;
+    }
+    const float *ws_gate = wsbase + j * G;                       // block row of the gate / down tile
+    const float *ws_up = GATEUP ? wsbase + (I / 128 + j) * G : ws_gate;
+
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    const int nb = (int)(G / KC);
+    for (int r0 = 0; r0 < cnt; r0 += 16) {
+        const int rows = min(16, cnt - r0);
+        v4f acc[NCT];
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) acc[c] = zero;
+
+        for (int b = 0; b < nb; ++b) {
+            const int64_t g0 = (int64_t)b * KC;
+            __syncthreads();  // LDS free (previous batch / row tile done)
+
+            // activation side: QA modes quantise a bf16 row group per 16 lanes
+            constexpr bool QA = MODE != DOWN_CODES;
+            const int task = tid >> 4;  // 16 row groups per pass, KC passes cover 16 rows x KC groups
+            uint4 avs[KC];
+            if (QA) {
+#pragma unroll
+                for (int it = 0; it < KC; ++it) {
+                    const int tk = task + 16 * it;  // tk = row * KC + g
+                    if (tk < rows * KC) {
+                        const int r = tk / KC, g = tk % KC;
+                        const int pr = list[r0 + r];
+                        const uint16_t *src = GATEUP ? p.x + (int64_t)(pr / topk) * H : p.h + (int64_t)pr * I;
+                        avs[it] = *(const uint4 *)(src + (g0 + g) * 128 + l16 * 8);
+                    }
+                }
+            }
+
+            uint4 wr[KC][NCT][2];
+#pragma unroll
+            for (int g = 0; g < KC; ++g)
+#pragma unroll
+                for (int c = 0; c < NCT; ++c) {
+                    const uint8_t *src = wbase + wrow[c] * K + (g0 + g) * 128 + 16 * q;
+                    wr[g][c][0] = load_nt16(src);
+                    wr[g][c][1] = load_nt16(src + 64);
+                }
+
+            // zero rows past the pair count, then fill the valid rows
+            for (int i = tid; i < (16 - rows) * KC * 8; i += 256) {
+                const int r = rows + i / (KC * 8), c16 = i % (KC * 8);
+                *(uint4 *)&sm.codes[r * PITCH + c16 * 16] = make_uint4(0, 0, 0, 0);
+            }
+            for (int i = tid; i < (16 - rows) * KC; i += 256) sm.scales[(i % KC) * 16 + rows + i / KC] = 0.0f;
+            if (QA) {
+#pragma unroll
+                for (int it = 0; it < KC; ++it) {
+                    const int tk = task + 16 * it;
+                    if (tk < rows * KC) {
+                        const int r = tk / KC, g = tk % KC;
+                        float s;
+                        const uint2 codes = quant_group16(avs[it], s);
+                        *(uint2 *)&sm.codes[r * PITCH + g * 128 + l16 * 8] = codes;
+                        if (l16 == 0) sm.scales[g * 16 + r] = s;
+                    }
+                }
+            } else {
+                for (int i = tid; i < rows * KC * 8; i += 256) {
+                    const int r = i / (KC * 8), c16 = i % (KC * 8);
+                    const int pr = list[r0 + r];
+                    *(uint4 *)&sm.codes[r * PITCH + c16 * 16] =
+                        *(const uint4 *)(p.hq + (int64_t)pr * I + g0 * 128 + c16 * 16);
+                }
+                for (int i = tid; i < rows * KC; i += 256) {
+                    const int r = i / KC, g = i % KC;
+                    sm.scales[g * 16 + r] = p.hs[(int64_t)list[r0 + r] * G + g0 + g];
+                }
+            }
+            __syncthreads();
+
+#pragma unroll
+            for (int g = 0; g < KC; ++g) {
+                const uint8_t *ap = &sm.codes[l16 * PITCH + g * 128 + 16 * q];
+                const v8i af = make_frag(*(const uint4 *)ap, *(const uint4 *)(ap + 64));
+                const float sa = sm.scales[g * 16 + l16];
+                const float sc_g = sa * ws_gate[g0 + g];
+                const float sc_u = sa * ws_up[g0 + g];
+#pragma unroll
+                for (int c = 0; c < NCT; ++c) {
+                    const v4f pr = mfma_e4m3_16x16x128(make_frag(wr[g][c][0], wr[g][c][1]), af, zero);
+                    const float sc = (GATEUP && c >= 2) ? sc_u : sc_g;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[c][i] = __builtin_fmaf(pr[i], sc, acc[c][i]);
+                }
+            }
+        }
+
+        // epilogue: lane holds rows (pairs) list[r0 + l16], columns 4q + i of each tile c
+        if (l16 < rows) {
+            const int64_t pr = list[r0 + l16];
+            if (MODE == GATEUP_STORE) {
+#pragma unroll
+                for (int c = 0; c < NCT; ++c) {
+                    const int64_t n = wrow[c] - l16 + 4 * q;  // first of the lane's 4 columns
+                    *(uint2 *)(p.gu + pr * 2 * I + n) = bf16x4_rne(acc[c][0], acc[c][1], acc[c][2], acc[c][3]);
+                }
+            } else if (MODE == GATEUP_SILU) {
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    uint32_t hb[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float g = __uint_as_float(bf16_rne(acc[c][i]) << 16);
+                        const float u = __uint_as_float(bf16_rne(acc[c + 2][i]) << 16);
+                        hb[i] = silu_mul_bf16(g, u);
+                    }
+                    const int64_t n = wrow[c] - l16 + 4 * q;
+                    *(uint2 *)(p.h + pr * I + n) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < NCT; ++c) {
+                    const int64_t n = wrow[c] - l16 + 4 * q;
+                    *(v4f *)(p.y + pr * H + n) = acc[c];
+                }
+            }
+        }
+    }
+}
+
+// Three-launch path, middle launch: h = bf16(silu(gate) * up) from the stored
+// bf16 gu, then h's group-128 quant.  16 lanes per group, 16 groups per block.
+__global__ __launch_bounds__(256) void k_moe_silu_quant(MoeArgs p) {
+    const int64_t I = p.I, GI = I / 128;
+    const int64_t P = p.T * p.topk;
+    const int64_t gid = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const int l = threadIdx.x & 15;
+    if (gid >= P * GI) return;
+    const int64_t pr = gid / GI, g = gid % GI;
+    const uint4 gv = *(const uint4 *)(p.gu + pr * 2 * I + g * 128 + l * 8);
+    const uint4 uv = *(const uint4 *)(p.gu + pr * 2 * I + I + g * 128 + l * 8);
+    uint4 hv;
+    hv.x = silu_mul_bf16(bf16_lo(gv.x), bf16_lo(uv.x)) | (silu_mul_bf16(bf16_hi(gv.x), bf16_hi(uv.x)) << 16);
+    hv.y = silu_mul_bf16(bf16_lo(gv.y), bf16_lo(uv.y)) | (silu_mul_bf16(bf16_hi(gv.y), bf16_hi(uv.y)) << 16);
+    hv.z = silu_mul_bf16(bf16_lo(gv.z), bf16_lo(uv.z)) | (silu_mul_bf16(bf16_hi(gv.z), bf16_hi(uv.z)) << 16);
+    hv.w = silu_mul_bf16(bf16_lo(gv.w), bf16_lo(uv.w)) | (silu_mul_bf16(bf16_hi(gv.w), bf16_hi(uv.w)) << 16);
+    *(uint4 *)(p.h + pr * I + g * 128 + l * 8) = hv;
+    float s;
+    const uint2 codes = quant_group16(hv, s);
+    *(uint2 *)(p.hq + pr * I + g * 128 + l * 8) = codes;
+    if (l == 0) p.hs[pr * GI + g] = s;
+}
+
+// out[t][n] = bf16(sum_j w[t][j] * y[t*topk + j][n]), j ascending, fp32 fma.
+// Pairs whose expert id is out of range contribute nothing.  4 columns per thread.
+__global__ __launch_bounds__(256) void k_moe_combine(MoeArgs p) {
+    const int64_t H = p.H, topk = p.topk;
+    const int64_t t = blockIdx.y;
+    const int64_t n = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (n >= H) return;
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t jj = 0; jj < topk; ++jj) {
+        const int64_t pr = t * topk + jj;
+        const int32_t e = p.ids[pr];
+        if (e < 0 || e >= p.E) continue;
+        const float w = p.tw[pr];
+        const v4f y = *(const v4f *)(p.y + pr * H + n);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(w, y[i], acc[i]);
+    }
+    *(uint2 *)(p.out + t * H + n) = bf16x4_rne(acc[0], acc[1], acc[2], acc[3]);
+}
+
+MoeLayout moe_layout(int64_t T, int64_t H, int64_t E, int64_t I, int64_t topk) {
+    (void)E;
+    const size_t P = (size_t)(T * topk);
+    MoeLayout L;
+    size_t off = 0;
+    L.gu = off; off = align_up(off + P * 2 * I * 2, 256);
+    L.h = off;  off = align_up(off + P * I * 2, 256);
+    L.hq = off; off = align_up(off + P * I, 256);
+    L.hs = off; off = align_up(off + P * (I / 128) * 4, 256);
+    L.y = off;  off = align_up(off + P * H * 4, 256);
+    L.total = off;
+    return L;
+}
+
+template <int MODE>
+static hipError_t launch_gemm_mode(const MoeArgs &a, hipStream_t s) {
+    constexpr bool GATEUP = MODE == GATEUP_STORE || MODE == GATEUP_SILU;
+    const int64_t G = (GATEUP ? a.H : a.I) / 128;
+    const int64_t ntile = GATEUP ? a.I / 128 : a.H / 128;
+    const dim3 grid((unsigned)(a.E * ntile));
+    // the largest K batch within the register budget that divides K/128
+    const int kcmax = GATEUP ? 4 : 8;
+    int kc = 1;
+    for (int cand : {8, 6, 4, 3, 2, 1})
+        if (cand <= kcmax && G % cand == 0) { kc = cand; break; }
+    switch (kc) {
+        case 8: if constexpr (!GATEUP) { hipLaunchKernelGGL((k_moe_gemm<MODE, 8>), grid, dim3(256), 0, s, a); break; }
+                return hipErrorInvalidValue;
+        case 6: if constexpr (!GATEUP) { hipLaunchKernelGGL((k_moe_gemm<MODE, 6>), grid, dim3(256), 0, s, a); break; }
+                return hipErrorInvalidValue;
+        case 4: hipLaunchKernelGGL((k_moe_gemm<MODE, 4>), grid, dim3(256), 0, s, a); break;
+        case 3: hipLaunchKernelGGL((k_moe_gemm<MODE, 3>), grid, dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((k_moe_gemm<MODE, 2>), grid, dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL((k_moe_gemm<MODE, 1>), grid, dim3(256), 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_moe_decode(const MoeArgs &a, bool fused, hipStream_t s) {
+    hipError_t e;
+    if (fused) {
+        if ((e = launch_gemm_mode<GATEUP_SILU>(a, s)) != hipSuccess) return e;
+        if ((e = launch_gemm_mode<DOWN_QUANT>(a, s)) != hipSuccess) return e;
+    } else {
+        if ((e = launch_gemm_mode<GATEUP_STORE>(a, s)) != hipSuccess) return e;
+        const int64_t ngroups = a.T * a.topk * (a.I / 128);
+        hipLaunchKernelGGL(k_moe_silu_quant, dim3((unsigned)((ngroups + 15) / 16)), dim3(256), 0, s, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = launch_gemm_mode<DOWN_CODES>(a, s)) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((a.H / 4 + 255) / 256), (unsigned)a.T), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace r9k

@@ -1,0 +1,92 @@
+// Quantisation kernels: activation groups of 128 (per token along K), weight
+// blocks of 128x128, and the elementwise e4m3 encoder.
+//
+// Activation quant is the per-token-group-128 quant of the r9700-stack release
+// v0.3.1 ("What changed for someone running it"), here as its own launch (the
+// split form); weight quant is the load-time conversion of release v0.3.2
+// (same section).  All three are HBM-bound streaming kernels: 16 lanes share
+// one group, each lane moving 16 bytes of bf16 in and 8 bytes of codes out.
+#include "r9k_device.h"
+#include "r9k_internal.h"
+
+namespace r9k {
+
+// Group gid covers bf16 [gid*128, gid*128 + 128) of the row-major [M][K]
+// array (row m, group g has gid = m*K/128 + g), which is also where its codes
+// go; its scale goes to as[gid].  16 groups per 256-thread block.
+__global__ __launch_bounds__(256) void k_quant_act(const uint4 *__restrict__ a, uint2 *__restrict__ aq,
+                                                   float *__restrict__ as, int64_t ngroups) {
+    const int64_t gid = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const int l = threadIdx.x & 15;
+    if (gid >= ngroups) return;  // uniform across the 16 lanes of a group
+    uint4 v = load_nt16(a + gid * 16 + l);
+    float s;
+    uint2 q = quant_group16(v, s);
+    aq[gid * 16 + l] = q;
+    if (l == 0) as[gid] = s;
+}
+
+hipError_t launch_quant_act(const uint16_t *a, int64_t M, int64_t K, uint8_t *aq, float *as, hipStream_t s) {
+    int64_t ngroups = M * (K / 128);
+    int64_t blocks = (ngroups + 15) / 16;
+    hipLaunchKernelGGL(k_quant_act, dim3((unsigned)blocks), dim3(256), 0, s, (const uint4 *)a, (uint2 *)aq, as,
+                       ngroups);
+    return hipGetLastError();
+}
+
+// One 256-thread block per 128x128 weight block (grid: K/128 x N/128).
+// Thread t handles rows t/16 + 16 i (i = 0..7) and columns 8 (t % 16) .. +7.
+__global__ __launch_bounds__(256) void k_quant_weight(const uint16_t *__restrict__ w, int64_t K,
+                                                      uint8_t *__restrict__ wq, float *__restrict__ ws) {
+    const int64_t bk = blockIdx.x, bn = blockIdx.y;
+    const int t = threadIdx.x;
+    const int r0 = t >> 4, col = (t & 15) * 8;
+    const uint16_t *blk = w + (bn * 128) * K + bk * 128 + col;
+    uint4 v[8];
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        v[i] = *(const uint4 *)(blk + (int64_t)(r0 + 16 * i) * K);
+        m = max(m, absmax8_bits(v[i]));
+    }
+    m = max16_dpp(m);
+    __shared__ uint32_t red[16];
+    if ((t & 15) == 0) red[t >> 4] = m;
+    __syncthreads();
+    uint32_t mm = red[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mm = max(mm, red[i]);
+    const float s = group_scale(__uint_as_float(mm << 16));
+    const float r = 1.0f / s;
+    uint8_t *qb = wq + (bn * 128) * K + bk * 128 + col;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *(uint2 *)(qb + (int64_t)(r0 + 16 * i) * K) = quant8(v[i], s, r);
+    if (t == 0) ws[bn * (K / 128) + bk] = s;
+}
+
+hipError_t launch_quant_weight(const uint16_t *w, int64_t N, int64_t K, uint8_t *wq, float *ws, hipStream_t s) {
+    hipLaunchKernelGGL(k_quant_weight, dim3((unsigned)(K / 128), (unsigned)(N / 128)), dim3(256), 0, s, w, K, wq,
+                       ws);
+    return hipGetLastError();
+}
+
+// Elementwise encoder: 4 values per thread, scalar tail.
+__global__ __launch_bounds__(256) void k_encode_e4m3(const float *__restrict__ x, int64_t n,
+                                                     uint8_t *__restrict__ out) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i + 4 <= n) {
+        float4 v = *(const float4 *)(x + i);
+        *(uint32_t *)(out + i) = e4m3x4(v.x, v.y, v.z, v.w);
+    } else {
+        for (int64_t j = i; j < n; ++j) out[j] = (uint8_t)(e4m3x4(x[j], 0.0f, 0.0f, 0.0f) & 0xFFu);
+    }
+}
+
+hipError_t launch_encode_e4m3(const float *x, int64_t n, uint8_t *codes, hipStream_t s) {
+    int64_t threads = (n + 3) / 4;
+    int64_t blocks = (threads + 255) / 256;
+    hipLaunchKernelGGL(k_encode_e4m3, dim3((unsigned)blocks), dim3(256), 0, s, x, n, codes);
+    return hipGetLastError();
+}
+
+}  // namespace r9k

@@ -1,0 +1,81 @@
+// Host-side interfaces between the C ABI (api.hip) and the kernel files.
+// Every launcher enqueues on `stream` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace r9k {
+
+// ---- quantisation (quant.hip) ----
+hipError_t launch_quant_act(const uint16_t *a, int64_t M, int64_t K, uint8_t *aq, float *as, hipStream_t s);
+hipError_t launch_quant_weight(const uint16_t *w, int64_t N, int64_t K, uint8_t *wq, float *ws, hipStream_t s);
+hipError_t launch_encode_e4m3(const float *x, int64_t n, uint8_t *codes, hipStream_t s);
+
+// ---- skinny weight-streaming engine (gemm_skinny.hip) ----
+// One CTA covers 128 output columns (one weight block row), mt16 * 16 rows of
+// A (a chunk of at most 256 rows) and kc K-groups; `ksplit` CTAs share a tile
+// and reduce their fp32 partials in a fixed order (the last one to finish).
+struct SkinnyCfg {
+    int mt16;    // row tiles of 16 per CTA: 1, 2, 4, 8 or 16
+    int kc;      // K-groups (of 128) per batch: the weight bytes one CTA holds in flight
+    int ksplit;  // CTAs sharing an output tile along K
+    int nb;      // batches per CTA; kc * ksplit * nb = K/128
+    int mchunks; // ceil(M / (16 * mt16))
+};
+SkinnyCfg skinny_config(int64_t M, int64_t K, int64_t N);
+// Workspace the skinny engine needs for this config: tile counters, then partials.
+size_t skinny_counter_bytes(const SkinnyCfg &c, int64_t N);
+size_t skinny_partial_bytes(const SkinnyCfg &c, int64_t N);
+
+struct SkinnyArgs {
+    const uint16_t *a;  // bf16 activations when quantising in the A-load, else NULL
+    const uint8_t *aq;  // fp8 activation codes when pre-quantised
+    const float *as;    // their scales [M][K/128]
+    const uint8_t *w;
+    const float *ws;
+    uint16_t *c;
+    float *part;        // split-K partials
+    uint32_t *counters; // split-K tile counters (zero between calls)
+    int64_t M, K, N;
+};
+hipError_t launch_gemm_skinny(const SkinnyArgs &args, const SkinnyCfg &cfg, hipStream_t s);
+
+// ---- LDS-tiled MFMA engine (gemm_tiled.hip) ----
+struct TiledArgs {
+    const uint8_t *aq;
+    const float *as;
+    const uint8_t *w;
+    const float *ws;
+    uint16_t *c;
+    int64_t M, K, N;
+};
+hipError_t launch_gemm_tiled(const TiledArgs &args, hipStream_t s);
+
+// ---- MoE decode (moe.hip) ----
+struct MoeArgs {
+    const uint16_t *x;
+    const int32_t *ids;
+    const float *tw;
+    const uint8_t *w13;
+    const float *w13s;
+    const uint8_t *w2;
+    const float *w2s;
+    uint16_t *out;
+    uint16_t *gu;   // [P][2I] bf16 (three-launch path)
+    uint16_t *h;    // [P][I] bf16
+    uint8_t *hq;    // [P][I] fp8 (three-launch path)
+    float *hs;      // [P][I/128] (three-launch path)
+    float *y;       // [P][H] fp32
+    int64_t T, H, E, I, topk;
+};
+struct MoeLayout {
+    size_t gu, h, hq, hs, y, total;
+};
+MoeLayout moe_layout(int64_t T, int64_t H, int64_t E, int64_t I, int64_t topk);
+hipError_t launch_moe_decode(const MoeArgs &args, bool fused, hipStream_t s);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace r9k

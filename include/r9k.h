@@ -1,0 +1,191 @@
+/*
+ * r9k: block-scaled fp8 GEMMs for one AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libr9k.so.  What the library computes is the dense fp8 block GEMM
+ * of LLM decode and prefill described on the r9700-stack release pages:
+ *   - release v0.3.1, "What changed for someone running it": the dense fp8
+ *     block GEMM r9k_gemm_fp8_block_qa, whose per-token-group-128 activation
+ *     quant runs inside the GEMM's A-load with operands bit-identical to the
+ *     split form (a separate quant launch, then the GEMM);
+ *   - release v0.3.2, same section: fp8 kernels for up to 255 rows and the
+ *     tiled fp8 GEMMs above that; weights quantised once at load;
+ *   - release v0.3.3, same section: the fused MoE decode path (silu(gate)*up in
+ *     the gate_up GEMM's epilogue, the fp8 row quant in the down GEMM's A-load),
+ *     bit-identical to the three-launch path.
+ *
+ * Number formats (the workload's stated rules; the pages say only "fp8"):
+ *   fp8   = OCP e4m3fn codes (uint8_t), largest finite value 448;
+ *   bf16  = uint16_t bit patterns (the top half of an IEEE binary32);
+ *   scale = fp32.
+ * Group quantisation rule, used for activations (a row's 128 consecutive K
+ * values) and weights (a 128x128 block): s = max(amax, 1e-10f) / 448 in fp32,
+ * code = e4m3(fp32(a / s)), rounding to nearest even and saturating at +-448.
+ * The GEMM computes C[m,n] = bf16( sum_g P(m,n,g) * as[m,g] * ws[n/128,g] ),
+ * P = sum over the group's 128 k of dec(aq[m,k]) * dec(w[n,k]), accumulated in
+ * fp32, rounded to bf16 with ties to even.
+ *
+ * Layouts: every tensor is dense row-major with no strides.
+ *   A  [M][K] bf16        Aq [M][K] fp8     As [M][K/128] fp32
+ *   W  [N][K] fp8         Ws [N/128][K/128] fp32        (out x in)
+ *   C  [M][N] bf16
+ * K and N must be multiples of 128.  Every pointer passed to a compute call is
+ * a device pointer on the current HIP device; every base pointer must be 16-byte
+ * aligned.  `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *
+ * Ownership and behaviour common to every call:
+ *   - the caller owns every buffer, including workspaces; the library never
+ *     allocates device memory, never synchronises and never reads device data
+ *     on the host;
+ *   - calls are asynchronous on `stream` and capturable in a HIP graph; launch
+ *     grids depend only on the shapes, never on device data;
+ *   - arguments are checked on the host before any launch; a failed check
+ *     returns a negative code and launches nothing;
+ *   - M == 0 (or T == 0, n == 0) returns R9K_OK without launching;
+ *   - faults inside a kernel surface at the caller's next synchronisation;
+ *   - unchecked preconditions: inputs are finite; MoE expert ids lie in [0,E)
+ *     and are distinct within a token's row.
+ */
+#ifndef R9K_H
+#define R9K_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define R9K_ABI_VERSION 1
+
+/* Return codes. */
+#define R9K_OK 0
+#define R9K_ERR_NULLPTR (-1)   /* a required pointer is NULL */
+#define R9K_ERR_SHAPE (-2)     /* a size is out of range (see each call) */
+#define R9K_ERR_ALIGN (-3)     /* a base pointer is not 16-byte aligned */
+#define R9K_ERR_DEVICE (-4)    /* no HIP device, or the current device is not gfx950 */
+#define R9K_ERR_LAUNCH (-5)    /* a kernel launch failed (hipGetLastError) */
+#define R9K_ERR_WORKSPACE (-6) /* the workspace is smaller than the query returned */
+#define R9K_ERR_ARG (-7)       /* an enumerated argument has an unknown value */
+
+/* The ABI version this library implements (R9K_ABI_VERSION).  Callers refuse
+ * a library whose version differs from the header they were built against,
+ * the convention of the pages' plugin, which refuses an older library. */
+int r9k_abi_version(void);
+
+/* Static text for a return code; never NULL. */
+const char *r9k_strerror(int code);
+
+/* ------------------------------------------------------------------------ */
+/* Quantisation                                                              */
+/* ------------------------------------------------------------------------ */
+
+/* Per-token group-128 activation quant (the split form's first launch, and the
+ * definition the fused A-load reproduces bit for bit; release v0.3.1, "What
+ * changed for someone running it").
+ *   a  [M][K] bf16 in; aq [M][K] fp8 out; as [M][K/128] fp32 out.
+ * Errors: NULLPTR; SHAPE if M < 0, K <= 0 or K % 128 != 0; ALIGN; DEVICE; LAUNCH. */
+int r9k_quant_act(const uint16_t *a, int64_t M, int64_t K, uint8_t *aq, float *as, void *stream);
+
+/* Weight quant at load time, one fp32 scale per 128x128 block (release v0.3.2,
+ * "What changed for someone running it": weights quantised once, bf16 copies
+ * freed).  w [N][K] bf16 in; wq [N][K] fp8 out; ws [N/128][K/128] fp32 out.
+ * Errors: NULLPTR; SHAPE if N or K <= 0 or not multiples of 128; ALIGN;
+ * DEVICE; LAUNCH. */
+int r9k_quant_weight(const uint16_t *w, int64_t N, int64_t K, uint8_t *wq, float *ws, void *stream);
+
+/* Elementwise fp32 -> e4m3fn with the library's device encoder: round to
+ * nearest even, saturate at +-448 (inf too), sign of zero kept.  NaN inputs
+ * give an unspecified code.  x [n] fp32 in; codes [n] out.
+ * Errors: NULLPTR; SHAPE if n < 0; ALIGN; DEVICE; LAUNCH. */
+int r9k_encode_e4m3(const float *x, int64_t n, uint8_t *codes, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Dense block-scaled GEMM                                                   */
+/* ------------------------------------------------------------------------ */
+
+/* Workspace bytes that r9k_gemm_fp8_block and r9k_gemm_fp8_block_qa need for
+ * this shape, under any dispatch setting.  Host only; touches no device.
+ * The workspace must be zero-filled before its first use; every call leaves
+ * the part that must start at zero (split-K tile counters) at zero again.
+ * Calls that share a workspace must not overlap in time (same stream, or
+ * ordered by events).
+ * Errors: NULLPTR (bytes); SHAPE as for the GEMM. */
+int r9k_gemm_fp8_block_workspace(int64_t M, int64_t K, int64_t N, size_t *bytes);
+
+/* Block GEMM on pre-quantised activations: the split form, selected on the
+ * pages by turning the fused quant off (release v0.3.1), and the bitwise
+ * reference for the fused form.
+ *   aq [M][K] fp8, as [M][K/128] fp32, w [N][K] fp8, ws [N/128][K/128] fp32
+ *   -> c [M][N] bf16.
+ * Errors: NULLPTR; SHAPE if M < 0, K or N <= 0, or K, N not multiples of 128;
+ * ALIGN; WORKSPACE; DEVICE; LAUNCH. */
+int r9k_gemm_fp8_block(const uint8_t *aq, const float *as, int64_t M, int64_t K, const uint8_t *w,
+                       const float *ws, int64_t N, uint16_t *c, void *workspace, size_t ws_bytes,
+                       void *stream);
+
+/* The fused form r9k_gemm_fp8_block_qa (release v0.3.1): bf16 activations are
+ * quantised per token in groups of 128 inside the GEMM, with codes and scales
+ * bit-identical to r9k_quant_act; the result is bit-identical to
+ * r9k_quant_act followed by r9k_gemm_fp8_block under the same dispatch.
+ * The dispatcher picks the engine by M (release v0.3.2: the decode kernels to
+ * 255 rows, the tiled GEMMs above): M <= skinny_max_m -> the weight-streaming
+ * skinny engine, else the LDS-tiled MFMA engine.
+ *   a [M][K] bf16, w [N][K] fp8, ws [N/128][K/128] fp32 -> c [M][N] bf16.
+ * Errors: as r9k_gemm_fp8_block. */
+int r9k_gemm_fp8_block_qa(const uint16_t *a, int64_t M, int64_t K, const uint8_t *w, const float *ws,
+                          int64_t N, uint16_t *c, void *workspace, size_t ws_bytes, void *stream);
+
+/* Dispatch control.  skinny_max_m: the largest M the skinny engine takes
+ * (default 255, the pages' boundary; env R9K_FP8_SKINNY_MAXM).  engine:
+ * R9K_ENGINE_AUTO (by M), R9K_ENGINE_SKINNY or R9K_ENGINE_TILED (forced, for
+ * tests; env R9K_FP8_ENGINE=auto|skinny|tiled).  The setting is process-wide;
+ * change it only while no GEMM call is being issued.
+ * Errors: SHAPE if skinny_max_m < 0; ARG for an unknown engine. */
+#define R9K_ENGINE_AUTO 0
+#define R9K_ENGINE_SKINNY 1
+#define R9K_ENGINE_TILED 2
+int r9k_set_dispatch(int skinny_max_m, int engine);
+int r9k_get_dispatch(int *skinny_max_m, int *engine);
+
+/* ------------------------------------------------------------------------ */
+/* MoE decode                                                                */
+/* ------------------------------------------------------------------------ */
+
+/* Workspace bytes for r9k_moe_fp8_decode (host only).  Same zero-fill rule as
+ * the GEMM workspace.  Errors: NULLPTR (bytes); SHAPE as for the call. */
+int r9k_moe_fp8_decode_workspace(int64_t T, int64_t H, int64_t E, int64_t I, int64_t topk, size_t *bytes);
+
+/* Routed MoE decode (release v0.3.3, "What changed for someone running it").
+ * For token t and slot j, expert e = topk_ids[t][j]:
+ *   gu  = bf16(block GEMM of quant(x[t]) against w13[e])    rows [0,I) gate, [I,2I) up
+ *   h   = bf16(silu(gate) * up)                              fp32 arithmetic
+ *   y   = block GEMM of quant(h) (group 128 along I) against w2[e], fp32
+ *   out[t] = bf16(sum_j topk_w[t][j] * y(t,j)), j ascending.
+ * fused = 1: silu(gate)*up in the gate_up kernel's epilogue and h's row quant
+ * in the down kernel's A-load; fused = 0: the three-launch path (gate_up,
+ * silu*up + quant, down), bit-identical.  Both end with the ordered combine.
+ *   x [T][H] bf16; topk_ids [T][topk] int32; topk_w [T][topk] fp32;
+ *   w13 [E][2I][H] fp8, w13_s [E][2I/128][H/128] fp32;
+ *   w2 [E][H][I] fp8, w2_s [E][H/128][I/128] fp32 -> out [T][H] bf16.
+ * The workspace holds, at byte offsets r9k_moe_ws_offset() reports, the
+ * intermediates per pair p = t*topk + j: gu [T*topk][2I] bf16 (unfused only),
+ * h [T*topk][I] bf16, y [T*topk][H] fp32.
+ * Errors: NULLPTR; SHAPE if T < 0, T > 256, H or I not positive multiples of
+ * 128, E <= 0, topk < 1 or topk > E; ALIGN; WORKSPACE; ARG (fused not 0/1);
+ * DEVICE; LAUNCH. */
+int r9k_moe_fp8_decode(const uint16_t *x, int64_t T, int64_t H, const int32_t *topk_ids, const float *topk_w,
+                       int64_t topk, const uint8_t *w13, const float *w13_s, const uint8_t *w2,
+                       const float *w2_s, int64_t E, int64_t I, uint16_t *out, void *workspace,
+                       size_t ws_bytes, int fused, void *stream);
+
+/* Byte offset inside the MoE workspace of an intermediate (for tests):
+ * which = 0 gu [P][2I] bf16, 1 h [P][I] bf16, 2 y [P][H] fp32, 3 hq [P][I] fp8,
+ * 4 hs [P][I/128] fp32 (P = T*topk; gu, hq and hs are written by the
+ * three-launch path only).  Host only.  Errors: NULLPTR; SHAPE; ARG. */
+int r9k_moe_ws_offset(int64_t T, int64_t H, int64_t E, int64_t I, int64_t topk, int which, size_t *offset);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* R9K_H */

@@ -68,6 +68,7 @@ def lib():
                                         u16p, f64p, c_int]
         L.ora_moe_decode.argtypes = [u16p, c_int64, c_int64, i32p, f32p, c_int64, u8p, f32p, u8p, f32p, c_int64,
                                      c_int64, u16p, u16p, u16p, u8p, f32p, f64p, c_int]
+        L.ora_moe_silu_mul.argtypes = [u16p, c_int64, c_int64, u16p]
         L.ora_moe_down_from_h.argtypes = [u16p, c_int64, c_int64, i32p, f32p, c_int64, u8p, f32p, c_int64, c_int64,
                                           u16p, u8p, f32p, f64p, c_int]
         _lib = L
@@ -212,6 +213,15 @@ def moe_decode(x, ids, w, w13q, w13s, w2q, w2s, intermediates: bool = False):
                          g("gu", c_uint16), g("h", c_uint16), g("hq", c_uint8), g("hs", c_float), g("y", c_double),
                          threads())
     return (out, inter) if intermediates else out
+
+
+def moe_silu_mul(gu):
+    """h = bf16(silu(gate) * up) per pair from gu [P, 2I] (bf16 bits) -> h [P, I]."""
+    gu = _u16(gu)
+    P, twoI = gu.shape
+    h = np.empty((P, twoI // 2), np.uint16)
+    lib().ora_moe_silu_mul(_p(gu, c_uint16), P, twoI // 2, _p(h, c_uint16))
+    return h
 
 
 def moe_down_from_h(h, ids, w, w2q, w2s, intermediates: bool = False):

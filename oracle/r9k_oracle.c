@@ -315,6 +315,22 @@ void ora_gemm_block_at(const uint8_t *aq, const float *as, int64_t M, int64_t K,
  *   out[t] = bf16(sum_j w[t][j] * y(t, j)), j ascending, binary64.
  * Intermediates are written per pair p = t*topk + j when the pointers are not
  * NULL: gu [P][2I] bf16, h [P][I] bf16, hq [P][I], hs [P][I/128], y [P][H]. */
+/* h[i] = bf16(silu(gate[i]) * up[i]) for one pair, gate = gu[0..I), up =
+ * gu[I..2I), silu(z) = z / (1 + exp(-z)), all in binary64, rounded once. */
+static void silu_mul_row(const uint16_t *gu, int64_t I, uint16_t *h) {
+    for (int64_t i = 0; i < I; ++i) {
+        double g = (double)ora_bf16_value(gu[i]);
+        double u = (double)ora_bf16_value(gu[I + i]);
+        double silu = g / (1.0 + exp(-g));
+        h[i] = ora_bf16_round(silu * u);
+    }
+}
+
+/* The silu(gate) * up step alone, for P pairs: gu [P][2I] -> h [P][I]. */
+void ora_moe_silu_mul(const uint16_t *gu, int64_t P, int64_t I, uint16_t *h) {
+    for (int64_t p = 0; p < P; ++p) silu_mul_row(gu + p * 2 * I, I, h + p * I);
+}
+
 struct moe_ctx {
     const uint16_t *x; int64_t T, H;
     const int32_t *ids; const float *w; int64_t topk;
@@ -344,12 +360,7 @@ static void moe_pair_range(int64_t lo, int64_t hi, void *p) {
             for (int64_t n = 0; n < 2 * I; ++n)
                 gu[n] = ora_bf16_round(gemm_elem(T, c->xq + t * H, c->xs + t * GH, w13 + n * H,
                                                  w13s + (n / 128) * GH, H));
-            for (int64_t i = 0; i < I; ++i) {
-                double g = (double)ora_bf16_value(gu[i]);
-                double u = (double)ora_bf16_value(gu[I + i]);
-                double silu = g / (1.0 + exp(-g));
-                h[i] = ora_bf16_round(silu * u);
-            }
+            silu_mul_row(gu, I, h);
         }
         for (int64_t g = 0; g < GI; ++g) hs[g] = quant_group(h + 128 * g, 128, 1, hq + 128 * g, 1);
         for (int64_t n = 0; n < H; ++n)

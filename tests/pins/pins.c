@@ -118,14 +118,21 @@ void pin_bf16_round_bits_array(const float *x, int64_t n, uint16_t *out, int nt)
 }
 
 /* ------------------------------------------------------------------------ */
-/* Division by a group scale with one reciprocal per group:                  */
-/*   r = RN(1/s), q0 = RN(a*r), e = fma(-q0, s, a), q = fma(e, r, q0)         */
+/* Division by a group scale with one reciprocal per group, as the GPU       */
+/* kernels do it:                                                            */
+/*   r = RN(1/s), q0 = RN(a*r), d = fma(q0, s, -a), q = fma(-d, r, q0)        */
 /* (Markstein's correction; Muller et al., Handbook of Floating-Point        */
 /* Arithmetic, division chapter).  Counted: pairs where the e4m3 code of q     */
 /* differs from the e4m3 code of the correctly rounded a/s, over every        */
-/* positive bf16 amax (and the eps floor) and every bf16 a with |a| <= amax.   */
-/* The e4m3 codes are taken with pin_e4m3_encode_bits.                         */
+/* positive bf16 amax (and the eps floor) and every bf16 a with |a| <= amax,  */
+/* both signs of a (so -0 too).  The e4m3 codes are taken with               */
+/* pin_e4m3_encode_bits.                                                      */
 /* ------------------------------------------------------------------------ */
+static float div_device_formula(float a, float s, float r) {
+    float q0 = a * r;
+    float d = fmaf(q0, s, -a);
+    return fmaf(-d, r, q0);
+}
 static void div_rng(int64_t lo, int64_t hi, void *p, int64_t *cnt) {
     (void)p;
     const float eps = 1e-10f;
@@ -135,13 +142,10 @@ static void div_rng(int64_t lo, int64_t hi, void *p, int64_t *cnt) {
         float s = (amax > eps ? amax : eps) / 448.0f;
         float r = 1.0f / s;
         for (uint32_t xb = 0; xb <= (uint32_t)ab; ++xb) {
-            float a = fbits(xb << 16);
-            float q0 = a * r;
-            float e = fmaf(-q0, s, a);
-            float q = fmaf(e, r, q0);
-            float ref = a / s;
-            if (pin_e4m3_encode_bits(q) != pin_e4m3_encode_bits(ref)) ++bad;
-            if (pin_e4m3_encode_bits(-q) != pin_e4m3_encode_bits(-ref)) ++bad;
+            for (int neg = 0; neg < 2; ++neg) {
+                float a = fbits((xb << 16) | (neg ? 0x80000000u : 0u));
+                if (pin_e4m3_encode_bits(div_device_formula(a, s, r)) != pin_e4m3_encode_bits(a / s)) ++bad;
+            }
         }
     }
     *cnt = bad;

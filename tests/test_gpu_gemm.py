@@ -1,0 +1,179 @@
+"""GPU parity for the dense block-scaled GEMM through the C ABI.
+
+Outputs must satisfy |gpu - oracle| <= 1e-2 * RMS(oracle) + 1 bf16 ulp(oracle)
+elementwise (RMS over the whole output of the call; for sampled checks, over
+the sampled oracle values).  The fused form must equal the split form bit for
+bit, both engines must pass at every M (forced), and repeated runs must be
+bitwise identical.
+"""
+import numpy as np
+import pytest
+
+from block_scaled_fp8_r9k_amd import inputs
+from tests.gpu_util import assert_bits_equal, assert_close, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def r9k():
+    import torch
+    import block_scaled_fp8_r9k_amd as r9k
+    assert torch.cuda.is_available()
+    r9k.lib()
+    yield r9k
+    r9k.set_dispatch(255, r9k.ENGINE_AUTO)
+
+
+class Problem:
+    """Seeded inputs; the GPU quantises the weights with its own kernel and
+    the oracle with its own code (the quant parity is tested separately)."""
+
+    def __init__(self, r9k, ora, M, K, N, seed=0, outliers=True):
+        self.M, self.K, self.N = M, K, N
+        self.a = inputs.activations(seed, M, K, outliers=outliers)
+        self.w = inputs.weights(seed, N, K)
+        self.wq_o, self.ws_o = ora.quant_weight(self.w)
+        self.aq_o, self.as_o = ora.quant_act(self.a)
+        self.a_d = dev(self.a)
+        self.wq_d, self.ws_d = r9k.quant_weight(dev(self.w))
+
+    def oracle_full(self, ora):
+        _, c64 = ora.gemm_block(self.aq_o, self.as_o, self.wq_o, self.ws_o, want_f64=True)
+        return c64
+
+    def run(self, r9k, engine, fused=True):
+        r9k.set_dispatch(255, engine)
+        if fused:
+            return host(r9k.gemm_fp8_block_qa(self.a_d, self.wq_d, self.ws_d))
+        aq, as_ = r9k.quant_act(self.a_d)
+        return host(r9k.gemm_fp8_block(aq, as_, self.wq_d, self.ws_d))
+
+
+ENGINES = {"skinny": 1, "tiled": 2}
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 512, 1024), (1, 128, 128), (3, 384, 256), (16, 1024, 384),
+                                   (17, 256, 640), (33, 640, 256), (100, 384, 384), (255, 512, 256),
+                                   (256, 512, 256), (300, 256, 384), (129, 1280, 128)])
+@pytest.mark.parametrize("engine", ["skinny", "tiled"])
+def test_gemm_small_shapes(r9k, ora, M, K, N, engine):
+    say("gemm", engine, M, K, N)
+    p = Problem(r9k, ora, M, K, N, seed=M * 7 + K)
+    c64 = p.oracle_full(ora)
+    fused = p.run(r9k, ENGINES[engine], fused=True)
+    assert_close(ora, fused, c64, f"{engine} fused {M}x{K}x{N}")
+    split = p.run(r9k, ENGINES[engine], fused=False)
+    assert_bits_equal(fused, split, f"{engine} fused vs split {M}x{K}x{N}")
+    again = p.run(r9k, ENGINES[engine], fused=True)
+    assert_bits_equal(fused, again, f"{engine} repeat {M}x{K}x{N}")
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 16])
+def test_gemm_decode_sweep_full(r9k, ora, M):
+    """M in {1,2,4,8,16}, K=4096, N=14336, every output against the oracle."""
+    say("decode sweep", M)
+    p = Problem(r9k, ora, M, 4096, 14336)
+    c64 = p.oracle_full(ora)
+    got = p.run(r9k, 0, fused=True)
+    assert_close(ora, got, c64, f"decode M={M}")
+    assert_bits_equal(got, p.run(r9k, 0, fused=False), f"decode M={M} fused vs split")
+
+
+def _sampled(ora, p, rows, n_random=4000, seed=3):
+    r = np.random.default_rng(seed)
+    ms = np.concatenate([np.repeat(rows, p.N), r.integers(0, p.M, n_random)])
+    ns = np.concatenate([np.tile(np.arange(p.N), len(rows)), r.integers(0, p.N, n_random)])
+    _, c64 = ora.gemm_block_at(p.aq_o, p.as_o, p.wq_o, p.ws_o, ms, ns, want_f64=True)
+    return ms, ns, c64
+
+
+@pytest.mark.parametrize("M,K", [(32, 4096), (64, 4096), (128, 14336), (255, 4096), (255, 14336)])
+def test_gemm_mid_sweep_sampled(r9k, ora, M, K):
+    say("mid sweep", M, K)
+    p = Problem(r9k, ora, M, K, 4096)
+    rows = np.unique(np.array([0, 1, M // 2, M - 1]))
+    ms, ns, c64 = _sampled(ora, p, rows)
+    got = p.run(r9k, 0, fused=True)
+    assert_close(ora, got[ms, ns], c64, f"mid M={M} K={K}")
+    assert_bits_equal(got, p.run(r9k, 0, fused=False), f"mid M={M} fused vs split")
+
+
+def test_gemm_boundary_both_engines(r9k, ora):
+    """M = 255 and 256 at K=4096, N=4096, each engine forced."""
+    for M in (255, 256):
+        p = Problem(r9k, ora, M, 4096, 4096, seed=M)
+        rows = np.array([0, 127, 128, M - 1])
+        ms, ns, c64 = _sampled(ora, p, rows)
+        outs = {}
+        for name, e in ENGINES.items():
+            say("boundary", M, name)
+            outs[name] = p.run(r9k, e, fused=True)
+            assert_close(ora, outs[name][ms, ns], c64, f"boundary M={M} {name}")
+
+
+def test_gemm_prefill_sampled(r9k, ora):
+    """M=4096, K=4096, N=12288 (the prefill chunk), auto dispatch, sampled outputs."""
+    say("prefill 4096x4096x12288")
+    p = Problem(r9k, ora, 4096, 4096, 12288)
+    rows = np.array([0, 1, 127, 128, 2047, 4095])
+    ms, ns, c64 = _sampled(ora, p, rows, n_random=20000)
+    got = p.run(r9k, 0, fused=True)
+    assert_close(ora, got[ms, ns], c64, "prefill")
+    again = p.run(r9k, 0, fused=True)
+    assert_bits_equal(got, again, "prefill repeat")
+
+
+def test_gemm_reuses_workspace_and_streams(r9k, ora):
+    """Two shapes in a row through one explicit workspace, on a side stream:
+    the split-K counters come back to zero after every call."""
+    import torch
+    p1 = Problem(r9k, ora, 8, 4096, 2048, seed=5)
+    p2 = Problem(r9k, ora, 3, 1024, 1024, seed=6)
+    nbytes = max(r9k.gemm_fp8_block_workspace(8, 4096, 2048), r9k.gemm_fp8_block_workspace(3, 1024, 1024))
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    r9k.set_dispatch(255, 0)
+    outs = []
+    with torch.cuda.stream(s):
+        for p in (p1, p2, p1, p2):
+            outs.append(r9k.gemm_fp8_block_qa(p.a_d, p.wq_d, p.ws_d, workspace=ws, stream=s))
+    s.synchronize()
+    assert_close(ora, host(outs[0]), p1.oracle_full(ora), "stream p1")
+    assert_close(ora, host(outs[1]), p2.oracle_full(ora), "stream p2")
+    assert_bits_equal(host(outs[0]), host(outs[2]), "p1 twice")
+    assert_bits_equal(host(outs[1]), host(outs[3]), "p2 twice")
+    n_cnt = 4 * 16                                                # the counters region is zero again
+    assert int(ws[:n_cnt].sum().item()) == 0
+
+
+def test_gemm_in_hip_graph(r9k, ora):
+    """Captured decode and prefill calls replay to the eager result, several times."""
+    import torch
+    r9k.set_dispatch(255, 0)
+    pd = Problem(r9k, ora, 4, 4096, 4096, seed=8)
+    pp = Problem(r9k, ora, 512, 1024, 1024, seed=9)
+    ws_d = torch.zeros(r9k.gemm_fp8_block_workspace(4, 4096, 4096), dtype=torch.uint8, device="cuda")
+    ws_p = torch.zeros(r9k.gemm_fp8_block_workspace(512, 1024, 1024), dtype=torch.uint8, device="cuda")
+    cd = torch.empty((4, 4096), dtype=torch.bfloat16, device="cuda")
+    cp = torch.empty((512, 1024), dtype=torch.bfloat16, device="cuda")
+    eager_d = host(r9k.gemm_fp8_block_qa(pd.a_d, pd.wq_d, pd.ws_d, workspace=ws_d))
+    eager_p = host(r9k.gemm_fp8_block_qa(pp.a_d, pp.wq_d, pp.ws_d, workspace=ws_p))
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            r9k.gemm_fp8_block_qa(pd.a_d, pd.wq_d, pd.ws_d, c=cd, workspace=ws_d)
+            r9k.gemm_fp8_block_qa(pp.a_d, pp.wq_d, pp.ws_d, c=cp, workspace=ws_p)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(4):
+        say("graph replay", rep)
+        cd.zero_()
+        cp.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_bits_equal(host(cd), eager_d, f"graph decode replay {rep}")
+        assert_bits_equal(host(cp), eager_p, f"graph prefill replay {rep}")
+        torch.cuda.synchronize()
