@@ -1,0 +1,338 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-scaled fp8 GEMM path on one MI355X.
+
+Headline (one JSON line on stdout): the decode-width sweep, M in {1,2,4,8,16},
+K=4096, N=14336, bf16 activations quantised per token in groups of 128 inside
+the GEMM (r9k_gemm_fp8_block_qa), fp8 e4m3 weights with 128x128 fp32 block
+scales, bf16 out.  One step = the five fused GEMM calls on one batch of
+synthetic input; `value` is the algorithmic HBM bytes of the step divided by
+its time (GB/s).  Inputs are resident in HBM before timing; the weights rotate
+through enough distinct copies (>= 512 MB) that the 256 MB Infinity Cache
+cannot hold them between launches.  Timing: HIP graphs replayed on the current
+stream, bracketed by HIP events.
+
+The same line carries:
+  roofline      the dominant kernel (the skinny engine at decode widths):
+                algorithmic bytes per launch / its average launch time vs 8 TB/s;
+  cpu_baseline  the CPU oracle timed on one full step of the same inputs;
+  prefill       M=4096, K=4096, N=12288: fp8 TFLOP/s vs 5.03 PFLOP/s dense;
+  mid           M in {32,64,128,255} at (K,N) = (4096,4096) and (14336,4096);
+  moe           16 tokens, hidden 2048, 128 experts of 768, top-8: GB/s over
+                the bytes of the experts the routing touches.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only decode,prefill,mid,moe]
+                       [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+FP8_PEAK_TFLOPS = 5033.2        # 256 CU x 2.4 GHz x 8192 flop/CU/clk, dense fp8 MFMA
+DECODE_M = (1, 2, 4, 8, 16)
+DECODE_K, DECODE_N = 4096, 14336
+ROTATE_BYTES = 512 << 20
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def gemm_bytes(M, K, N):
+    """Algorithmic HBM bytes of one GEMM call: weight codes + block scales +
+    bf16 activations read once + bf16 output."""
+    return N * K + 4 * (N // 128) * (K // 128) + 2 * M * K + 2 * M * N
+
+
+class Timer:
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, fn, reps):
+        torch = self.torch
+        torch.cuda.synchronize()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for i in range(reps):
+            fn(i)
+        e.record()
+        e.synchronize()
+        return s.elapsed_time(e) / reps  # ms
+
+
+def capture(torch, calls):
+    """One HIP graph holding the given launches, captured on a side stream."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for c in calls:
+                c()
+    torch.cuda.current_stream().wait_stream(s)
+    return g
+
+
+def weight_copies(torch, r9k, dev, w_bits, min_bytes=ROTATE_BYTES, cap=16):
+    """Quantise W once on the GPU (r9k_quant_weight) and make enough distinct
+    device copies that rotating through them defeats the Infinity Cache."""
+    wq, ws = r9k.quant_weight(dev(w_bits))
+    n = max(2, min(cap, -(-min_bytes // wq.numel())))
+    copies = [(wq, ws)] + [(wq.clone(), ws.clone()) for _ in range(n - 1)]
+    torch.cuda.synchronize()
+    return copies
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("gemm_skinny.hip", "r9k_device.h", "api.hip"):
+        with open(os.path.join(ROOT, "block_scaled_fp8_r9k_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles():
+    """HBM bytes per launch of the skinny decode kernel, from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", "skinny_decode_traffic.json")
+    try:
+        with open(p) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+# --------------------------------------------------------------------------
+
+def bench_decode(torch, r9k, inputs, dev, steps, warmup):
+    K, N = DECODE_K, DECODE_N
+    Mmax = max(DECODE_M)
+    a_bits = inputs.activations(0, Mmax, K, outliers=True)
+    w_bits = inputs.weights(0, N, K)
+    a = dev(a_bits)
+    copies = weight_copies(torch, r9k, dev, w_bits)
+    C = len(copies)
+    log(f"decode: {C} weight copies of {copies[0][0].numel() / 1e6:.1f} MB")
+    ws_bytes = max(r9k.gemm_fp8_block_workspace(M, K, N) for M in DECODE_M)
+    wsp = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+    outs = {M: torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for M in DECODE_M}
+    a_rows = {M: a[:M].contiguous() for M in DECODE_M}
+
+    def call(M, c):
+        wq, ws = copies[c]
+        return lambda: r9k.gemm_fp8_block_qa(a_rows[M], wq, ws, c=outs[M], workspace=wsp)
+
+    for c in range(C):  # eager warm-up of every call
+        for M in DECODE_M:
+            call(M, c)()
+    torch.cuda.synchronize()
+    step_graphs = [capture(torch, [call(M, c) for M in DECODE_M]) for c in range(C)]
+    step_bytes = sum(gemm_bytes(M, K, N) for M in DECODE_M)
+    tm = Timer(torch)
+    tm.run(lambda i: step_graphs[i % C].replay(), max(warmup, 1))
+    ms_step = tm.run(lambda i: step_graphs[i % C].replay(), steps)
+
+    # the dominant kernel alone: graphs of back-to-back launches at one M
+    per_m = {}
+    for M in DECODE_M:
+        reps_per_graph = 2 * C
+        g = capture(torch, [call(M, i % C) for i in range(reps_per_graph)])
+        tm.run(lambda i: g.replay(), 2)
+        ms = tm.run(lambda i: g.replay(), max(3, steps // 4)) / reps_per_graph
+        b = gemm_bytes(M, K, N)
+        per_m[M] = dict(us=ms * 1e3, GBs=b / (ms * 1e-3) / 1e9)
+        log(f"decode M={M}: {ms * 1e3:.2f} us/launch, {per_m[M]['GBs']:.0f} GB/s")
+    us_avg = float(np.mean([per_m[M]["us"] for M in DECODE_M]))
+    bytes_avg = float(np.mean([gemm_bytes(M, K, N) for M in DECODE_M]))
+    achieved = bytes_avg / (us_avg * 1e-6) / 1e9
+    return dict(ms_step=ms_step, step_bytes=step_bytes, per_m=per_m, achieved=achieved, us_avg=us_avg,
+                bytes_avg=bytes_avg, a_bits=a_bits, w_bits=w_bits)
+
+
+def cpu_baseline(ora, a_bits, w_bits, step_bytes):
+    """The oracle (exact fp64 group sums, one bf16 rounding) on one full step:
+    activation quant + GEMM for every M of the sweep; weight quant is setup."""
+    wq, ws = ora.quant_weight(w_bits)
+    times = []
+    t_total = 0.0
+    while len(times) < 3 and t_total < 30.0:
+        t0 = time.perf_counter()
+        for M in DECODE_M:
+            ora.gemm_block_qa(a_bits[:M], wq, ws)
+        dt = time.perf_counter() - t0
+        times.append(dt)
+        t_total += dt
+    t = float(np.median(times))
+    return dict(value=step_bytes / t / 1e9, unit="GB/s", cores=ora.threads(), kind="oracle",
+                seconds_per_step=t, repeats=len(times),
+                sample=f"one full step: oracle group-128 act quant + exact block GEMM for M in "
+                       f"{list(DECODE_M)}, K={DECODE_K}, N={DECODE_N} (weight quant not timed), "
+                       f"median of {len(times)}")
+
+
+def bench_prefill(torch, r9k, inputs, dev, reps):
+    M, K, N = 4096, 4096, 12288
+    a = dev(inputs.activations(1, M, K, outliers=True))
+    copies = weight_copies(torch, r9k, dev, inputs.weights(1, N, K), min_bytes=256 << 20, cap=6)
+    C = len(copies)
+    wsp = torch.zeros(r9k.gemm_fp8_block_workspace(M, K, N), dtype=torch.uint8, device="cuda")
+    c_out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    calls = [lambda c=c: r9k.gemm_fp8_block_qa(a, copies[c][0], copies[c][1], c=c_out, workspace=wsp)
+             for c in range(C)]
+    for f in calls:
+        f()
+    g = capture(torch, calls)
+    tm = Timer(torch)
+    tm.run(lambda i: g.replay(), 1)
+    ms = tm.run(lambda i: g.replay(), reps) / C
+    tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+    log(f"prefill {M}x{K}x{N}: {ms * 1e3:.1f} us, {tflops:.0f} TFLOP/s")
+    return dict(workload=f"M={M}, K={K}, N={N}, fused act quant", us=ms * 1e3, value=tflops, unit="TFLOP/s",
+                peak=FP8_PEAK_TFLOPS, frac=tflops / FP8_PEAK_TFLOPS)
+
+
+def bench_mid(torch, r9k, inputs, dev, reps):
+    res = []
+    for K, N in ((4096, 4096), (14336, 4096)):
+        a = dev(inputs.activations(2, 255, K, outliers=True))
+        copies = weight_copies(torch, r9k, dev, inputs.weights(2, N, K))
+        C = len(copies)
+        for M in (32, 64, 128, 255):
+            wsp = torch.zeros(r9k.gemm_fp8_block_workspace(M, K, N), dtype=torch.uint8, device="cuda")
+            am = a[:M].contiguous()
+            c_out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            calls = [lambda c=c: r9k.gemm_fp8_block_qa(am, copies[c][0], copies[c][1], c=c_out, workspace=wsp)
+                     for c in range(C)]
+            for f in calls:
+                f()
+            g = capture(torch, calls)
+            tm = Timer(torch)
+            tm.run(lambda i: g.replay(), 1)
+            ms = tm.run(lambda i: g.replay(), reps) / C
+            gbs = gemm_bytes(M, K, N) / (ms * 1e-3) / 1e9
+            tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+            log(f"mid M={M} K={K} N={N}: {ms * 1e3:.2f} us, {gbs:.0f} GB/s, {tf:.0f} TFLOP/s")
+            res.append(dict(M=M, K=K, N=N, us=ms * 1e3, GBs=gbs, hbm_frac=gbs / HBM_PEAK_GBS, TFLOPs=tf))
+        del copies
+        torch.cuda.empty_cache()
+    return res
+
+
+def bench_moe(torch, r9k, inputs, dev, reps):
+    T, H, E, I, k = 16, 2048, 128, 768, 8
+    x, ids, tw, w13, w2 = inputs.moe_inputs(0, T, H, E, I, k)
+    q13, s13 = r9k.quant_weight(dev(w13.reshape(E * 2 * I, H)))
+    q2, s2 = r9k.quant_weight(dev(w2.reshape(E * H, I)))
+    del w13, w2
+    sets = [(q13, s13, q2, s2), (q13.clone(), s13.clone(), q2.clone(), s2.clone())]
+    x_d, ids_d, tw_d = dev(x), torch.from_numpy(ids).cuda(), torch.from_numpy(tw).cuda()
+    wsp = torch.zeros(r9k.moe_fp8_decode_workspace(T, H, E, I, k), dtype=torch.uint8, device="cuda")
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    touched = len(np.unique(ids))
+    per_expert = 2 * I * H + 4 * (2 * I // 128) * (H // 128) + H * I + 4 * (H // 128) * (I // 128)
+    nbytes = touched * per_expert + 2 * T * H * 2 + T * k * 8
+    res = {}
+    for fused in (True, False):
+        calls = [lambda s=s: r9k.moe_fp8_decode(x_d, ids_d, tw_d, s[0].view(E, 2 * I, H),
+                                                s[1].view(E, 2 * I // 128, H // 128), s[2].view(E, H, I),
+                                                s[3].view(E, H // 128, I // 128), out=out, workspace=wsp,
+                                                fused=fused) for s in sets]
+        for f in calls:
+            f()
+        g = capture(torch, calls)
+        tm = Timer(torch)
+        tm.run(lambda i: g.replay(), 1)
+        ms = tm.run(lambda i: g.replay(), reps) / len(sets)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        log(f"moe fused={fused}: {ms * 1e3:.1f} us, {gbs:.0f} GB/s over {touched} touched experts")
+        res["fused" if fused else "three_launch"] = dict(us=ms * 1e3, GBs=gbs, hbm_frac=gbs / HBM_PEAK_GBS)
+    res.update(workload=f"T={T}, H={H}, E={E}, I={I}, top-{k}", touched_experts=touched, bytes=nbytes)
+    return res
+
+
+def copy_bandwidth(torch):
+    """Context only: a plain device copy of 1 GiB (read + write bytes / time)."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    tm = Timer(torch)
+    tm.run(lambda i: dst.copy_(src), 2)
+    ms = tm.run(lambda i: dst.copy_(src), 10)
+    del src, dst
+    return 2 * n / (ms * 1e-3) / 1e9
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--only", default="decode,prefill,mid,moe")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one MI355X: the path is single-GPU (no collectives); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+    which = set(args.only.split(","))
+
+    import torch
+    import block_scaled_fp8_r9k_amd as r9k
+    from block_scaled_fp8_r9k_amd import inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    r9k.lib()
+
+    def dev(x):
+        x = np.ascontiguousarray(x)
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(x).cuda()
+
+    line = dict(metric="block-fp8 GEMM: HBM GB/s (% peak) at M<=16; fp8 TFLOPS (% MFMA peak) at M=4096",
+                value=None, unit="GB/s", n_gpus=1, steps=args.steps, warmup=args.warmup, ms_per_step=None,
+                higher_is_better=True, scaling="weak", vs_baseline=None, dtype="fp8_e4m3", data="synthetic",
+                config=dict(workload="decode-width sweep: M in {1,2,4,8,16}, K=4096, N=14336, bf16 act quantised "
+                                     "per token in groups of 128 inside the GEMM, fp8 e4m3 weights with 128x128 "
+                                     "fp32 block scales, bf16 out", M=list(DECODE_M), K=DECODE_K, N=DECODE_N))
+    if "decode" in which:
+        d = bench_decode(torch, r9k, inputs, dev, args.steps, args.warmup)
+        line["value"] = d["step_bytes"] / (d["ms_step"] * 1e-3) / 1e9
+        line["ms_per_step"] = d["ms_step"]
+        line["hbm_frac"] = line["value"] / HBM_PEAK_GBS
+        line["roofline"] = dict(bound="hbm", achieved=d["achieved"], peak=HBM_PEAK_GBS, unit="GB/s",
+                                frac=d["achieved"] / HBM_PEAK_GBS, traffic=traffic_from_profiles(),
+                                kernel="k_gemm_skinny (fused act quant), average over the sweep's launches",
+                                bytes_per_launch=d["bytes_avg"], us_per_launch=d["us_avg"])
+        line["per_m"] = {str(M): v for M, v in d["per_m"].items()}
+        if not args.no_cpu_baseline:
+            import oracle
+            log("cpu baseline (oracle) ...")
+            line["cpu_baseline"] = cpu_baseline(oracle, d["a_bits"], d["w_bits"], d["step_bytes"])
+    reps = max(5, args.steps // 20)
+    if "prefill" in which:
+        line["prefill"] = bench_prefill(torch, r9k, inputs, dev, reps)
+    if "mid" in which:
+        line["mid"] = bench_mid(torch, r9k, inputs, dev, reps)
+    if "moe" in which:
+        line["moe"] = bench_moe(torch, r9k, inputs, dev, reps)
+    line["copy_GBs_context"] = copy_bandwidth(torch)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
