@@ -82,16 +82,15 @@ int engine_for(int64_t M) {
     return M <= g_skinny_max_m.load() ? R9K_ENGINE_SKINNY : R9K_ENGINE_TILED;
 }
 
-// GEMM workspace: [skinny tile counters][skinny split-K partials][A codes][A scales]
+// GEMM workspace: [skinny split-K partials][A codes][A scales]
 struct GemmWs {
-    size_t counters, part, aq, as, total;
+    size_t part, aq, as, total;
 };
 GemmWs gemm_ws(int64_t M, int64_t K, int64_t N) {
     GemmWs w;
     const SkinnyCfg c = skinny_config(M, K, N);
-    w.counters = 0;
-    w.part = skinny_counter_bytes(c, N);
-    w.aq = w.part + skinny_partial_bytes(c, N);
+    w.part = 0;
+    w.aq = w.part + skinny_partial_bytes(c, M, N);
     w.as = w.aq + align_up((size_t)(M * K), 256);
     w.total = w.as + align_up((size_t)(M * (K / 128)) * sizeof(float), 256);
     return w;
@@ -108,6 +107,15 @@ int run_gemm(const uint16_t *a, const uint8_t *aq, const float *as, int64_t M, i
     if (rc) return rc;
     uint8_t *base = (uint8_t *)workspace;
     const int engine = engine_for(M);
+    if (engine == R9K_ENGINE_SKINNY) {
+        // decode widths: the dedicated weight-streaming kernel when the shape
+        // fits it, with the activation quant in its A-load
+        const DecodeCfg dc = decode_config(M, K, N);
+        if (dc.wn) {
+            DecodeArgs d{a, aq, as, w, ws, c, M, K, N};
+            return launch_result(launch_gemm_decode(d, dc, s));
+        }
+    }
     if (a && (engine == R9K_ENGINE_TILED || M > g_qa_inload_max_m.load())) {
         // quantise A once per call into the workspace, then run on codes
         uint8_t *wq_a = base + L.aq;
@@ -123,7 +131,7 @@ int run_gemm(const uint16_t *a, const uint8_t *aq, const float *as, int64_t M, i
         return launch_result(launch_gemm_tiled(t, s));
     }
     const SkinnyCfg cfg = skinny_config(M, K, N);
-    SkinnyArgs sa{a, aq, as, w, ws, c, (float *)(base + L.part), (uint32_t *)(base + L.counters), M, K, N};
+    SkinnyArgs sa{a, aq, as, w, ws, c, (float *)(base + L.part), M, K, N};
     return launch_result(launch_gemm_skinny(sa, cfg, s));
 }
 

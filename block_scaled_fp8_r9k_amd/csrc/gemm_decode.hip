@@ -1,0 +1,286 @@
+// Engine (a), decode widths (1 <= M <= 16): the weight-streaming skinny GEMM.
+//
+// The r9700-stack release v0.3.1 notes ("What changed for someone running
+// it") describe the decode GEMMs as the step's largest weight stream and move
+// the per-token-group-128 activation quant into the GEMM's A-load.  Here the
+// kernel is shaped around that stream:
+//   - a CTA's wn x wk waves own (16-column tile, K slice) pairs, 16 weight rows
+//     by K/wk bytes each, and all of K is covered inside the CTA, so no CTA
+//     ever waits for another and the result does not depend on timing;
+//   - every wave first requests its share of the activation groups, then its
+//     whole weight slice, straight into the registers that feed the MFMA
+//     (16-byte loads, at most 32 per lane); a wave's loads complete in issue
+//     order, so the activations are usable while the weights still stream;
+//   - the CTA quantises the M activation rows over all of K into LDS, 4 lanes
+//     (a DPP quad) per 128-value group: the fused A-load of
+//     r9k_gemm_fp8_block_qa; the split form copies pre-quantised codes instead;
+//   - per K-group one e4m3 16x16x128 MFMA, promoted as acc += P * as * ws;
+//   - the wk K-slices of a tile are summed through LDS in ascending slice order
+//     by the slice-0 wave, rounded to bf16 and stored.
+// Rows M..15 of the MFMA's 16 are never stored, so their LDS contents are left
+// as they are.  MFMA roles: weight rows are the A operand (16 n), activation
+// rows the B operand (16 m); a lane's four outputs are four consecutive n of
+// row l % 16.  K order inside a group: lane quarter q feeds bytes [16q, +16)
+// and [64+16q, +16) for both operands.
+#include <algorithm>
+#include <climits>
+#include <cstdlib>
+#include <mutex>
+
+#include "r9k_device.h"
+#include "r9k_internal.h"
+
+namespace r9k {
+
+namespace {
+constexpr int MAX_GS = 16;  // K-groups per wave: 32 x 16-byte loads per lane
+}
+
+// GS = K-groups per wave, PASSES = activation groups per lane quad; both fixed
+// at compile time so that every load is unconditional and each wait covers
+// only the loads it needs.
+//
+// Issue schedule per wave.  A wave that has more loads than the memory system
+// takes at once stalls at the load instruction itself, so anything placed
+// after all of its weight loads would start only near the end of the stream.
+// The weight slice therefore goes out in NCH chunks, and the activation side
+// is worked on between them: activation batch 0, weight chunk 0, quantise
+// batch 0, activation batch 1, weight chunk 1, quantise batch 1, remaining
+// weight chunks.  Loads of one wave complete in issue order, so each quantise
+// step waits only for its own batch and the chunks issued before it.
+template <bool QA, int GS, int PASSES>
+__global__ __launch_bounds__(512) void k_gemm_decode(DecodeArgs p, int wn, int wk) {
+    constexpr int PB = PASSES < 4 ? PASSES : 4;      // passes per activation batch
+    constexpr int NB = PASSES / PB;                  // activation batches (1 or 2)
+    constexpr int NCH = GS < 4 ? GS : 4;             // weight chunks
+    constexpr int CH = GS / NCH;                     // K-groups per chunk
+    static_assert(NB <= NCH, "each activation batch follows a weight chunk");
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int64_t K = p.K, N = p.N, G = K / 128;
+    const int M = (int)p.M;
+    const int pitch = (int)K + 16;                    // codes [16][K + 16]
+    float *scales = (float *)(lds + 16 * pitch);       // [G][16]
+    const int tid = threadIdx.x, nthreads = blockDim.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l16 = lane & 15, q = lane >> 4;
+    const int ct = wave % wn, slice = wave / wn;
+    const int64_t n0 = ((int64_t)blockIdx.x * wn + ct) * 16;  // first column of this wave's tile
+    const int64_t gbeg = (int64_t)slice * GS;
+
+    // activation task (row r, group g) per lane quad, 32 values a lane; quads
+    // past M * G load task 0 again and discard it
+    const int quads = nthreads >> 2, quad = tid >> 2, sub = tid & 3;
+    const int tasks = M * (int)G;
+    uint4 av[PB][QA ? 4 : 2];
+    float sv[PB];
+    auto load_act = [&](int batch) {
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+            int task = quad + quads * (batch * PB + j);
+            task = task < tasks ? task : 0;
+            const int r = task / (int)G, g = task % (int)G;
+            if (QA) {
+                const uint4 *src = (const uint4 *)(p.a + (int64_t)r * K + g * 128 + sub * 32);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) av[j][i] = src[i];
+            } else {
+                const uint4 *src = (const uint4 *)(p.aq + (int64_t)r * K + g * 128 + sub * 32);
+                av[j][0] = src[0];
+                av[j][1] = src[1];
+                sv[j] = p.as[(int64_t)r * G + g];
+            }
+        }
+    };
+    auto quant_act = [&](int batch) {
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+            const int task = quad + quads * (batch * PB + j);
+            if (task < tasks) {  // uniform across the 4 lanes of a quad
+                const int r = task / (int)G, g = task % (int)G;
+                uint4 codes[2];
+                float sc;
+                if (QA) {
+                    uint4 v[4] = {av[j][0], av[j][1], av[j][2], av[j][3]};
+                    quant_group4(v, codes, sc);
+                } else {
+                    codes[0] = av[j][0];
+                    codes[1] = av[j][1];
+                    sc = sv[j];
+                }
+                uint4 *dst = (uint4 *)(lds + r * pitch + g * 128 + sub * 32);
+                dst[0] = codes[0];
+                dst[1] = codes[1];
+                if (sub == 0) scales[g * 16 + r] = sc;
+            }
+        }
+    };
+
+    // the weight slice: 16 rows x GS groups, 2 x 16 B per lane per group
+    uint4 wr[GS][2];
+    const uint8_t *wrow = p.w + (n0 + l16) * K + gbeg * 128 + 16 * q;
+    auto load_w = [&](int chunk) {
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const int g = chunk * CH + j;
+            wr[g][0] = *(const uint4 *)(wrow + g * 128);
+            wr[g][1] = *(const uint4 *)(wrow + g * 128 + 64);
+        }
+    };
+
+    load_act(0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+        load_w(ch);
+        __builtin_amdgcn_sched_barrier(0);
+        if (ch < NB) {
+            quant_act(ch);
+            __builtin_amdgcn_sched_barrier(0);
+            if (ch + 1 < NB) {
+                load_act(ch + 1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- MFMA per group and promotion; the block scales are uniform per wave
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    const int64_t nb = __builtin_amdgcn_readfirstlane((int)(n0 / 128));
+    const float *wsrow = p.ws + nb * G + gbeg;
+#pragma unroll
+    for (int g = 0; g < GS; ++g) {
+        const int gg = (int)gbeg + g;
+        const uint8_t *ap = lds + l16 * pitch + gg * 128 + 16 * q;
+        const v8i af = make_frag(*(const uint4 *)ap, *(const uint4 *)(ap + 64));
+        const float sc = scales[gg * 16 + l16] * wsrow[g];
+        const v4f pr = mfma_e4m3_16x16x128(make_frag(wr[g][0], wr[g][1]), af, zero);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(pr[i], sc, acc[i]);
+    }
+
+    // ---- sum the K slices in ascending order, round, store
+    __syncthreads();                                   // every wave is done reading the codes
+    v4f *red = (v4f *)lds;                             // [wave][64 lanes]
+    if (slice > 0) red[wave * 64 + lane] = acc;
+    __syncthreads();
+    if (slice == 0) {
+        for (int s = 1; s < wk; ++s) acc += red[(s * wn + ct) * 64 + lane];
+        if (l16 < M)
+            *(uint2 *)(p.c + (int64_t)l16 * N + n0 + 4 * q) = bf16x4_rne(acc[0], acc[1], acc[2], acc[3]);
+    }
+}
+
+// (wn, wk, passes) for a shape.  Measured on the MI355X: weight streaming is
+// fastest with CTAs of 2 column tiles x 2 K slices (1-2 CTAs per compute
+// unit), so wn = 2 when that still leaves at least 256 CTAs (else 1), then the
+// smallest K split (K-groups per wave a power of two, at most 16) that gives at
+// least 4 waves per compute unit, at most 8 per CTA.  The activation side needs
+// PASSES = M * (K/128) / (16 * waves) register passes, at most 8 (two batches
+// of 4).  R9K_DECODE_WN / R9K_DECODE_WK override (tuning).
+DecodeCfg decode_config(int64_t M, int64_t K, int64_t N) {
+    DecodeCfg c{0, 0, 0, 0, 0};
+    const int64_t G = K / 128, tiles = N / 16;
+    if (M < 1 || M > 16) return c;
+    const size_t lds = (size_t)16 * (K + 16) + (size_t)G * 16 * 4;
+    if (lds > 150 * 1024) return c;
+    int wn = (tiles % 2 == 0 && tiles / 2 >= 256) ? 2 : 1;
+    if (const char *e = getenv("R9K_DECODE_WN")) {
+        const int v = atoi(e);
+        if (v >= 1 && v <= 4 && tiles % v == 0) wn = v;
+    }
+    int force_wk = 0;
+    if (const char *e = getenv("R9K_DECODE_WK")) force_wk = atoi(e);
+    int wk = 0;
+    for (int cand : {1, 2, 4, 8}) {
+        if (force_wk && cand != force_wk) continue;
+        if (G % cand || wn * cand > 8) continue;
+        const int64_t gs = G / cand;
+        if (gs > MAX_GS || (gs & (gs - 1))) continue;
+        wk = cand;
+        if ((tiles / wn) * wn * cand >= 4 * 256) break;
+    }
+    if (!wk) return c;
+    const int64_t quads = 16 * wn * wk;
+    int passes = 1;
+    while (passes * quads < M * G) passes *= 2;
+    if (passes > 8) return c;
+    const int64_t gs = G / wk, nch = gs < 4 ? gs : 4;
+    if ((passes < 4 ? 1 : passes / 4) > nch) return c;  // each activation batch follows a weight chunk
+    c.wn = wn;
+    c.wk = wk;
+    c.gs = (int)(G / wk);
+    c.passes = passes;
+    // the slice reduction reuses the codes region: one 1 KiB row of v4f per wave
+    c.lds = std::max(lds, (size_t)wn * wk * 64 * 16);
+    return c;
+}
+
+template <bool QA, int GS, int PS>
+static hipError_t set_attr() {
+    return hipFuncSetAttribute((const void *)k_gemm_decode<QA, GS, PS>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+}
+
+template <bool QA, int GS>
+static hipError_t set_attrs_gs() {
+    hipError_t e = hipSuccess;
+    for (hipError_t r : {set_attr<QA, GS, 1>(), set_attr<QA, GS, 2>(), set_attr<QA, GS, 4>()})
+        if (r != hipSuccess) e = r;
+    if constexpr (GS >= 2) {
+        if (hipError_t r = set_attr<QA, GS, 8>(); r != hipSuccess) e = r;
+    }
+    return e;
+}
+
+template <bool QA, int GS>
+static hipError_t launch_ps(const DecodeArgs &a, const DecodeCfg &c, hipStream_t s, dim3 grid, dim3 block) {
+    switch (c.passes) {
+        case 1: hipLaunchKernelGGL((k_gemm_decode<QA, GS, 1>), grid, block, c.lds, s, a, c.wn, c.wk); break;
+        case 2: hipLaunchKernelGGL((k_gemm_decode<QA, GS, 2>), grid, block, c.lds, s, a, c.wn, c.wk); break;
+        case 4: hipLaunchKernelGGL((k_gemm_decode<QA, GS, 4>), grid, block, c.lds, s, a, c.wn, c.wk); break;
+        case 8:
+            if constexpr (GS >= 2) {
+                hipLaunchKernelGGL((k_gemm_decode<QA, GS, 8>), grid, block, c.lds, s, a, c.wn, c.wk);
+                break;
+            }
+            return hipErrorInvalidValue;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <bool QA>
+static hipError_t launch_qa(const DecodeArgs &a, const DecodeCfg &c, hipStream_t s, dim3 grid, dim3 block) {
+    switch (c.gs) {
+        case 1: return launch_ps<QA, 1>(a, c, s, grid, block);
+        case 2: return launch_ps<QA, 2>(a, c, s, grid, block);
+        case 4: return launch_ps<QA, 4>(a, c, s, grid, block);
+        case 8: return launch_ps<QA, 8>(a, c, s, grid, block);
+        case 16: return launch_ps<QA, 16>(a, c, s, grid, block);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_decode(const DecodeArgs &a, const DecodeCfg &c, hipStream_t s) {
+    static std::once_flag once[64];
+    static hipError_t attr_err[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::call_once(once[dev], [&] {
+        hipError_t e = hipSuccess;
+        for (hipError_t r : {set_attrs_gs<true, 1>(), set_attrs_gs<true, 2>(), set_attrs_gs<true, 4>(),
+                             set_attrs_gs<true, 8>(), set_attrs_gs<true, 16>(), set_attrs_gs<false, 1>(),
+                             set_attrs_gs<false, 2>(), set_attrs_gs<false, 4>(), set_attrs_gs<false, 8>(),
+                             set_attrs_gs<false, 16>()})
+            if (r != hipSuccess) e = r;
+        attr_err[dev] = e;
+    });
+    if (attr_err[dev] != hipSuccess) return attr_err[dev];
+    const dim3 grid((unsigned)(a.N / 16 / c.wn));
+    const dim3 block((unsigned)(64 * c.wn * c.wk));
+    return a.a ? launch_qa<true>(a, c, s, grid, block) : launch_qa<false>(a, c, s, grid, block);
+}
+
+}  // namespace r9k

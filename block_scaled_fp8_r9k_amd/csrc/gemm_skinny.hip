@@ -43,11 +43,9 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(SkinnyArgs p, int ksplit, i
     using Smem = SkinnySmem<MT, KC>;
     constexpr int ROWS = Smem::ROWS, PITCH = Smem::PITCH;
     __shared__ Smem sm;
-    __shared__ int s_last;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, q = lane >> 4;
     const int64_t K = p.K, N = p.N, G = K / 128;
-    const int64_t ntiles = N / 128;
     const int64_t nt = blockIdx.x / ksplit;
     const int ks = blockIdx.x % ksplit;
     const int64_t m_base = (int64_t)blockIdx.y * ROWS;
@@ -174,35 +172,28 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(SkinnyArgs p, int ksplit, i
         return;
     }
 
-    // split-K: partial tile [ROWS][128] fp32 per (row chunk, column tile, split)
-    const int64_t tile = (int64_t)blockIdx.y * ntiles + nt;
-    float *part_tile = p.part + tile * (int64_t)ksplit * ROWS * 128;
-    float *mine = part_tile + (int64_t)ks * ROWS * 128;
+    // split-K: this split's fp32 partial of the tile, part[ks][m][n]; the
+    // reduce kernel sums the splits in ascending order
+    float *mine = p.part + (int64_t)ks * p.M * N;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const int r = mt * 16 + l16;
         if (r < rows) {
 #pragma unroll
-            for (int c = 0; c < 2; ++c) *(v4f *)(mine + r * 128 + wave * 32 + 16 * c + 4 * q) = acc[mt][c];
+            for (int c = 0; c < 2; ++c)
+                *(v4f *)(mine + (m_base + r) * N + n_wave + 16 * c + 4 * q) = acc[mt][c];
         }
     }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const unsigned prev = atomicAdd(p.counters + tile, 1u);
-        s_last = (prev == (unsigned)(ksplit - 1));
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    const int n4s = rows * 32;  // float4 units in the valid rows of the tile
-    for (int i = tid; i < n4s; i += 256) {
-        const int r = i >> 5, c4 = i & 31;
-        v4f sum = *(const v4f *)(part_tile + r * 128 + c4 * 4);
-        for (int k = 1; k < ksplit; ++k) sum += *(const v4f *)(part_tile + (int64_t)k * ROWS * 128 + r * 128 + c4 * 4);
-        *(uint2 *)(p.c + (m_base + r) * N + nt * 128 + c4 * 4) = bf16x4_rne(sum[0], sum[1], sum[2], sum[3]);
-    }
-    if (tid == 0) atomicExch(p.counters + tile, 0u);
+}
+
+// C[m][n] = bf16(sum over splits, ascending, of part[ks][m][n]); 4 columns a thread.
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__ part, uint16_t *__restrict__ c,
+                                                       int64_t MN, int ksplit) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= MN) return;
+    v4f sum = *(const v4f *)(part + i);
+    for (int k = 1; k < ksplit; ++k) sum += *(const v4f *)(part + (int64_t)k * MN + i);
+    *(uint2 *)(c + i) = bf16x4_rne(sum[0], sum[1], sum[2], sum[3]);
 }
 
 // ---- configuration ----------------------------------------------------------
@@ -258,12 +249,9 @@ SkinnyCfg skinny_config(int64_t M, int64_t K, int64_t N) {
     return c;
 }
 
-size_t skinny_counter_bytes(const SkinnyCfg &c, int64_t N) {
-    return align_up(sizeof(uint32_t) * (size_t)(N / 128) * c.mchunks, 256);
-}
-size_t skinny_partial_bytes(const SkinnyCfg &c, int64_t N) {
+size_t skinny_partial_bytes(const SkinnyCfg &c, int64_t M, int64_t N) {
     if (c.ksplit <= 1) return 0;
-    return align_up(sizeof(float) * (size_t)c.mchunks * (N / 128) * c.ksplit * (c.mt16 * 16) * 128, 256);
+    return align_up(sizeof(float) * (size_t)c.ksplit * M * N, 256);
 }
 
 template <int MT, int KC>
@@ -288,14 +276,19 @@ static hipError_t launch_m(const SkinnyArgs &a, const SkinnyCfg &c, hipStream_t 
 }
 
 hipError_t launch_gemm_skinny(const SkinnyArgs &a, const SkinnyCfg &c, hipStream_t s) {
+    hipError_t e = hipErrorInvalidValue;
     switch (c.mt16) {
-        case 1: return launch_m<1>(a, c, s);
-        case 2: return launch_m<2>(a, c, s);
-        case 4: return launch_m<4>(a, c, s);
-        case 8: return launch_m<8>(a, c, s);
-        case 16: return launch_m<16>(a, c, s);
+        case 1: e = launch_m<1>(a, c, s); break;
+        case 2: e = launch_m<2>(a, c, s); break;
+        case 4: e = launch_m<4>(a, c, s); break;
+        case 8: e = launch_m<8>(a, c, s); break;
+        case 16: e = launch_m<16>(a, c, s); break;
     }
-    return hipErrorInvalidValue;
+    if (e != hipSuccess || c.ksplit == 1) return e;
+    const int64_t MN = a.M * a.N;
+    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((MN / 4 + 255) / 256)), dim3(256), 0, s, a.part, a.c, MN,
+                       c.ksplit);
+    return hipGetLastError();
 }
 
 }  // namespace r9k

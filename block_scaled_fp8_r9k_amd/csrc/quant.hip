@@ -13,23 +13,28 @@ namespace r9k {
 
 // Group gid covers bf16 [gid*128, gid*128 + 128) of the row-major [M][K]
 // array (row m, group g has gid = m*K/128 + g), which is also where its codes
-// go; its scale goes to as[gid].  16 groups per 256-thread block.
-__global__ __launch_bounds__(256) void k_quant_act(const uint4 *__restrict__ a, uint2 *__restrict__ aq,
+// go; its scale goes to as[gid].  4 lanes (a DPP quad) per group, 32 values a
+// lane, 64 groups per 256-thread block.
+__global__ __launch_bounds__(256) void k_quant_act(const uint4 *__restrict__ a, uint4 *__restrict__ aq,
                                                    float *__restrict__ as, int64_t ngroups) {
-    const int64_t gid = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-    const int l = threadIdx.x & 15;
-    if (gid >= ngroups) return;  // uniform across the 16 lanes of a group
-    uint4 v = load_nt16(a + gid * 16 + l);
+    const int64_t gid = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
+    const int l = threadIdx.x & 3;
+    if (gid >= ngroups) return;  // uniform across the 4 lanes of a group
+    uint4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = a[gid * 16 + l * 4 + i];
+    uint4 codes[2];
     float s;
-    uint2 q = quant_group16(v, s);
-    aq[gid * 16 + l] = q;
+    quant_group4(v, codes, s);
+    aq[gid * 8 + l * 2] = codes[0];
+    aq[gid * 8 + l * 2 + 1] = codes[1];
     if (l == 0) as[gid] = s;
 }
 
 hipError_t launch_quant_act(const uint16_t *a, int64_t M, int64_t K, uint8_t *aq, float *as, hipStream_t s) {
     int64_t ngroups = M * (K / 128);
-    int64_t blocks = (ngroups + 15) / 16;
-    hipLaunchKernelGGL(k_quant_act, dim3((unsigned)blocks), dim3(256), 0, s, (const uint4 *)a, (uint2 *)aq, as,
+    int64_t blocks = (ngroups + 63) / 64;
+    hipLaunchKernelGGL(k_quant_act, dim3((unsigned)blocks), dim3(256), 0, s, (const uint4 *)a, (uint4 *)aq, as,
                        ngroups);
     return hipGetLastError();
 }

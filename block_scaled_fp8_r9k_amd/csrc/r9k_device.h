@@ -63,8 +63,17 @@ __device__ __forceinline__ uint32_t max16_dpp(uint32_t v) {
 
 // ---- group scale and the quotient -----------------------------------------
 
-// s = max(amax, 1e-10f) / 448 as a correctly rounded fp32 division.
-__device__ __forceinline__ float group_scale(float amax) { return fmaxf(amax, 1e-10f) / 448.0f; }
+// s = max(amax, 1e-10f) / 448, the correctly rounded fp32 quotient, as a
+// multiply by RN(1/448) and one fma correction (the same refinement as the
+// element division below); for amax a bf16 value, as it always is here, this
+// equals the division exactly (checked over every bf16 amax on the CPU).
+__device__ __forceinline__ float group_scale(float amax) {
+    const float c = 1.0f / 448.0f;
+    const float x = fmaxf(amax, 1e-10f);
+    const float q0 = x * c;
+    const float e = __builtin_fmaf(-q0, 448.0f, x);
+    return __builtin_fmaf(e, c, q0);
+}
 
 // RN32(a / s) from r = RN32(1 / s) with one correction step:
 // q0 = RN(a r), d = q0 s - a (exact by fma), q = RN(q0 - d r).  This is
@@ -110,6 +119,20 @@ __device__ __forceinline__ uint2 quant_group16(uint4 v, float &scale) {
     float r = 1.0f / s;
     scale = s;
     return quant8(v, s, r);
+}
+
+// One 128-value group spread over the 4 lanes of a DPP quad, 32 values (four
+// uint4 of bf16) per lane: this lane's 32 codes (two uint4) and the scale.
+__device__ __forceinline__ void quant_group4(const uint4 (&v)[4], uint4 (&codes)[2], float &scale) {
+    uint32_t m = max(max(absmax8_bits(v[0]), absmax8_bits(v[1])), max(absmax8_bits(v[2]), absmax8_bits(v[3])));
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
+    const float s = group_scale(__uint_as_float(m << 16));
+    const float r = 1.0f / s;
+    const uint2 a = quant8(v[0], s, r), b = quant8(v[1], s, r), c = quant8(v[2], s, r), d = quant8(v[3], s, r);
+    codes[0] = make_uint4(a.x, a.y, b.x, b.y);
+    codes[1] = make_uint4(c.x, c.y, d.x, d.y);
+    scale = s;
 }
 
 // ---- MFMA --------------------------------------------------------------------

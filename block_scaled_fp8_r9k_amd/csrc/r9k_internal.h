@@ -13,10 +13,31 @@ hipError_t launch_quant_act(const uint16_t *a, int64_t M, int64_t K, uint8_t *aq
 hipError_t launch_quant_weight(const uint16_t *w, int64_t N, int64_t K, uint8_t *wq, float *ws, hipStream_t s);
 hipError_t launch_encode_e4m3(const float *x, int64_t n, uint8_t *codes, hipStream_t s);
 
+// ---- decode engine, 1 <= M <= 16 (gemm_decode.hip) ----
+struct DecodeCfg {
+    int wn;      // 16-column tiles per CTA (0: the shape does not fit this engine)
+    int wk;      // K slices per column tile (waves per CTA = wn * wk)
+    int gs;      // K-groups per wave: (K / 128) / wk
+    int passes;  // activation groups per lane quad
+    size_t lds;  // dynamic LDS bytes
+};
+// fused: the kernel quantises the activations itself; otherwise it reads codes.
+DecodeCfg decode_config(int64_t M, int64_t K, int64_t N);
+struct DecodeArgs {
+    const uint16_t *a;  // bf16 activations (fused form), or NULL
+    const uint8_t *aq;  // pre-quantised codes (split form)
+    const float *as;
+    const uint8_t *w;
+    const float *ws;
+    uint16_t *c;
+    int64_t M, K, N;
+};
+hipError_t launch_gemm_decode(const DecodeArgs &args, const DecodeCfg &cfg, hipStream_t s);
+
 // ---- skinny weight-streaming engine (gemm_skinny.hip) ----
 // One CTA covers 128 output columns (one weight block row), mt16 * 16 rows of
-// A (a chunk of at most 256 rows) and kc K-groups; `ksplit` CTAs share a tile
-// and reduce their fp32 partials in a fixed order (the last one to finish).
+// A (a chunk of at most 256 rows) and kc * nb K-groups; `ksplit` CTAs share a
+// tile, write fp32 partials, and a second kernel sums them in split order.
 struct SkinnyCfg {
     int mt16;    // row tiles of 16 per CTA: 1, 2, 4, 8 or 16
     int kc;      // K-groups (of 128) per batch: the weight bytes one CTA holds in flight
@@ -25,9 +46,8 @@ struct SkinnyCfg {
     int mchunks; // ceil(M / (16 * mt16))
 };
 SkinnyCfg skinny_config(int64_t M, int64_t K, int64_t N);
-// Workspace the skinny engine needs for this config: tile counters, then partials.
-size_t skinny_counter_bytes(const SkinnyCfg &c, int64_t N);
-size_t skinny_partial_bytes(const SkinnyCfg &c, int64_t N);
+// Workspace the skinny engine needs for this config: the split-K partials.
+size_t skinny_partial_bytes(const SkinnyCfg &c, int64_t M, int64_t N);
 
 struct SkinnyArgs {
     const uint16_t *a;  // bf16 activations when quantising in the A-load, else NULL
@@ -36,8 +56,7 @@ struct SkinnyArgs {
     const uint8_t *w;
     const float *ws;
     uint16_t *c;
-    float *part;        // split-K partials
-    uint32_t *counters; // split-K tile counters (zero between calls)
+    float *part;        // split-K partials [ksplit][M][N]
     int64_t M, K, N;
 };
 hipError_t launch_gemm_skinny(const SkinnyArgs &args, const SkinnyCfg &cfg, hipStream_t s);

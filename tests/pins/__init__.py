@@ -32,5 +32,7 @@ def load():
         L.pin_div_correction_mismatches.restype = c_int64
         L.pin_exhaustive.argtypes = [ctypes.c_void_p, c_int, c_int, POINTER(ctypes.c_uint32)]
         L.pin_exhaustive.restype = c_int64
+        L.pin_scale_formula_mismatches.argtypes = []
+        L.pin_scale_formula_mismatches.restype = c_int64
         _lib = L
     return _lib

@@ -211,3 +211,23 @@ int64_t pin_exhaustive(void *fn, int kind, int nt, uint32_t *first) {
     *first = c.first;
     return n;
 }
+
+/* ------------------------------------------------------------------------ */
+/* The group scale as the GPU kernels compute it: x = max(amax, 1e-10f),     */
+/* q0 = RN(x * RN(1/448)), e = fma(-q0, 448, x), s = fma(e, RN(1/448), q0).   */
+/* Returns how many bf16 amax values (0 .. largest finite) give a different   */
+/* s than the correctly rounded x / 448.                                      */
+/* ------------------------------------------------------------------------ */
+int64_t pin_scale_formula_mismatches(void) {
+    const float c = 1.0f / 448.0f, eps = 1e-10f;
+    int64_t bad = 0;
+    for (uint32_t b = 0; b < 0x7F80u; ++b) {
+        float amax = fbits(b << 16);
+        float x = amax > eps ? amax : eps;
+        float q0 = x * c;
+        float e = fmaf(-q0, 448.0f, x);
+        float s = fmaf(e, c, q0);
+        if (ubits(s) != ubits(x / 448.0f)) ++bad;
+    }
+    return bad;
+}

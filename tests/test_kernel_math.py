@@ -14,3 +14,9 @@ import pytest
 def test_division_correction_matches_correct_rounding(pins, ora):
     bad = pins.pin_div_correction_mismatches(0, 0x7F80, ora.threads())
     assert bad == 0
+
+
+def test_scale_formula_matches_division(pins):
+    """s = max(amax, 1e-10f) / 448 by multiply-and-correct equals the correctly
+    rounded division for every bf16 amax."""
+    assert pins.pin_scale_formula_mismatches() == 0
