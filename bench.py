@@ -12,8 +12,11 @@ cannot hold them between launches.  Timing: HIP graphs replayed on the current
 stream, bracketed by HIP events.
 
 The same line carries:
-  roofline      the dominant kernel (the skinny engine at decode widths):
-                algorithmic bytes per launch / its average launch time vs 8 TB/s;
+  roofline      the dominant kernel (k_gemm_decode, the weight-streaming
+                kernel of the decode widths): algorithmic bytes per launch /
+                its average launch time vs 8 TB/s, averaged over the sweep;
+                `traffic` is the HBM bytes per launch that the committed
+                rocprofv3 counter summary measured on the same kernel source;
   cpu_baseline  the CPU oracle timed on one full step of the same inputs;
   prefill       M=4096, K=4096, N=12288: fp8 TFLOP/s vs 5.03 PFLOP/s dense;
   mid           M in {32,64,128,255} at (K,N) = (4096,4096) and (14336,4096);
@@ -94,26 +97,37 @@ def weight_copies(torch, r9k, dev, w_bits, min_bytes=ROTATE_BYTES, cap=16):
     return copies
 
 
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_gemm_decode_sweep_k4096_n14336_traffic.md")
+
+
 def kernel_source_hash():
+    """Hash of the sources that make up the decode kernel and its launch."""
     h = hashlib.sha256()
-    for f in ("gemm_skinny.hip", "r9k_device.h", "api.hip"):
+    for f in ("gemm_decode.hip", "r9k_device.h", "r9k_internal.h", "api.hip"):
         with open(os.path.join(ROOT, "block_scaled_fp8_r9k_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
 def traffic_from_profiles():
-    """HBM bytes per launch of the skinny decode kernel, from the committed
-    rocprofv3 counter summary, if it was taken on the current kernel source."""
-    p = os.path.join(ROOT, "profiles", "skinny_decode_traffic.json")
+    """HBM bytes per launch of the decode kernel over the sweep, from the
+    committed rocprofv3 counter summary (lines `source_hash: ...` and
+    `hbm_bytes_per_launch: ...`), if it was taken on the current source."""
+    fields = {}
     try:
-        with open(p) as fh:
-            t = json.load(fh)
-    except (OSError, ValueError):
+        with open(TRAFFIC_SUMMARY) as fh:
+            for ln in fh:
+                k, sep, v = ln.partition(":")
+                if sep and k.strip() in ("source_hash", "hbm_bytes_per_launch"):
+                    fields[k.strip()] = v.strip().strip("`")
+    except OSError:
         return None
-    if t.get("source_hash") != kernel_source_hash():
+    if fields.get("source_hash") != kernel_source_hash():
         return None
-    return t.get("hbm_bytes_per_launch")
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 # --------------------------------------------------------------------------
@@ -316,7 +330,8 @@ def main():
         line["hbm_frac"] = line["value"] / HBM_PEAK_GBS
         line["roofline"] = dict(bound="hbm", achieved=d["achieved"], peak=HBM_PEAK_GBS, unit="GB/s",
                                 frac=d["achieved"] / HBM_PEAK_GBS, traffic=traffic_from_profiles(),
-                                kernel="k_gemm_skinny (fused act quant), average over the sweep's launches",
+                                kernel="k_gemm_decode (activation quant in the A-load), average over the "
+                                       "sweep's five launches",
                                 bytes_per_launch=d["bytes_avg"], us_per_launch=d["us_avg"])
         line["per_m"] = {str(M): v for M, v in d["per_m"].items()}
         if not args.no_cpu_baseline:
@@ -331,6 +346,7 @@ def main():
     if "moe" in which:
         line["moe"] = bench_moe(torch, r9k, inputs, dev, reps)
     line["copy_GBs_context"] = copy_bandwidth(torch)
+    line["kernel_source_hash"] = kernel_source_hash()
     print(json.dumps(line), flush=True)
 
 

@@ -42,8 +42,7 @@
  *     returns a negative code and launches nothing;
  *   - M == 0 (or T == 0, n == 0) returns R9K_OK without launching;
  *   - faults inside a kernel surface at the caller's next synchronisation;
- *   - unchecked preconditions: inputs are finite; MoE expert ids lie in [0,E)
- *     and are distinct within a token's row.
+ *   - unchecked precondition: inputs are finite.
  */
 #ifndef R9K_H
 #define R9K_H
@@ -105,10 +104,11 @@ int r9k_encode_e4m3(const float *x, int64_t n, uint8_t *codes, void *stream);
 
 /* Workspace bytes that r9k_gemm_fp8_block and r9k_gemm_fp8_block_qa need for
  * this shape, under any dispatch setting.  Host only; touches no device.
- * The workspace must be zero-filled before its first use; every call leaves
- * the part that must start at zero (split-K tile counters) at zero again.
- * Calls that share a workspace must not overlap in time (same stream, or
- * ordered by events).
+ * The workspace holds the activation codes and scales of a call that
+ * quantises once before the GEMM, and the fp32 split-K partial sums of the
+ * skinny engine; every call writes what it reads, so the contents need no
+ * initialisation.  Calls that share a workspace must not overlap in time
+ * (same stream, or ordered by events).
  * Errors: NULLPTR (bytes); SHAPE as for the GEMM. */
 int r9k_gemm_fp8_block_workspace(int64_t M, int64_t K, int64_t N, size_t *bytes);
 
@@ -151,8 +151,9 @@ int r9k_get_dispatch(int *skinny_max_m, int *engine);
 /* MoE decode                                                                */
 /* ------------------------------------------------------------------------ */
 
-/* Workspace bytes for r9k_moe_fp8_decode (host only).  Same zero-fill rule as
- * the GEMM workspace.  Errors: NULLPTR (bytes); SHAPE as for the call. */
+/* Workspace bytes for r9k_moe_fp8_decode (host only).  Needs no
+ * initialisation; calls sharing one must not overlap in time.
+ * Errors: NULLPTR (bytes); SHAPE as for the call. */
 int r9k_moe_fp8_decode_workspace(int64_t T, int64_t H, int64_t E, int64_t I, int64_t topk, size_t *bytes);
 
 /* Routed MoE decode (release v0.3.3, "What changed for someone running it").
@@ -161,6 +162,8 @@ int r9k_moe_fp8_decode_workspace(int64_t T, int64_t H, int64_t E, int64_t I, int
  *   h   = bf16(silu(gate) * up)                              fp32 arithmetic
  *   y   = block GEMM of quant(h) (group 128 along I) against w2[e], fp32
  *   out[t] = bf16(sum_j topk_w[t][j] * y(t,j)), j ascending.
+ * A slot whose id lies outside [0,E) contributes nothing; ids need not be
+ * distinct within a row (a repeated expert is computed once per slot).
  * fused = 1: silu(gate)*up in the gate_up kernel's epilogue and h's row quant
  * in the down kernel's A-load; fused = 0: the three-launch path (gate_up,
  * silu*up + quant, down), bit-identical.  Both end with the ordered combine.
