@@ -6,7 +6,8 @@ Every .hip file under csrc/ is compiled by hipcc in parallel and linked into
 block_scaled_fp8_r9k_amd/libr9k.so.  Flags: the numerics need IEEE fp32
 division and denormals and no contraction of a*b+c into fma behind the code's
 back (the kernels write their fmas explicitly); packed-fp32 instructions are
-turned off.
+turned off.  MFMA results go to ordinary VGPRs: every kernel promotes them with
+VALU FMAs, and results in the accumulator registers would need a move each.
 """
 from __future__ import annotations
 
@@ -27,6 +28,7 @@ CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]

@@ -116,7 +116,22 @@ int run_gemm(const uint16_t *a, const uint8_t *aq, const float *as, int64_t M, i
             return launch_result(launch_gemm_decode(d, dc, s));
         }
     }
-    if (a && (engine == R9K_ENGINE_TILED || M > g_qa_inload_max_m.load())) {
+    if (engine == R9K_ENGINE_TILED) {
+        // the tiled engine reads codes and transposed scales [K/128][M] from
+        // the workspace: quantise A once per call, or transpose the caller's scales
+        float *as_t = (float *)(base + L.as);
+        if (a) {
+            uint8_t *aq_w = base + L.aq;
+            rc = launch_result(launch_quant_act(a, M, K, aq_w, as_t, s, true));
+            aq = aq_w;
+        } else {
+            rc = launch_result(launch_transpose_scales(as, M, K / 128, as_t, s));
+        }
+        if (rc) return rc;
+        TiledArgs t{aq, as_t, w, ws, c, M, K, N};
+        return launch_result(launch_gemm_tiled(t, s));
+    }
+    if (a && M > g_qa_inload_max_m.load()) {
         // quantise A once per call into the workspace, then run on codes
         uint8_t *wq_a = base + L.aq;
         float *ws_a = (float *)(base + L.as);
@@ -125,10 +140,6 @@ int run_gemm(const uint16_t *a, const uint8_t *aq, const float *as, int64_t M, i
         a = nullptr;
         aq = wq_a;
         as = ws_a;
-    }
-    if (engine == R9K_ENGINE_TILED) {
-        TiledArgs t{aq, as, w, ws, c, M, K, N};
-        return launch_result(launch_gemm_tiled(t, s));
     }
     const SkinnyCfg cfg = skinny_config(M, K, N);
     SkinnyArgs sa{a, aq, as, w, ws, c, (float *)(base + L.part), M, K, N};

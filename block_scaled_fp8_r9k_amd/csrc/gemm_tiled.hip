@@ -6,17 +6,29 @@
 // semantics kept here: the K loop steps one 128-wide group at a time, and each
 // group's MFMA sum is promoted with its own scales, acc += P * as[m,g] * ws[n/128,g].
 //
-// Activations arrive pre-quantised (codes + scales): at these widths the
-// fused entry point quantises A once per call in a streaming pre-pass instead
-// of once per column tile, which would cost more VALU time than the MFMAs.
+// Activations arrive pre-quantised, with the scales transposed to [K/128][M]
+// so that a group's scales for consecutive rows are contiguous: at these
+// widths the fused entry point quantises A once per call instead of once per
+// column tile, which would cost more VALU time than the MFMAs.
 //
-// CTA tile: 128 output columns (one weight block row, so one ws per group)
-// x 128 rows; 4 waves in 2 x 2, each 64 n x 64 m = 4 x 4 MFMA tiles of
-// 16 x 16 x 128.  Both operand tiles are [128 rows][128 bytes] in LDS, double
-// buffered (2 x 32 KiB); the next group's tiles are loaded into registers
-// while the current one is multiplied.  The 16-byte chunk c of row r is stored
-// at chunk c ^ ((r >> 1) & 7), so the 16 rows a lane column reads, and the
-// 2 rows x 8 chunks a store instruction writes, fall on distinct banks.
+// CTA tile: 128 rows of A x 256 columns (two weight block rows), 4 waves, one
+// per SIMD, so that each wave has the whole register file (the 128 fp32
+// accumulators, the fragments and the MFMA results in flight).  Wave w owns
+// columns 128 (w & 1) .. +127 (one weight block row, so one weight scale per
+// group) and rows 64 (w >> 1) .. +63: 8 x 4 MFMA tiles of 16 x 16 x 128,
+// computed as C^T = W A^T so that a lane's four outputs of a tile share one
+// row of A, and with it one activation scale.  The promotion is then one
+// multiply per row tile and one FMA per output per group.
+//
+// A stage holds one group: the W tile [256 rows][128 bytes], the A tile
+// [128 rows][128 bytes] and the wave's 64 activation scales; three stages
+// (147 KiB of LDS), filled two groups ahead.  Everything moves from global
+// memory straight into LDS (global_load_lds, no register staging), so one
+// wait on the wave's load counter covers a stage.  A 16-byte load instruction
+// fills 1 KiB of LDS, 8 rows; lane l writes physical chunk l % 8 of its row
+// and fetches the logical chunk that belongs there: chunk c of row r lives at
+// chunk c ^ ((r >> 1) & 7), so the 16 rows a fragment read touches in one LDS
+// cycle fall on distinct banks.
 #include <mutex>
 
 #include "r9k_device.h"
@@ -25,21 +37,58 @@
 namespace r9k {
 
 namespace {
-constexpr int BN = 128, BM = 128;
-constexpr int TILE_BYTES = 128 * 128;
+constexpr int BN = 256;                 // output columns (W rows) per CTA
+constexpr int BM = 128;                 // output rows (A rows) per CTA
+constexpr int WBYTES = BN * 128;        // W tile of a stage
+constexpr int ABYTES = BM * 128;        // A tile of a stage
+constexpr int SBYTES = 4 * 2 * 64 * 4;  // per wave: 64 activation scales, the weight scale x 64
+constexpr int STAGE = WBYTES + ABYTES + SBYTES;
+constexpr int NST = 3;
+constexpr int SMEM = NST * STAGE;
+constexpr int THREADS = 256;
+constexpr int LOADS_PER_STAGE = 8 + 4 + 2;  // per wave: W, A, activation scales, weight scale
+static_assert(SMEM <= 160 * 1024, "LDS");
+
+// Global -> LDS loads (lane l's bytes land at LDS address `l_addr` + size * l,
+// the address taken from M0).  Issued from inline asm so that the compiler
+// neither waits for them at every barrier nor before every LDS read (it cannot
+// tell that the reads touch another stage); the kernel waits for them itself
+// with wait_vm, counting this wave's load instructions.
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)p;
+}
+__device__ __forceinline__ void load_lds16(const uint8_t *g, uint32_t l_addr) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(l_addr) : "memory", "m0");
+}
+__device__ __forceinline__ void load_lds4(const float *g, uint32_t l_addr) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(l_addr) : "memory", "m0");
+}
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
+
+__device__ __forceinline__ v8i frag(const uint8_t *tile, int row, int q) {
+    return make_frag(*(const uint4 *)(tile + swz(row, q)), *(const uint4 *)(tile + swz(row, q + 4)));
+}
+
+// wait until at most VM of this wave's vector-memory instructions are in flight
+template <int VM>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(VM >= 0 && VM < 64, "vmcnt");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(VM) : "memory");
+}
 }  // namespace
 
-__global__ __launch_bounds__(256, 2) void k_gemm_tiled(TiledArgs p) {
-    extern __shared__ __align__(16) uint8_t lds[];  // [2 stages][W tile, A tile]
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, q = lane >> 4;
+__global__ __launch_bounds__(THREADS, 1) void k_gemm_tiled(TiledArgs p) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, q = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wn = wave & 1, wm = wave >> 1;
     const int64_t K = p.K, N = p.N, M = p.M, G = K / 128;
-    const int64_t ntn = N / BN, ntm = (M + BM - 1) / BM;
+    const int64_t ntn = (N + BN - 1) / BN, ntm = (M + BM - 1) / BM;
 
-    // block -> tile: each XCD (blocks are dealt round-robin to 8) gets a
-    // contiguous range of tiles, walked in groups of 8 row tiles so that
-    // concurrently running blocks share weight and activation tiles in L2.
+    // block -> tile.  Blocks are dealt round-robin to the 8 XCDs; each XCD
+    // takes a contiguous range of tiles, walked in groups of GM row tiles, so
+    // that the blocks running together on one XCD share A and W tiles in its L2.
     const int64_t nblk = ntn * ntm;
     int64_t lid = blockIdx.x;
     if (nblk % 8 == 0) lid = (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8;
@@ -48,87 +97,75 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tiled(TiledArgs p) {
     const int64_t first_m = group * GM;
     const int64_t gsz = min<int64_t>(GM, ntm - first_m);
     const int64_t in_group = lid % (GM * ntn);
-    const int64_t mt = first_m + in_group % gsz;
-    const int64_t nt = in_group / gsz;
-    const int64_t n0 = nt * BN, m0 = mt * BM;
+    const int64_t m0 = (first_m + in_group % gsz) * BM;
+    const int64_t n0 = (in_group / gsz) * BN;
 
-    // global -> register loads: thread t moves rows t/8 + 32 i, chunk t % 8
-    const int lrow = tid >> 3, lchunk = tid & 7;
-    const uint8_t *wsrc[4];
+    // This wave's loads of a stage: W instructions 8 wave + u (u < 8) and A
+    // instructions 4 wave + u (u < 4), each 8 rows from row 8 * index + lane / 8,
+    // its 64 activation scales, and its weight scale (every lane the same).  W rows past N (the upper half of a last,
+    // half-full column tile; an instruction's 8 rows are all on one side) read
+    // the lower half instead; A rows past M read row M - 1.  Neither is stored.
+    const uint8_t *wsrc[8];
     const uint8_t *asrc[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = lrow + 32 * i;
-        wsrc[i] = p.w + (n0 + r) * K + lchunk * 16;
-        const int64_t am = min<int64_t>(m0 + r, M - 1);  // rows past M read row M-1; never stored
-        asrc[i] = p.aq + am * K + lchunk * 16;
+    for (int u = 0; u < 8; ++u) {
+        const int row = 8 * (8 * wave + u) + (lane >> 3);
+        const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+        const int64_t wrow = (n0 + 8 * (8 * wave + u) < N) ? n0 + row : n0 + row - 128;
+        wsrc[u] = p.w + wrow * K + 16 * chunk;
     }
-    uint4 wreg[4], areg[4];
-    auto load_tiles = [&](int64_t g) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            wreg[i] = *(const uint4 *)(wsrc[i] + g * 128);
-            areg[i] = *(const uint4 *)(asrc[i] + g * 128);
-        }
-    };
-    auto store_tiles = [&](int stage) {
-        uint8_t *wt = lds + stage * 2 * TILE_BYTES;
-        uint8_t *at = wt + TILE_BYTES;
+    for (int u = 0; u < 4; ++u) {
+        const int row = 8 * (4 * wave + u) + (lane >> 3);
+        const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+        asrc[u] = p.aq + min<int64_t>(m0 + row, M - 1) * K + 16 * chunk;
+    }
+    const float *ssrc = p.as_t + min<int64_t>(m0 + 64 * wm + lane, M - 1);
+    const int64_t nb = min<int64_t>(n0 / 128 + wn, N / 128 - 1);
+    const float *wssrc = p.ws + nb * G;
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
+    auto issue = [&](int64_t g, int st) {
+        const uint32_t sb = lds0 + st * STAGE;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = lrow + 32 * i;
-            *(uint4 *)(wt + swz(r, lchunk)) = wreg[i];
-            *(uint4 *)(at + swz(r, lchunk)) = areg[i];
-        }
+        for (int u = 0; u < 8; ++u) load_lds16(wsrc[u] + g * 128, sb + (8 * wave + u) * 1024);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) load_lds16(asrc[u] + g * 128, sb + WBYTES + (4 * wave + u) * 1024);
+        load_lds4(ssrc + g * M, sb + WBYTES + ABYTES + wave * 512);
+        load_lds4(wssrc + g, sb + WBYTES + ABYTES + wave * 512 + 256);
     };
 
-    // per-lane activation scale rows: m = m0 + wm + 16 j + l16
-    const int wn = (wave & 1) * 64, wm = (wave >> 1) * 64;
-    const float *as_row[4];
+    v4f acc[8][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) as_row[j] = p.as + min<int64_t>(m0 + wm + 16 * j + l16, M - 1) * G;
-    const float *ws_row = p.ws + nt * G;
-
-    v4f acc[4][4];  // [n tile][m tile]
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
 
-    load_tiles(0);
-    store_tiles(0);
-    float sa_next[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sa_next[j] = as_row[j][0];
-    __syncthreads();
-
+    issue(0, 0);
+    if (G > 1) issue(1, 1);
     for (int64_t g = 0; g < G; ++g) {
-        const int stage = (int)(g & 1);
-        float sa[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sa[j] = sa_next[j];
-        const float swg = ws_row[g];
-        if (g + 1 < G) {
-            load_tiles(g + 1);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) sa_next[j] = as_row[j][g + 1];
-        }
-        const uint8_t *wt = lds + stage * 2 * TILE_BYTES;
-        const uint8_t *at = wt + TILE_BYTES;
-        v8i af[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = wm + 16 * j + l16;
-            af[j] = make_frag(*(const uint4 *)(at + swz(r, q)), *(const uint4 *)(at + swz(r, 4 + q)));
-        }
+        const int st = (int)(g % NST);
+        // group g's stage has landed: this wave's loads issued after it are
+        // group g + 1's, if any; then every wave's, and every wave is done
+        // with the stage that group g + 2 will overwrite
+        if (g + 1 < G) wait_vm<LOADS_PER_STAGE>();
+        else wait_vm<0>();
+        __syncthreads();
+        if (g + 2 < G) issue(g + 2, (int)((g + 2) % NST));
+
+        const uint8_t *wt = lds + st * STAGE;
+        const uint8_t *at = wt + WBYTES;
+        const float *sl = (const float *)(at + ABYTES + wave * 512);
+        const float wsg = sl[64 + lane];
         float sc[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sc[j] = sa[j] * swg;
+        for (int j = 0; j < 4; ++j) sc[j] = sl[16 * j + l16] * wsg;
+        v8i af[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = wn + 16 * i + l16;
-            const v8i wf = make_frag(*(const uint4 *)(wt + swz(r, q)), *(const uint4 *)(wt + swz(r, 4 + q)));
+        for (int j = 0; j < 4; ++j) af[j] = frag(at, 64 * wm + 16 * j + l16, q);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const v8i wf = frag(wt, 128 * wn + 16 * i + l16, q);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const v4f pr = mfma_e4m3_16x16x128(wf, af[j], zero);
@@ -136,26 +173,24 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tiled(TiledArgs p) {
                 for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(pr[e], sc[j], acc[i][j][e]);
             }
         }
-        if (g + 1 < G) store_tiles(stage ^ 1);
-        __syncthreads();
     }
 
-    // epilogue: lane holds C[m][n .. n+3] for m = m0 + wm + 16 j + l16, n = n0 + wn + 16 i + 4 q
+    // lane holds, per tile (i, j), row m = m0 + 64 wm + 16 j + l16 and the four
+    // columns n = n0 + 128 wn + 16 i + 4 q .. +3
+    const int64_t nbase = n0 + 128 * wn;
+    if (nbase >= N) return;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int64_t m = m0 + wm + 16 * j + l16;
-        if (m < M) {
+        const int64_t m = m0 + 64 * wm + 16 * j + l16;
+        if (m >= M) continue;
+        uint16_t *crow = p.c + m * N + nbase + 4 * q;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t n = n0 + wn + 16 * i + 4 * q;
-                *(uint2 *)(p.c + m * N + n) = bf16x4_rne(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-            }
-        }
+        for (int i = 0; i < 8; ++i)
+            *(uint2 *)(crow + 16 * i) = bf16x4_rne(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
     }
 }
 
 hipError_t launch_gemm_tiled(const TiledArgs &a, hipStream_t s) {
-    const size_t smem = 2 * 2 * TILE_BYTES;
     // the dynamic LDS limit is a per-device function attribute: set it once per device
     static std::once_flag once[64];
     static hipError_t attr_err[64];
@@ -163,11 +198,11 @@ hipError_t launch_gemm_tiled(const TiledArgs &a, hipStream_t s) {
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     std::call_once(once[dev], [&] {
         attr_err[dev] = hipFuncSetAttribute((const void *)k_gemm_tiled, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                            (int)smem);
+                                            SMEM);
     });
     if (attr_err[dev] != hipSuccess) return attr_err[dev];
-    const int64_t nblk = (a.N / BN) * ((a.M + BM - 1) / BM);
-    hipLaunchKernelGGL(k_gemm_tiled, dim3((unsigned)nblk), dim3(256), smem, s, a);
+    const int64_t nblk = ((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM);
+    hipLaunchKernelGGL(k_gemm_tiled, dim3((unsigned)nblk), dim3(THREADS), SMEM, s, a);
     return hipGetLastError();
 }
 

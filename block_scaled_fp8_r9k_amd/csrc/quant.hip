@@ -15,8 +15,11 @@ namespace r9k {
 // array (row m, group g has gid = m*K/128 + g), which is also where its codes
 // go; its scale goes to as[gid].  4 lanes (a DPP quad) per group, 32 values a
 // lane, 64 groups per 256-thread block.
+// With `transposed`, the scale of row m, group g goes to as[g*M + m] instead
+// (the tiled engine reads the scales of 256 consecutive rows per group).
 __global__ __launch_bounds__(256) void k_quant_act(const uint4 *__restrict__ a, uint4 *__restrict__ aq,
-                                                   float *__restrict__ as, int64_t ngroups) {
+                                                   float *__restrict__ as, int64_t ngroups, int64_t G, int64_t M,
+                                                   bool transposed) {
     const int64_t gid = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
     const int l = threadIdx.x & 3;
     if (gid >= ngroups) return;  // uniform across the 4 lanes of a group
@@ -28,14 +31,30 @@ __global__ __launch_bounds__(256) void k_quant_act(const uint4 *__restrict__ a, 
     quant_group4(v, codes, s);
     aq[gid * 8 + l * 2] = codes[0];
     aq[gid * 8 + l * 2 + 1] = codes[1];
-    if (l == 0) as[gid] = s;
+    if (l == 0) as[transposed ? (gid % G) * M + gid / G : gid] = s;
 }
 
-hipError_t launch_quant_act(const uint16_t *a, int64_t M, int64_t K, uint8_t *aq, float *as, hipStream_t s) {
+hipError_t launch_quant_act(const uint16_t *a, int64_t M, int64_t K, uint8_t *aq, float *as, hipStream_t s,
+                            bool scales_transposed) {
     int64_t ngroups = M * (K / 128);
     int64_t blocks = (ngroups + 63) / 64;
     hipLaunchKernelGGL(k_quant_act, dim3((unsigned)blocks), dim3(256), 0, s, (const uint4 *)a, (uint4 *)aq, as,
-                       ngroups);
+                       ngroups, K / 128, M, scales_transposed);
+    return hipGetLastError();
+}
+
+// as [M][G] -> as_t [G][M]; one thread per scale.
+__global__ __launch_bounds__(256) void k_transpose_scales(const float *__restrict__ as, float *__restrict__ as_t,
+                                                          int64_t M, int64_t G) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // index into as_t
+    if (i >= M * G) return;
+    const int64_t g = i / M, m = i % M;
+    as_t[i] = as[m * G + g];
+}
+
+hipError_t launch_transpose_scales(const float *as, int64_t M, int64_t G, float *as_t, hipStream_t s) {
+    const int64_t n = M * G;
+    hipLaunchKernelGGL(k_transpose_scales, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, as, as_t, M, G);
     return hipGetLastError();
 }
 

@@ -9,7 +9,10 @@
 namespace r9k {
 
 // ---- quantisation (quant.hip) ----
-hipError_t launch_quant_act(const uint16_t *a, int64_t M, int64_t K, uint8_t *aq, float *as, hipStream_t s);
+// scales_transposed: write as [K/128][M] instead of [M][K/128]
+hipError_t launch_quant_act(const uint16_t *a, int64_t M, int64_t K, uint8_t *aq, float *as, hipStream_t s,
+                            bool scales_transposed = false);
+hipError_t launch_transpose_scales(const float *as, int64_t M, int64_t G, float *as_t, hipStream_t s);
 hipError_t launch_quant_weight(const uint16_t *w, int64_t N, int64_t K, uint8_t *wq, float *ws, hipStream_t s);
 hipError_t launch_encode_e4m3(const float *x, int64_t n, uint8_t *codes, hipStream_t s);
 
@@ -62,9 +65,10 @@ struct SkinnyArgs {
 hipError_t launch_gemm_skinny(const SkinnyArgs &args, const SkinnyCfg &cfg, hipStream_t s);
 
 // ---- LDS-tiled MFMA engine (gemm_tiled.hip) ----
+// Activations come pre-quantised, with their scales transposed: as_t [K/128][M].
 struct TiledArgs {
     const uint8_t *aq;
-    const float *as;
+    const float *as_t;
     const uint8_t *w;
     const float *ws;
     uint16_t *c;
