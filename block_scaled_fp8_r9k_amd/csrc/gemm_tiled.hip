@@ -37,17 +37,30 @@
 namespace r9k {
 
 namespace {
-constexpr int BN = 256;                 // output columns (W rows) per CTA
-constexpr int BM = 128;                 // output rows (A rows) per CTA
-constexpr int WBYTES = BN * 128;        // W tile of a stage
-constexpr int ABYTES = BM * 128;        // A tile of a stage
-constexpr int SBYTES = 4 * 2 * 64 * 4;  // per wave: 64 activation scales, the weight scale x 64
-constexpr int STAGE = WBYTES + ABYTES + SBYTES;
-constexpr int NST = 3;
-constexpr int SMEM = NST * STAGE;
-constexpr int THREADS = 256;
-constexpr int LOADS_PER_STAGE = 8 + 4 + 2;  // per wave: W, A, activation scales, weight scale
-static_assert(SMEM <= 160 * 1024, "LDS");
+// Tile shape: WN x WM waves, each TN x 4 MFMA tiles of 16 x 16 (TN * 16
+// columns, 64 rows).  The shape built is 4 x 2 waves of 4 x 4 tiles, a
+// 256 x 128 CTA tile with two waves per SIMD, so that one wave's LDS and
+// barrier waits hide behind the other's MFMAs (one wave per SIMD with 8 x 4
+// tiles each, the same CTA tile, measured slower).
+template <int WN_, int WM_, int TN_>
+struct Cfg {
+    static constexpr int WN = WN_, WM = WM_, TN = TN_, TM = 4;
+    static constexpr int NW = WN * WM, THREADS = 64 * NW;
+    static constexpr int BN = WN * TN * 16;        // output columns (W rows) per CTA
+    static constexpr int BM = WM * TM * 16;        // output rows (A rows) per CTA
+    static constexpr int WBYTES = BN * 128;        // W tile of a stage
+    static constexpr int ABYTES = BM * 128;        // A tile of a stage
+    static constexpr int SBYTES = NW * 2 * 64 * 4; // per wave: 64 activation scales, the weight scale x 64
+    static constexpr int STAGE = WBYTES + ABYTES + SBYTES;
+    static constexpr int NST = 3;
+    static constexpr int SMEM = NST * STAGE;
+    static constexpr int WLOADS = BN / 8 / NW, ALOADS = BM / 8 / NW;  // 1 KiB load instructions per wave
+    static constexpr int LOADS_PER_STAGE = WLOADS + ALOADS + 2;
+    static_assert(SMEM <= 160 * 1024, "LDS");
+    static_assert(WLOADS * NW * 8 == BN && ALOADS * NW * 8 == BM, "loads split evenly");
+    static_assert(TN * 16 <= 128 && 128 % (TN * 16) == 0, "a wave's columns lie in one weight block row");
+};
+using CfgB = Cfg<4, 2, 4>;
 
 // Global -> LDS loads (lane l's bytes land at LDS address `l_addr` + size * l,
 // the address taken from M0).  Issued from inline asm so that the compiler
@@ -57,17 +70,43 @@ static_assert(SMEM <= 160 * 1024, "LDS");
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t *p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)p;
 }
-__device__ __forceinline__ void load_lds16(const uint8_t *g, uint32_t l_addr) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(l_addr) : "memory", "m0");
+// The global address is a wave-uniform base (SGPRs) plus a 32-bit lane offset.
+__device__ __forceinline__ void load_lds16(const void *base, uint32_t off, uint32_t l_addr) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(l_addr)
+                 : "memory", "m0");
 }
-__device__ __forceinline__ void load_lds4(const float *g, uint32_t l_addr) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(l_addr) : "memory", "m0");
+__device__ __forceinline__ void load_lds4(const void *base, uint32_t off, uint32_t l_addr) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(l_addr)
+                 : "memory", "m0");
 }
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
-__device__ __forceinline__ v8i frag(const uint8_t *tile, int row, int q) {
-    return make_frag(*(const uint4 *)(tile + swz(row, q)), *(const uint4 *)(tile + swz(row, q + 4)));
+// an MFMA fragment: 16 bytes at p0 and 16 at p1 (chunks q and q + 4 of a
+// swizzled row; the swizzle leaves bit 6 of the chunk offset alone, so the
+// second chunk's offset is the first one's with bit 6 flipped)
+__device__ __forceinline__ v8i frag2(const uint8_t *p0, const uint8_t *p1) {
+    return make_frag(*(const uint4 *)p0, *(const uint4 *)p1);
+}
+
+// pc = the fp8 MFMA of a and b (unit block exponents); acc += pp * sc, for the
+// products pp of an earlier MFMA.  One asm block, so that the compiler keeps
+// the issue order: each block's FMAs read a result that several MFMAs issued
+// before have long produced, and run while this block's MFMA executes.  The
+// caller guarantees that distance (at least four MFMAs), which also covers
+// the wait the hardware needs before VALU reads an MFMA result.
+__device__ __forceinline__ void mfma_promote(v4f &pc, const v8i &a, const v8i &b, int e127, const v4f &pp,
+                                             float sc, v4f &acc) {
+    float a0 = acc[0], a1 = acc[1], a2 = acc[2], a3 = acc[3];
+    asm volatile(
+        "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %5, %6, 0, %7, %7 op_sel_hi:[0,0,0]\n\t"
+        "v_fmac_f32 %1, %8, %12\n\t"
+        "v_fmac_f32 %2, %9, %12\n\t"
+        "v_fmac_f32 %3, %10, %12\n\t"
+        "v_fmac_f32 %4, %11, %12"
+        : "=&v"(pc), "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3)
+        : "v"(a), "v"(b), "v"(e127), "v"(pp[0]), "v"(pp[1]), "v"(pp[2]), "v"(pp[3]), "v"(sc));
+    acc = v4f{a0, a1, a2, a3};
 }
 
 // wait until at most VM of this wave's vector-memory instructions are in flight
@@ -78,11 +117,14 @@ __device__ __forceinline__ void wait_vm() {
 }
 }  // namespace
 
-__global__ __launch_bounds__(THREADS, 1) void k_gemm_tiled(TiledArgs p) {
+template <class C>
+__global__ __launch_bounds__(C::THREADS, 1) void k_gemm_tiled(TiledArgs p) {
+    constexpr int WN = C::WN, TN = C::TN, BN = C::BN, BM = C::BM, NW = C::NW;
+    constexpr int WBYTES = C::WBYTES, ABYTES = C::ABYTES, STAGE = C::STAGE, NST = C::NST;
     extern __shared__ __align__(16) uint8_t lds[];
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, q = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wn = wave & 1, wm = wave >> 1;
+    const int wn = wave % WN, wm = wave / WN;
     const int64_t K = p.K, N = p.N, M = p.M, G = K / 128;
     const int64_t ntn = (N + BN - 1) / BN, ntm = (M + BM - 1) / BM;
 
@@ -100,46 +142,66 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_tiled(TiledArgs p) {
     const int64_t m0 = (first_m + in_group % gsz) * BM;
     const int64_t n0 = (in_group / gsz) * BN;
 
-    // This wave's loads of a stage: W instructions 8 wave + u (u < 8) and A
-    // instructions 4 wave + u (u < 4), each 8 rows from row 8 * index + lane / 8,
-    // its 64 activation scales, and its weight scale (every lane the same).  W rows past N (the upper half of a last,
-    // half-full column tile; an instruction's 8 rows are all on one side) read
-    // the lower half instead; A rows past M read row M - 1.  Neither is stored.
-    const uint8_t *wsrc[8];
-    const uint8_t *asrc[4];
+    // This wave's loads of a stage: W instructions WLOADS wave + u and A
+    // instructions ALOADS wave + u, each 8 rows from row 8 * index + lane / 8,
+    // its 64 activation scales, and its weight scale (every lane the same).
+    // W rows past N (the upper half of a last, half-full column tile; an
+    // instruction's 8 rows are all on one side) read the lower half instead;
+    // A rows past M read row M - 1.  Neither is ever stored.
+    uint32_t woff[C::WLOADS], aoff[C::ALOADS];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-        const int row = 8 * (8 * wave + u) + (lane >> 3);
+    for (int u = 0; u < C::WLOADS; ++u) {
+        const int idx = C::WLOADS * wave + u;
+        const int row = 8 * idx + (lane >> 3);
         const int chunk = (lane & 7) ^ ((row >> 1) & 7);
-        const int64_t wrow = (n0 + 8 * (8 * wave + u) < N) ? n0 + row : n0 + row - 128;
-        wsrc[u] = p.w + wrow * K + 16 * chunk;
+        const int wrow = (n0 + 8 * idx < N) ? row : row - 128;
+        woff[u] = (uint32_t)wrow * (uint32_t)K + 16 * chunk;
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int row = 8 * (4 * wave + u) + (lane >> 3);
+    for (int u = 0; u < C::ALOADS; ++u) {
+        const int row = 8 * (C::ALOADS * wave + u) + (lane >> 3);
         const int chunk = (lane & 7) ^ ((row >> 1) & 7);
-        asrc[u] = p.aq + min<int64_t>(m0 + row, M - 1) * K + 16 * chunk;
+        aoff[u] = (uint32_t)min<int64_t>(row, M - 1 - m0) * (uint32_t)K + 16 * chunk;
     }
-    const float *ssrc = p.as_t + min<int64_t>(m0 + 64 * wm + lane, M - 1);
-    const int64_t nb = min<int64_t>(n0 / 128 + wn, N / 128 - 1);
-    const float *wssrc = p.ws + nb * G;
+    const uint32_t soff = 4u * (uint32_t)min<int64_t>(m0 + 64 * wm + lane, M - 1);
+    const int64_t nb = min<int64_t>((n0 + TN * 16 * wn) / 128, N / 128 - 1);
+    const uint8_t *wbase = p.w + n0 * K;
+    const uint8_t *abase = p.aq + m0 * K;
+    const float *wsbase = p.ws + nb * G;
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
     auto issue = [&](int64_t g, int st) {
-        const uint32_t sb = lds0 + st * STAGE;
+        const uint32_t sb = lds0 + st * STAGE + C::WLOADS * wave * 1024;
+        const uint32_t sa = lds0 + st * STAGE + WBYTES + C::ALOADS * wave * 1024;
+        const uint32_t ss = lds0 + st * STAGE + WBYTES + ABYTES + wave * 512;
+        const uint8_t *wg = wbase + g * 128, *ag = abase + g * 128;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) load_lds16(wsrc[u] + g * 128, sb + (8 * wave + u) * 1024);
+        for (int u = 0; u < C::WLOADS; ++u) load_lds16(wg, woff[u], sb + u * 1024);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) load_lds16(asrc[u] + g * 128, sb + WBYTES + (4 * wave + u) * 1024);
-        load_lds4(ssrc + g * M, sb + WBYTES + ABYTES + wave * 512);
-        load_lds4(wssrc + g, sb + WBYTES + ABYTES + wave * 512 + 256);
+        for (int u = 0; u < C::ALOADS; ++u) load_lds16(ag, aoff[u], sa + u * 1024);
+        load_lds4(p.as_t + g * M, soff, ss);
+        load_lds4(wsbase + g, 0u, ss + 256);
     };
 
-    v4f acc[8][4];
+    // fragment addresses inside a stage: column tile i of this wave at
+    // wfo + 2048 i (and ^ 64), row tile j at afo + 2048 j (rows 16 apart keep
+    // their swizzle)
+    const int wfo = swz(TN * 16 * wn + l16, q), afo = WBYTES + swz(64 * wm + l16, q);
+    const int wfo2 = wfo ^ 64, afo2 = afo ^ 64;
+
+    v4f acc[TN][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < TN; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    // products and scales of the previous column tile, zero before the first
+    v4f pp[4];
+    float scp[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        pp[j] = v4f{0.f, 0.f, 0.f, 0.f};
+        scp[j] = 0.f;
+    }
+    const int e127 = 127;  // E8M0 block exponent 0: unit scale
 
     issue(0, 0);
     if (G > 1) issue(1, 1);
@@ -148,7 +210,7 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_tiled(TiledArgs p) {
         // group g's stage has landed: this wave's loads issued after it are
         // group g + 1's, if any; then every wave's, and every wave is done
         // with the stage that group g + 2 will overwrite
-        if (g + 1 < G) wait_vm<LOADS_PER_STAGE>();
+        if (g + 1 < G) wait_vm<C::LOADS_PER_STAGE>();
         else wait_vm<0>();
         __syncthreads();
         if (g + 2 < G) issue(g + 2, (int)((g + 2) % NST));
@@ -162,22 +224,36 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_tiled(TiledArgs p) {
         for (int j = 0; j < 4; ++j) sc[j] = sl[16 * j + l16] * wsg;
         v8i af[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) af[j] = frag(at, 64 * wm + 16 * j + l16, q);
+        for (int j = 0; j < 4; ++j) af[j] = frag2(wt + afo + 2048 * j, wt + afo2 + 2048 * j);
+
+        // Column tile i's MFMAs run together with the promotion of tile
+        // i - 1 (tile 0's with the previous group's last tile), so an FMA
+        // reads a product four MFMAs old.
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const v8i wf = frag(wt, 128 * wn + 16 * i + l16, q);
+        for (int i = 0; i < TN; ++i) {
+            const v8i wf = frag2(wt + wfo + 2048 * i, wt + wfo2 + 2048 * i);
+            v4f pc[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const v4f pr = mfma_e4m3_16x16x128(wf, af[j], zero);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(pr[e], sc[j], acc[i][j][e]);
+                if (i == 0) mfma_promote(pc[j], wf, af[j], e127, pp[j], scp[j], acc[TN - 1][j]);
+                else mfma_promote(pc[j], wf, af[j], e127, pp[j], sc[j], acc[i - 1][j]);
             }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pp[j] = pc[j];
         }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) scp[j] = sc[j];
     }
+    // the last group's last tile: wait out the MFMA latency, then promote
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[TN - 1][j][e] = __builtin_fmaf(pp[j][e], scp[j], acc[TN - 1][j][e]);
 
     // lane holds, per tile (i, j), row m = m0 + 64 wm + 16 j + l16 and the four
-    // columns n = n0 + 128 wn + 16 i + 4 q .. +3
-    const int64_t nbase = n0 + 128 * wn;
+    // columns n = n0 + TN 16 wn + 16 i + 4 q .. +3
+    const int64_t nbase = n0 + TN * 16 * wn;
     if (nbase >= N) return;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -185,25 +261,30 @@ __global__ __launch_bounds__(THREADS, 1) void k_gemm_tiled(TiledArgs p) {
         if (m >= M) continue;
         uint16_t *crow = p.c + m * N + nbase + 4 * q;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < TN; ++i)
             *(uint2 *)(crow + 16 * i) = bf16x4_rne(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
     }
 }
 
-hipError_t launch_gemm_tiled(const TiledArgs &a, hipStream_t s) {
+template <class C>
+static hipError_t launch_cfg(const TiledArgs &a, hipStream_t s) {
     // the dynamic LDS limit is a per-device function attribute: set it once per device
     static std::once_flag once[64];
     static hipError_t attr_err[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     std::call_once(once[dev], [&] {
-        attr_err[dev] = hipFuncSetAttribute((const void *)k_gemm_tiled, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                            SMEM);
+        attr_err[dev] = hipFuncSetAttribute((const void *)k_gemm_tiled<C>,
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, C::SMEM);
     });
     if (attr_err[dev] != hipSuccess) return attr_err[dev];
-    const int64_t nblk = ((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM);
-    hipLaunchKernelGGL(k_gemm_tiled, dim3((unsigned)nblk), dim3(THREADS), SMEM, s, a);
+    const int64_t nblk = ((a.N + C::BN - 1) / C::BN) * ((a.M + C::BM - 1) / C::BM);
+    hipLaunchKernelGGL(k_gemm_tiled<C>, dim3((unsigned)nblk), dim3(C::THREADS), C::SMEM, s, a);
     return hipGetLastError();
+}
+
+hipError_t launch_gemm_tiled(const TiledArgs &a, hipStream_t s) {
+    return launch_cfg<CfgB>(a, s);
 }
 
 }  // namespace r9k
