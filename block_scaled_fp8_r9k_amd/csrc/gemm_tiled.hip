@@ -38,11 +38,13 @@ namespace r9k {
 
 namespace {
 // Tile shape: WN x WM waves, each TN x 4 MFMA tiles of 16 x 16 (TN * 16
-// columns, 64 rows).  The shape built is 4 x 2 waves of 4 x 4 tiles, a
-// 256 x 128 CTA tile with two waves per SIMD, so that one wave's LDS and
-// barrier waits hide behind the other's MFMAs (one wave per SIMD with 8 x 4
-// tiles each, the same CTA tile, measured slower).
-template <int WN_, int WM_, int TN_>
+// columns, 64 rows), two waves per SIMD so that one wave's LDS and barrier
+// waits hide behind the other's MFMAs.  Two shapes are built:
+//   C: 2 x 4 waves of 8 x 4 tiles, a 256 x 256 CTA tile, two LDS stages;
+//   B: 4 x 2 waves of 4 x 4 tiles, a 256 x 128 CTA tile, three LDS stages.
+// C reads 0.75 KiB of LDS per MFMA instead of 1 KiB and moves a third less
+// from L2 per flop; B makes twice as many CTAs for shapes too small for C.
+template <int WN_, int WM_, int TN_, int NST_>
 struct Cfg {
     static constexpr int WN = WN_, WM = WM_, TN = TN_, TM = 4;
     static constexpr int NW = WN * WM, THREADS = 64 * NW;
@@ -52,15 +54,17 @@ struct Cfg {
     static constexpr int ABYTES = BM * 128;        // A tile of a stage
     static constexpr int SBYTES = NW * 2 * 64 * 4; // per wave: 64 activation scales, the weight scale x 64
     static constexpr int STAGE = WBYTES + ABYTES + SBYTES;
-    static constexpr int NST = 3;
+    static constexpr int NST = NST_;  // stages in the LDS ring; loads run NST - 1 groups ahead
     static constexpr int SMEM = NST * STAGE;
     static constexpr int WLOADS = BN / 8 / NW, ALOADS = BM / 8 / NW;  // 1 KiB load instructions per wave
     static constexpr int LOADS_PER_STAGE = WLOADS + ALOADS + 2;
     static_assert(SMEM <= 160 * 1024, "LDS");
+    static_assert(NST == 2 || NST == 3, "stages");
     static_assert(WLOADS * NW * 8 == BN && ALOADS * NW * 8 == BM, "loads split evenly");
     static_assert(TN * 16 <= 128 && 128 % (TN * 16) == 0, "a wave's columns lie in one weight block row");
 };
-using CfgB = Cfg<4, 2, 4>;
+using CfgB = Cfg<4, 2, 4, 3>;
+using CfgC = Cfg<2, 4, 8, 2>;
 
 // Global -> LDS loads (lane l's bytes land at LDS address `l_addr` + size * l,
 // the address taken from M0).  Issued from inline asm so that the compiler
@@ -203,17 +207,19 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_gemm_tiled(TiledArgs p) {
     }
     const int e127 = 127;  // E8M0 block exponent 0: unit scale
 
-    issue(0, 0);
-    if (G > 1) issue(1, 1);
+#pragma unroll
+    for (int k = 0; k < NST - 1; ++k)
+        if (k < G) issue(k, k);
     for (int64_t g = 0; g < G; ++g) {
         const int st = (int)(g % NST);
         // group g's stage has landed: this wave's loads issued after it are
-        // group g + 1's, if any; then every wave's, and every wave is done
-        // with the stage that group g + 2 will overwrite
-        if (g + 1 < G) wait_vm<C::LOADS_PER_STAGE>();
+        // those of groups g + 1 .. g + NST - 2 (three stages: g + 1, if any);
+        // then every wave's, and every wave is done with the stage that
+        // group g + NST - 1 will overwrite
+        if (NST == 3 && g + 1 < G) wait_vm<C::LOADS_PER_STAGE>();
         else wait_vm<0>();
         __syncthreads();
-        if (g + 2 < G) issue(g + 2, (int)((g + 2) % NST));
+        if (g + NST - 1 < G) issue(g + NST - 1, (int)((g + NST - 1) % NST));
 
         const uint8_t *wt = lds + st * STAGE;
         const uint8_t *at = wt + WBYTES;
@@ -229,17 +235,27 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_gemm_tiled(TiledArgs p) {
         // Column tile i's MFMAs run together with the promotion of tile
         // i - 1 (tile 0's with the previous group's last tile), so an FMA
         // reads a product four MFMAs old.
+        // With eight column tiles the next tile's fragment is read only after
+        // this tile's first block (its offset passes through an empty asm, so
+        // the compiler cannot hoist all eight reads and run out of registers).
+        v8i wf = frag2(wt + wfo, wt + wfo2);
 #pragma unroll
         for (int i = 0; i < TN; ++i) {
-            const v8i wf = frag2(wt + wfo + 2048 * i, wt + wfo2 + 2048 * i);
             v4f pc[4];
+            v8i wfn;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 if (i == 0) mfma_promote(pc[j], wf, af[j], e127, pp[j], scp[j], acc[TN - 1][j]);
                 else mfma_promote(pc[j], wf, af[j], e127, pp[j], sc[j], acc[i - 1][j]);
+                if (j == 0 && i + 1 < TN) {
+                    int o1 = wfo + 2048 * (i + 1), o2 = wfo2 + 2048 * (i + 1);
+                    if (TN > 4) asm volatile("" : "+v"(o1), "+v"(o2));
+                    wfn = frag2(wt + o1, wt + o2);
+                }
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) pp[j] = pc[j];
+            if (i + 1 < TN) wf = wfn;
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) scp[j] = sc[j];
@@ -284,7 +300,16 @@ static hipError_t launch_cfg(const TiledArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_gemm_tiled(const TiledArgs &a, hipStream_t s) {
-    return launch_cfg<CfgB>(a, s);
+    // the 256 x 256 tile moves a third less data per flop and reads less LDS
+    // per MFMA; below one CTA per compute unit the 256 x 128 tile keeps more
+    // of the chip busy.  R9K_TILED_CFG=b|c forces one (tuning).
+    static const int force = [] {
+        const char *e = getenv("R9K_TILED_CFG");
+        return e ? (int)e[0] : 0;
+    }();
+    const int64_t ctas_c = ((a.N + CfgC::BN - 1) / CfgC::BN) * ((a.M + CfgC::BM - 1) / CfgC::BM);
+    const bool use_c = force ? force == 'c' : ctas_c >= 256;
+    return use_c ? launch_cfg<CfgC>(a, s) : launch_cfg<CfgB>(a, s);
 }
 
 }  // namespace r9k
