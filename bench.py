@@ -132,15 +132,22 @@ def traffic_from_profiles():
 
 # --------------------------------------------------------------------------
 
-def bench_decode(torch, r9k, inputs, dev, steps, warmup):
+def bench_decode(torch, r9k, inputs, dev, steps, warmup, packed=True):
+    """The decode sweep.  packed: the weights in fragment order (r9k_pack_weight,
+    done once at load like the quantisation, not timed); else row-major."""
     K, N = DECODE_K, DECODE_N
     Mmax = max(DECODE_M)
     a_bits = inputs.activations(0, Mmax, K, outliers=True)
     w_bits = inputs.weights(0, N, K)
     a = dev(a_bits)
     copies = weight_copies(torch, r9k, dev, w_bits)
+    if packed:
+        copies = [(r9k.pack_weight(wq), ws) for wq, ws in copies]
+        torch.cuda.synchronize()
+    gemm = r9k.gemm_fp8_block_qa_packed if packed else r9k.gemm_fp8_block_qa
     C = len(copies)
-    log(f"decode: {C} weight copies of {copies[0][0].numel() / 1e6:.1f} MB")
+    log(f"decode ({'packed' if packed else 'row-major'} weights): {C} weight copies of "
+        f"{copies[0][0].numel() / 1e6:.1f} MB")
     ws_bytes = max(r9k.gemm_fp8_block_workspace(M, K, N) for M in DECODE_M)
     wsp = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
     outs = {M: torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for M in DECODE_M}
@@ -148,7 +155,7 @@ def bench_decode(torch, r9k, inputs, dev, steps, warmup):
 
     def call(M, c):
         wq, ws = copies[c]
-        return lambda: r9k.gemm_fp8_block_qa(a_rows[M], wq, ws, c=outs[M], workspace=wsp)
+        return lambda: gemm(a_rows[M], wq, ws, c=outs[M], workspace=wsp)
 
     for c in range(C):  # eager warm-up of every call
         for M in DECODE_M:
@@ -170,6 +177,8 @@ def bench_decode(torch, r9k, inputs, dev, steps, warmup):
         b = gemm_bytes(M, K, N)
         per_m[M] = dict(us=ms * 1e3, GBs=b / (ms * 1e-3) / 1e9)
         log(f"decode M={M}: {ms * 1e3:.2f} us/launch, {per_m[M]['GBs']:.0f} GB/s")
+    del step_graphs, copies
+    torch.cuda.empty_cache()
     us_avg = float(np.mean([per_m[M]["us"] for M in DECODE_M]))
     bytes_avg = float(np.mean([gemm_bytes(M, K, N) for M in DECODE_M]))
     achieved = bytes_avg / (us_avg * 1e-6) / 1e9
@@ -324,7 +333,10 @@ def main():
                                      "per token in groups of 128 inside the GEMM, fp8 e4m3 weights with 128x128 "
                                      "fp32 block scales, bf16 out", M=list(DECODE_M), K=DECODE_K, N=DECODE_N))
     if "decode" in which:
-        d = bench_decode(torch, r9k, inputs, dev, args.steps, args.warmup)
+        drm = bench_decode(torch, r9k, inputs, dev, args.steps, args.warmup, packed=False)
+        line["per_m_row_major"] = {str(M): v for M, v in drm["per_m"].items()}
+        line["value_row_major"] = drm["step_bytes"] / (drm["ms_step"] * 1e-3) / 1e9
+        d = bench_decode(torch, r9k, inputs, dev, args.steps, args.warmup, packed=True)
         line["value"] = d["step_bytes"] / (d["ms_step"] * 1e-3) / 1e9
         line["ms_per_step"] = d["ms_step"]
         line["hbm_frac"] = line["value"] / HBM_PEAK_GBS

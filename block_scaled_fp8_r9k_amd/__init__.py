@@ -20,7 +20,7 @@ from ctypes import POINTER, c_char_p, c_int, c_int64, c_size_t, c_void_p
 
 import torch
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 ENGINE_AUTO, ENGINE_SKINNY, ENGINE_TILED = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -53,6 +53,9 @@ def lib() -> ctypes.CDLL:
                                          c_void_p, c_void_p, c_size_t, c_void_p]
         L.r9k_gemm_fp8_block_qa.argtypes = [c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_int64, c_void_p,
                                             c_void_p, c_size_t, c_void_p]
+        L.r9k_gemm_fp8_block_packed.argtypes = L.r9k_gemm_fp8_block.argtypes
+        L.r9k_gemm_fp8_block_qa_packed.argtypes = L.r9k_gemm_fp8_block_qa.argtypes
+        L.r9k_pack_weight.argtypes = [c_void_p, c_int64, c_int64, c_void_p, c_void_p]
         L.r9k_set_dispatch.argtypes = [c_int, c_int]
         L.r9k_get_dispatch.argtypes = [POINTER(c_int), POINTER(c_int)]
         L.r9k_moe_fp8_decode_workspace.argtypes = [c_int64] * 5 + [POINTER(c_size_t)]
@@ -202,6 +205,46 @@ def gemm_fp8_block_qa(a, w, ws, c=None, workspace=None, stream=None) -> torch.Te
     _check(lib().r9k_gemm_fp8_block_qa(_ptr(a, BF16, "a"), M, K, _ptr(w, FP8, "w"), _ptr(ws, F32, "ws"), N,
                                        _ptr(c, BF16, "c"), _ptr(wsb, FP8, "workspace"), wsb.numel(),
                                        _stream(stream)), "r9k_gemm_fp8_block_qa")
+    return c
+
+
+def pack_weight(wq: torch.Tensor, wp: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Fragment-order copy of the weight codes (r9k_pack_weight): wq [N,K] u8
+    row-major -> wp, also [N,K] u8 in shape, bytes in fragment order."""
+    N, K = wq.shape
+    if wp is None:
+        wp = torch.empty((N, K), dtype=torch.uint8, device=wq.device)
+    _check(lib().r9k_pack_weight(_ptr(wq, FP8, "wq"), N, K, _ptr(wp, FP8, "wp"), _stream(stream)),
+           "r9k_pack_weight")
+    return wp
+
+
+def gemm_fp8_block_packed(aq, as_, wp, ws, c=None, workspace=None, stream=None) -> torch.Tensor:
+    """gemm_fp8_block on fragment-order weights (pack_weight)."""
+    M, K = aq.shape
+    N = wp.shape[0]
+    if c is None:
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=aq.device)
+    nbytes = gemm_fp8_block_workspace(M, K, N)
+    wsb = _workspace(workspace, nbytes)
+    _check(lib().r9k_gemm_fp8_block_packed(_ptr(aq, FP8, "aq"), _ptr(as_, F32, "as"), M, K, _ptr(wp, FP8, "wp"),
+                                           _ptr(ws, F32, "ws"), N, _ptr(c, BF16, "c"),
+                                           _ptr(wsb, FP8, "workspace"), wsb.numel(), _stream(stream)),
+           "r9k_gemm_fp8_block_packed")
+    return c
+
+
+def gemm_fp8_block_qa_packed(a, wp, ws, c=None, workspace=None, stream=None) -> torch.Tensor:
+    """gemm_fp8_block_qa on fragment-order weights (pack_weight)."""
+    M, K = a.shape
+    N = wp.shape[0]
+    if c is None:
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    nbytes = gemm_fp8_block_workspace(M, K, N)
+    wsb = _workspace(workspace, nbytes)
+    _check(lib().r9k_gemm_fp8_block_qa_packed(_ptr(a, BF16, "a"), M, K, _ptr(wp, FP8, "wp"), _ptr(ws, F32, "ws"),
+                                              N, _ptr(c, BF16, "c"), _ptr(wsb, FP8, "workspace"), wsb.numel(),
+                                              _stream(stream)), "r9k_gemm_fp8_block_qa_packed")
     return c
 
 

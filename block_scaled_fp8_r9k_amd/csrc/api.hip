@@ -99,7 +99,8 @@ GemmWs gemm_ws(int64_t M, int64_t K, int64_t N) {
 int launch_result(hipError_t e) { return e == hipSuccess ? R9K_OK : R9K_ERR_LAUNCH; }
 
 int run_gemm(const uint16_t *a, const uint8_t *aq, const float *as, int64_t M, int64_t K, const uint8_t *w,
-             const float *ws, int64_t N, uint16_t *c, void *workspace, size_t ws_bytes, hipStream_t s) {
+             const float *ws, int64_t N, uint16_t *c, void *workspace, size_t ws_bytes, hipStream_t s,
+             bool packed) {
     if (M == 0) return R9K_OK;
     const GemmWs L = gemm_ws(M, K, N);
     if (ws_bytes < L.total) return R9K_ERR_WORKSPACE;
@@ -112,7 +113,7 @@ int run_gemm(const uint16_t *a, const uint8_t *aq, const float *as, int64_t M, i
         // fits it, with the activation quant in its A-load
         const DecodeCfg dc = decode_config(M, K, N);
         if (dc.wn) {
-            DecodeArgs d{a, aq, as, w, ws, c, M, K, N};
+            DecodeArgs d{a, aq, as, w, ws, c, M, K, N, packed};
             return launch_result(launch_gemm_decode(d, dc, s));
         }
     }
@@ -128,7 +129,7 @@ int run_gemm(const uint16_t *a, const uint8_t *aq, const float *as, int64_t M, i
             rc = launch_result(launch_transpose_scales(as, M, K / 128, as_t, s));
         }
         if (rc) return rc;
-        TiledArgs t{aq, as_t, w, ws, c, M, K, N};
+        TiledArgs t{aq, as_t, w, ws, c, M, K, N, packed};
         return launch_result(launch_gemm_tiled(t, s));
     }
     if (a && M > g_qa_inload_max_m.load()) {
@@ -142,7 +143,7 @@ int run_gemm(const uint16_t *a, const uint8_t *aq, const float *as, int64_t M, i
         as = ws_a;
     }
     const SkinnyCfg cfg = skinny_config(M, K, N);
-    SkinnyArgs sa{a, aq, as, w, ws, c, (float *)(base + L.part), M, K, N};
+    SkinnyArgs sa{a, aq, as, w, ws, c, (float *)(base + L.part), M, K, N, packed};
     return launch_result(launch_gemm_skinny(sa, cfg, s));
 }
 
@@ -205,7 +206,18 @@ int r9k_gemm_fp8_block(const uint8_t *aq, const float *as, int64_t M, int64_t K,
     if (int rc = check_gemm_shape(M, K, N)) return rc;
     if (!aligned16(aq) || !aligned16(as) || !aligned16(w) || !aligned16(ws) || !aligned16(c) || !aligned16(workspace))
         return R9K_ERR_ALIGN;
-    return run_gemm(nullptr, aq, as, M, K, w, ws, N, c, workspace, ws_bytes, (hipStream_t)stream);
+    return run_gemm(nullptr, aq, as, M, K, w, ws, N, c, workspace, ws_bytes, (hipStream_t)stream, false);
+}
+
+int r9k_gemm_fp8_block_packed(const uint8_t *aq, const float *as, int64_t M, int64_t K, const uint8_t *wp,
+                              const float *ws, int64_t N, uint16_t *c, void *workspace, size_t ws_bytes,
+                              void *stream) {
+    if (!aq || !as || !wp || !ws || !c || !workspace) return R9K_ERR_NULLPTR;
+    if (int rc = check_gemm_shape(M, K, N)) return rc;
+    if (!aligned16(aq) || !aligned16(as) || !aligned16(wp) || !aligned16(ws) || !aligned16(c) ||
+        !aligned16(workspace))
+        return R9K_ERR_ALIGN;
+    return run_gemm(nullptr, aq, as, M, K, wp, ws, N, c, workspace, ws_bytes, (hipStream_t)stream, true);
 }
 
 int r9k_gemm_fp8_block_qa(const uint16_t *a, int64_t M, int64_t K, const uint8_t *w, const float *ws, int64_t N,
@@ -214,7 +226,26 @@ int r9k_gemm_fp8_block_qa(const uint16_t *a, int64_t M, int64_t K, const uint8_t
     if (int rc = check_gemm_shape(M, K, N)) return rc;
     if (!aligned16(a) || !aligned16(w) || !aligned16(ws) || !aligned16(c) || !aligned16(workspace))
         return R9K_ERR_ALIGN;
-    return run_gemm(a, nullptr, nullptr, M, K, w, ws, N, c, workspace, ws_bytes, (hipStream_t)stream);
+    return run_gemm(a, nullptr, nullptr, M, K, w, ws, N, c, workspace, ws_bytes, (hipStream_t)stream, false);
+}
+
+int r9k_gemm_fp8_block_qa_packed(const uint16_t *a, int64_t M, int64_t K, const uint8_t *wp, const float *ws,
+                                 int64_t N, uint16_t *c, void *workspace, size_t ws_bytes, void *stream) {
+    if (!a || !wp || !ws || !c || !workspace) return R9K_ERR_NULLPTR;
+    if (int rc = check_gemm_shape(M, K, N)) return rc;
+    if (!aligned16(a) || !aligned16(wp) || !aligned16(ws) || !aligned16(c) || !aligned16(workspace))
+        return R9K_ERR_ALIGN;
+    return run_gemm(a, nullptr, nullptr, M, K, wp, ws, N, c, workspace, ws_bytes, (hipStream_t)stream, true);
+}
+
+int r9k_pack_weight(const uint8_t *wq, int64_t N, int64_t K, uint8_t *wp, void *stream) {
+    if (!wq || !wp) return R9K_ERR_NULLPTR;
+    if (N <= 0 || K <= 0 || N % 128 || K % 128 || N > MAX_DIM || K > MAX_DIM) return R9K_ERR_SHAPE;
+    if (!aligned16(wq) || !aligned16(wp)) return R9K_ERR_ALIGN;
+    const uintptr_t lo = (uintptr_t)wq, hi = lo + (uintptr_t)(N * K), plo = (uintptr_t)wp;
+    if (plo < hi && lo < plo + (uintptr_t)(N * K)) return R9K_ERR_ARG;  // in place is not supported
+    if (int rc = check_device()) return rc;
+    return launch_result(launch_pack_weight(wq, N, K, wp, (hipStream_t)stream));
 }
 
 int r9k_set_dispatch(int skinny_max_m, int engine) {

@@ -48,7 +48,12 @@ constexpr int MAX_GS = 16;  // K-groups per wave: 32 x 16-byte loads per lane
 // batch 0, activation batch 1, weight chunk 1, quantise batch 1, remaining
 // weight chunks.  Loads of one wave complete in issue order, so each quantise
 // step waits only for its own batch and the chunks issued before it.
-template <bool QA, int GS, int PASSES>
+//
+// PK: the weights are in fragment order (r9k_pack_weight), so a wave's slice
+// is one contiguous run and every 16-byte load instruction reads 1 KiB of
+// consecutive bytes; the registers receive exactly what the row-major loads
+// would give them.
+template <bool QA, bool PK, int GS, int PASSES>
 __global__ __launch_bounds__(512) void k_gemm_decode(DecodeArgs p, int wn, int wk) {
     constexpr int PB = PASSES < 4 ? PASSES : 4;      // passes per activation batch
     constexpr int NB = PASSES / PB;                  // activation batches (1 or 2)
@@ -117,13 +122,19 @@ __global__ __launch_bounds__(512) void k_gemm_decode(DecodeArgs p, int wn, int w
 
     // the weight slice: 16 rows x GS groups, 2 x 16 B per lane per group
     uint4 wr[GS][2];
-    const uint8_t *wrow = p.w + (n0 + l16) * K + gbeg * 128 + 16 * q;
+    const uint8_t *wrow = PK ? p.w + ((n0 / 16) * G + gbeg) * 2048 + 16 * lane
+                             : p.w + (n0 + l16) * K + gbeg * 128 + 16 * q;
     auto load_w = [&](int chunk) {
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
             const int g = chunk * CH + j;
-            wr[g][0] = *(const uint4 *)(wrow + g * 128);
-            wr[g][1] = *(const uint4 *)(wrow + g * 128 + 64);
+            if (PK) {
+                wr[g][0] = *(const uint4 *)(wrow + g * 2048);
+                wr[g][1] = *(const uint4 *)(wrow + g * 2048 + 1024);
+            } else {
+                wr[g][0] = *(const uint4 *)(wrow + g * 128);
+                wr[g][1] = *(const uint4 *)(wrow + g * 128 + 64);
+            }
         }
     };
 
@@ -217,70 +228,52 @@ DecodeCfg decode_config(int64_t M, int64_t K, int64_t N) {
     return c;
 }
 
-template <bool QA, int GS, int PS>
-static hipError_t set_attr() {
-    return hipFuncSetAttribute((const void *)k_gemm_decode<QA, GS, PS>,
-                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-}
-
-template <bool QA, int GS>
-static hipError_t set_attrs_gs() {
-    hipError_t e = hipSuccess;
-    for (hipError_t r : {set_attr<QA, GS, 1>(), set_attr<QA, GS, 2>(), set_attr<QA, GS, 4>()})
-        if (r != hipSuccess) e = r;
-    if constexpr (GS >= 2) {
-        if (hipError_t r = set_attr<QA, GS, 8>(); r != hipSuccess) e = r;
-    }
-    return e;
-}
-
-template <bool QA, int GS>
-static hipError_t launch_ps(const DecodeArgs &a, const DecodeCfg &c, hipStream_t s, dim3 grid, dim3 block) {
-    switch (c.passes) {
-        case 1: hipLaunchKernelGGL((k_gemm_decode<QA, GS, 1>), grid, block, c.lds, s, a, c.wn, c.wk); break;
-        case 2: hipLaunchKernelGGL((k_gemm_decode<QA, GS, 2>), grid, block, c.lds, s, a, c.wn, c.wk); break;
-        case 4: hipLaunchKernelGGL((k_gemm_decode<QA, GS, 4>), grid, block, c.lds, s, a, c.wn, c.wk); break;
-        case 8:
-            if constexpr (GS >= 2) {
-                hipLaunchKernelGGL((k_gemm_decode<QA, GS, 8>), grid, block, c.lds, s, a, c.wn, c.wk);
-                break;
-            }
-            return hipErrorInvalidValue;
-        default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-}
-
-template <bool QA>
-static hipError_t launch_qa(const DecodeArgs &a, const DecodeCfg &c, hipStream_t s, dim3 grid, dim3 block) {
-    switch (c.gs) {
-        case 1: return launch_ps<QA, 1>(a, c, s, grid, block);
-        case 2: return launch_ps<QA, 2>(a, c, s, grid, block);
-        case 4: return launch_ps<QA, 4>(a, c, s, grid, block);
-        case 8: return launch_ps<QA, 8>(a, c, s, grid, block);
-        case 16: return launch_ps<QA, 16>(a, c, s, grid, block);
-    }
-    return hipErrorInvalidValue;
-}
-
-hipError_t launch_gemm_decode(const DecodeArgs &a, const DecodeCfg &c, hipStream_t s) {
+// one instantiation: its 160 KiB dynamic-LDS limit is set once per device
+template <bool QA, bool PK, int GS, int PS>
+static hipError_t launch_one(const DecodeArgs &a, const DecodeCfg &c, hipStream_t s, dim3 grid, dim3 block) {
     static std::once_flag once[64];
     static hipError_t attr_err[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     std::call_once(once[dev], [&] {
-        hipError_t e = hipSuccess;
-        for (hipError_t r : {set_attrs_gs<true, 1>(), set_attrs_gs<true, 2>(), set_attrs_gs<true, 4>(),
-                             set_attrs_gs<true, 8>(), set_attrs_gs<true, 16>(), set_attrs_gs<false, 1>(),
-                             set_attrs_gs<false, 2>(), set_attrs_gs<false, 4>(), set_attrs_gs<false, 8>(),
-                             set_attrs_gs<false, 16>()})
-            if (r != hipSuccess) e = r;
-        attr_err[dev] = e;
+        attr_err[dev] = hipFuncSetAttribute((const void *)k_gemm_decode<QA, PK, GS, PS>,
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     });
     if (attr_err[dev] != hipSuccess) return attr_err[dev];
+    hipLaunchKernelGGL((k_gemm_decode<QA, PK, GS, PS>), grid, block, c.lds, s, a, c.wn, c.wk);
+    return hipGetLastError();
+}
+
+template <bool QA, bool PK, int GS>
+static hipError_t launch_ps(const DecodeArgs &a, const DecodeCfg &c, hipStream_t s, dim3 grid, dim3 block) {
+    switch (c.passes) {
+        case 1: return launch_one<QA, PK, GS, 1>(a, c, s, grid, block);
+        case 2: return launch_one<QA, PK, GS, 2>(a, c, s, grid, block);
+        case 4: return launch_one<QA, PK, GS, 4>(a, c, s, grid, block);
+        case 8:
+            if constexpr (GS >= 2) return launch_one<QA, PK, GS, 8>(a, c, s, grid, block);
+            break;
+    }
+    return hipErrorInvalidValue;
+}
+
+template <bool QA, bool PK>
+static hipError_t launch_gs(const DecodeArgs &a, const DecodeCfg &c, hipStream_t s, dim3 grid, dim3 block) {
+    switch (c.gs) {
+        case 1: return launch_ps<QA, PK, 1>(a, c, s, grid, block);
+        case 2: return launch_ps<QA, PK, 2>(a, c, s, grid, block);
+        case 4: return launch_ps<QA, PK, 4>(a, c, s, grid, block);
+        case 8: return launch_ps<QA, PK, 8>(a, c, s, grid, block);
+        case 16: return launch_ps<QA, PK, 16>(a, c, s, grid, block);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_decode(const DecodeArgs &a, const DecodeCfg &c, hipStream_t s) {
     const dim3 grid((unsigned)(a.N / 16 / c.wn));
     const dim3 block((unsigned)(64 * c.wn * c.wk));
-    return a.a ? launch_qa<true>(a, c, s, grid, block) : launch_qa<false>(a, c, s, grid, block);
+    if (a.a) return a.packed ? launch_gs<true, true>(a, c, s, grid, block) : launch_gs<true, false>(a, c, s, grid, block);
+    return a.packed ? launch_gs<false, true>(a, c, s, grid, block) : launch_gs<false, false>(a, c, s, grid, block);
 }
 
 }  // namespace r9k

@@ -14,10 +14,10 @@
 //   - per K-group, one e4m3 16x16x128 MFMA per 16x16 output tile gives the
 //     group's exact-product sum P in fp32, which is promoted into the fp32
 //     accumulator as acc += P * as[m,g] * ws[n/128,g];
-//   - ksplit CTAs share an output tile; each writes its fp32 partial, and the
-//     last to arrive (a device-scope counter) sums the partials in ascending
-//     split order, so the result does not depend on arrival order, rounds to
-//     bf16 and resets the counter to zero for the next call.
+//   - ksplit CTAs share an output tile; each writes its fp32 partial to the
+//     workspace and a second kernel sums the partials in ascending split order
+//     (the result does not depend on which CTA finishes first) and rounds to
+//     bf16.
 // MFMA roles: the weight rows are the MFMA's A operand (16 n-rows), the
 // activation rows its B operand (16 m-columns), so a lane's four outputs are
 // four consecutive n of one row m: one 8-byte bf16 store.
@@ -38,7 +38,9 @@ struct SkinnySmem {
     float scales[KC * ROWS];
 };
 
-template <int MT, int KC, bool QA>
+// PK: weights in fragment order (r9k_pack_weight); the same registers come
+// from 1 KiB contiguous runs instead of 16 rows x 64 bytes.
+template <int MT, int KC, bool QA, bool PK>
 __global__ __launch_bounds__(256) void k_gemm_skinny(SkinnyArgs p, int ksplit, int nb) {
     using Smem = SkinnySmem<MT, KC>;
     constexpr int ROWS = Smem::ROWS, PITCH = Smem::PITCH;
@@ -98,9 +100,15 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(SkinnyArgs p, int ksplit, i
         for (int g = 0; g < KC; ++g)
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
-                const uint8_t *src = p.w + (n_wave + 16 * c + l16) * K + (g0 + g) * 128 + 16 * q;
-                wr[g][c][0] = load_nt16(src);
-                wr[g][c][1] = load_nt16(src + 64);
+                if (PK) {
+                    const uint8_t *src = p.w + (((n_wave + 16 * c) / 16) * G + g0 + g) * 2048 + 16 * lane;
+                    wr[g][c][0] = load_nt16(src);
+                    wr[g][c][1] = load_nt16(src + 1024);
+                } else {
+                    const uint8_t *src = p.w + (n_wave + 16 * c + l16) * K + (g0 + g) * 128 + 16 * q;
+                    wr[g][c][0] = load_nt16(src);
+                    wr[g][c][1] = load_nt16(src + 64);
+                }
             }
 
         // ---- A side into LDS: codes [row][batch K range], scales [g][row]
@@ -257,10 +265,14 @@ size_t skinny_partial_bytes(const SkinnyCfg &c, int64_t M, int64_t N) {
 template <int MT, int KC>
 static hipError_t launch_mk(const SkinnyArgs &a, const SkinnyCfg &c, hipStream_t s) {
     dim3 grid((unsigned)((a.N / 128) * c.ksplit), (unsigned)c.mchunks);
-    if (a.a)
-        hipLaunchKernelGGL((k_gemm_skinny<MT, KC, true>), grid, dim3(256), 0, s, a, c.ksplit, c.nb);
+    if (a.a && a.packed)
+        hipLaunchKernelGGL((k_gemm_skinny<MT, KC, true, true>), grid, dim3(256), 0, s, a, c.ksplit, c.nb);
+    else if (a.a)
+        hipLaunchKernelGGL((k_gemm_skinny<MT, KC, true, false>), grid, dim3(256), 0, s, a, c.ksplit, c.nb);
+    else if (a.packed)
+        hipLaunchKernelGGL((k_gemm_skinny<MT, KC, false, true>), grid, dim3(256), 0, s, a, c.ksplit, c.nb);
     else
-        hipLaunchKernelGGL((k_gemm_skinny<MT, KC, false>), grid, dim3(256), 0, s, a, c.ksplit, c.nb);
+        hipLaunchKernelGGL((k_gemm_skinny<MT, KC, false, false>), grid, dim3(256), 0, s, a, c.ksplit, c.nb);
     return hipGetLastError();
 }
 

@@ -121,9 +121,13 @@ __device__ __forceinline__ void wait_vm() {
 }
 }  // namespace
 
-template <class C>
+// PK: the weights are in fragment order (r9k_pack_weight).  The W tile of a
+// stage is then 16 blocks of 2 KiB, [column tile][half][lane][16 bytes], each
+// load instruction one half-block (1 KiB contiguous in memory and in LDS), and
+// a fragment read is 16 bytes at lane * 16 (no swizzle needed).
+template <class C, bool PK>
 __global__ __launch_bounds__(C::THREADS, 1) void k_gemm_tiled(TiledArgs p) {
-    constexpr int WN = C::WN, TN = C::TN, BN = C::BN, BM = C::BM, NW = C::NW;
+    constexpr int WN = C::WN, TN = C::TN, BN = C::BN, BM = C::BM;
     constexpr int WBYTES = C::WBYTES, ABYTES = C::ABYTES, STAGE = C::STAGE, NST = C::NST;
     extern __shared__ __align__(16) uint8_t lds[];
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, q = lane >> 4;
@@ -156,10 +160,16 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_gemm_tiled(TiledArgs p) {
 #pragma unroll
     for (int u = 0; u < C::WLOADS; ++u) {
         const int idx = C::WLOADS * wave + u;
-        const int row = 8 * idx + (lane >> 3);
-        const int chunk = (lane & 7) ^ ((row >> 1) & 7);
-        const int wrow = (n0 + 8 * idx < N) ? row : row - 128;
-        woff[u] = (uint32_t)wrow * (uint32_t)K + 16 * chunk;
+        if (PK) {  // column tile idx / 2, half idx % 2
+            int t = idx >> 1;
+            if (n0 + 16 * t >= N) t -= 8;
+            woff[u] = (uint32_t)t * (uint32_t)(G * 2048) + 1024 * (idx & 1) + 16 * lane;
+        } else {
+            const int row = 8 * idx + (lane >> 3);
+            const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+            const int wrow = (n0 + 8 * idx < N) ? row : row - 128;
+            woff[u] = (uint32_t)wrow * (uint32_t)K + 16 * chunk;
+        }
     }
 #pragma unroll
     for (int u = 0; u < C::ALOADS; ++u) {
@@ -169,7 +179,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_gemm_tiled(TiledArgs p) {
     }
     const uint32_t soff = 4u * (uint32_t)min<int64_t>(m0 + 64 * wm + lane, M - 1);
     const int64_t nb = min<int64_t>((n0 + TN * 16 * wn) / 128, N / 128 - 1);
-    const uint8_t *wbase = p.w + n0 * K;
+    const uint8_t *wbase = PK ? p.w + (n0 / 16) * G * 2048 : p.w + n0 * K;
     const uint8_t *abase = p.aq + m0 * K;
     const float *wsbase = p.ws + nb * G;
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
@@ -177,7 +187,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_gemm_tiled(TiledArgs p) {
         const uint32_t sb = lds0 + st * STAGE + C::WLOADS * wave * 1024;
         const uint32_t sa = lds0 + st * STAGE + WBYTES + C::ALOADS * wave * 1024;
         const uint32_t ss = lds0 + st * STAGE + WBYTES + ABYTES + wave * 512;
-        const uint8_t *wg = wbase + g * 128, *ag = abase + g * 128;
+        const uint8_t *wg = wbase + g * (PK ? 2048 : 128), *ag = abase + g * 128;
 #pragma unroll
         for (int u = 0; u < C::WLOADS; ++u) load_lds16(wg, woff[u], sb + u * 1024);
 #pragma unroll
@@ -189,8 +199,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_gemm_tiled(TiledArgs p) {
     // fragment addresses inside a stage: column tile i of this wave at
     // wfo + 2048 i (and ^ 64), row tile j at afo + 2048 j (rows 16 apart keep
     // their swizzle)
-    const int wfo = swz(TN * 16 * wn + l16, q), afo = WBYTES + swz(64 * wm + l16, q);
-    const int wfo2 = wfo ^ 64, afo2 = afo ^ 64;
+    const int wfo = PK ? TN * wn * 2048 + 16 * lane : swz(TN * 16 * wn + l16, q);
+    const int wfo2 = PK ? wfo + 1024 : wfo ^ 64;
+    const int afo = WBYTES + swz(64 * wm + l16, q), afo2 = afo ^ 64;
 
     v4f acc[TN][4];
 #pragma unroll
@@ -282,7 +293,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_gemm_tiled(TiledArgs p) {
     }
 }
 
-template <class C>
+template <class C, bool PK>
 static hipError_t launch_cfg(const TiledArgs &a, hipStream_t s) {
     // the dynamic LDS limit is a per-device function attribute: set it once per device
     static std::once_flag once[64];
@@ -290,12 +301,12 @@ static hipError_t launch_cfg(const TiledArgs &a, hipStream_t s) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     std::call_once(once[dev], [&] {
-        attr_err[dev] = hipFuncSetAttribute((const void *)k_gemm_tiled<C>,
+        attr_err[dev] = hipFuncSetAttribute((const void *)k_gemm_tiled<C, PK>,
                                             hipFuncAttributeMaxDynamicSharedMemorySize, C::SMEM);
     });
     if (attr_err[dev] != hipSuccess) return attr_err[dev];
     const int64_t nblk = ((a.N + C::BN - 1) / C::BN) * ((a.M + C::BM - 1) / C::BM);
-    hipLaunchKernelGGL(k_gemm_tiled<C>, dim3((unsigned)nblk), dim3(C::THREADS), C::SMEM, s, a);
+    hipLaunchKernelGGL((k_gemm_tiled<C, PK>), dim3((unsigned)nblk), dim3(C::THREADS), C::SMEM, s, a);
     return hipGetLastError();
 }
 
@@ -309,7 +320,8 @@ hipError_t launch_gemm_tiled(const TiledArgs &a, hipStream_t s) {
     }();
     const int64_t ctas_c = ((a.N + CfgC::BN - 1) / CfgC::BN) * ((a.M + CfgC::BM - 1) / CfgC::BM);
     const bool use_c = force ? force == 'c' : ctas_c >= 256;
-    return use_c ? launch_cfg<CfgC>(a, s) : launch_cfg<CfgB>(a, s);
+    if (a.packed) return use_c ? launch_cfg<CfgC, true>(a, s) : launch_cfg<CfgB, true>(a, s);
+    return use_c ? launch_cfg<CfgC, false>(a, s) : launch_cfg<CfgB, false>(a, s);
 }
 
 }  // namespace r9k

@@ -52,6 +52,28 @@ __global__ __launch_bounds__(256) void k_transpose_scales(const float *__restric
     as_t[i] = as[m * G + g];
 }
 
+// One thread per 16-byte chunk of the packed output (consecutive threads write
+// consecutive chunks; the reads gather 16 rows).
+__global__ __launch_bounds__(256) void k_pack_weight(const uint4 *__restrict__ wq, int64_t K, int64_t nchunks,
+                                                     uint4 *__restrict__ wp) {
+    const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (o >= nchunks) return;
+    const int64_t G = K / 128;
+    const int64_t blk = o >> 7;                  // 2 KiB block: (tile, group)
+    const int h = (int)(o >> 6) & 1, l = (int)o & 63;
+    const int64_t t = blk / G, g = blk % G;
+    const int64_t n = t * 16 + (l & 15);
+    const int64_t k = g * 128 + 64 * h + 16 * (l >> 4);
+    wp[o] = wq[(n * K + k) >> 4];
+}
+
+hipError_t launch_pack_weight(const uint8_t *wq, int64_t N, int64_t K, uint8_t *wp, hipStream_t s) {
+    const int64_t nchunks = N * K / 16;
+    hipLaunchKernelGGL(k_pack_weight, dim3((unsigned)((nchunks + 255) / 256)), dim3(256), 0, s, (const uint4 *)wq, K,
+                       nchunks, (uint4 *)wp);
+    return hipGetLastError();
+}
+
 hipError_t launch_transpose_scales(const float *as, int64_t M, int64_t G, float *as_t, hipStream_t s) {
     const int64_t n = M * G;
     hipLaunchKernelGGL(k_transpose_scales, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, as, as_t, M, G);

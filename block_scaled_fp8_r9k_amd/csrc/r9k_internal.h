@@ -13,6 +13,11 @@ namespace r9k {
 hipError_t launch_quant_act(const uint16_t *a, int64_t M, int64_t K, uint8_t *aq, float *as, hipStream_t s,
                             bool scales_transposed = false);
 hipError_t launch_transpose_scales(const float *as, int64_t M, int64_t G, float *as_t, hipStream_t s);
+// W [N][K] row-major -> the fragment-order layout every GEMM engine can read:
+// for 16-row tile t and K-group g, the 2 KiB block at (t * K/128 + g) * 2048
+// holds, at h * 1024 + 16 * l, the 16 bytes that MFMA lane l loads as its h-th
+// chunk: row 16 t + l % 16, bytes 128 g + 64 h + 16 (l / 16) .. +15.
+hipError_t launch_pack_weight(const uint8_t *wq, int64_t N, int64_t K, uint8_t *wp, hipStream_t s);
 hipError_t launch_quant_weight(const uint16_t *w, int64_t N, int64_t K, uint8_t *wq, float *ws, hipStream_t s);
 hipError_t launch_encode_e4m3(const float *x, int64_t n, uint8_t *codes, hipStream_t s);
 
@@ -30,10 +35,11 @@ struct DecodeArgs {
     const uint16_t *a;  // bf16 activations (fused form), or NULL
     const uint8_t *aq;  // pre-quantised codes (split form)
     const float *as;
-    const uint8_t *w;
+    const uint8_t *w;   // weight codes, row-major or fragment-order (packed)
     const float *ws;
     uint16_t *c;
     int64_t M, K, N;
+    bool packed;
 };
 hipError_t launch_gemm_decode(const DecodeArgs &args, const DecodeCfg &cfg, hipStream_t s);
 
@@ -56,11 +62,12 @@ struct SkinnyArgs {
     const uint16_t *a;  // bf16 activations when quantising in the A-load, else NULL
     const uint8_t *aq;  // fp8 activation codes when pre-quantised
     const float *as;    // their scales [M][K/128]
-    const uint8_t *w;
+    const uint8_t *w;   // weight codes, row-major or fragment-order (packed)
     const float *ws;
     uint16_t *c;
     float *part;        // split-K partials [ksplit][M][N]
     int64_t M, K, N;
+    bool packed;
 };
 hipError_t launch_gemm_skinny(const SkinnyArgs &args, const SkinnyCfg &cfg, hipStream_t s);
 
@@ -69,10 +76,11 @@ hipError_t launch_gemm_skinny(const SkinnyArgs &args, const SkinnyCfg &cfg, hipS
 struct TiledArgs {
     const uint8_t *aq;
     const float *as_t;
-    const uint8_t *w;
+    const uint8_t *w;   // weight codes, row-major or fragment-order (packed)
     const float *ws;
     uint16_t *c;
     int64_t M, K, N;
+    bool packed;
 };
 hipError_t launch_gemm_tiled(const TiledArgs &args, hipStream_t s);
 

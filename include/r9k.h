@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define R9K_ABI_VERSION 1
+#define R9K_ABI_VERSION 2
 
 /* Return codes. */
 #define R9K_OK 0
@@ -134,6 +134,31 @@ int r9k_gemm_fp8_block(const uint8_t *aq, const float *as, int64_t M, int64_t K,
  * Errors: as r9k_gemm_fp8_block. */
 int r9k_gemm_fp8_block_qa(const uint16_t *a, int64_t M, int64_t K, const uint8_t *w, const float *ws,
                           int64_t N, uint16_t *c, void *workspace, size_t ws_bytes, void *stream);
+
+/* Fragment-order weights.  The r9700-stack release v0.3.1 notes ("What
+ * changed for someone running it") keep fragment-order copies of the fp8
+ * decode weights; this is that copy for gfx950's 16x16x128 fp8 MFMA.  The
+ * codes and scales are unchanged (same values, same [N/128][K/128] scales);
+ * only the byte order of W differs: for 16-row tile t = n / 16 and K-group
+ * g = k / 128, the 2 KiB block at byte (t * K/128 + g) * 2048 holds, at
+ * h * 1024 + 16 * l (h = 0, 1; l = 0..63), the 16 bytes of row 16 t + l % 16
+ * starting at column 128 g + 64 h + 16 (l / 16).  A 16-row tile's groups are
+ * thus consecutive, and every 16-byte load instruction of the GEMMs reads
+ * 1 KiB of consecutive bytes.  Pack once at load time, after r9k_quant_weight.
+ *   wq [N][K] fp8 row-major -> wp [N*K] fp8 in fragment order (same size).
+ * Errors: NULLPTR; SHAPE if N or K is not a positive multiple of 128; ALIGN;
+ * ARG if wp overlaps wq (no in-place packing); DEVICE; LAUNCH. */
+int r9k_pack_weight(const uint8_t *wq, int64_t N, int64_t K, uint8_t *wp, void *stream);
+
+/* r9k_gemm_fp8_block and r9k_gemm_fp8_block_qa on fragment-order weights wp
+ * (r9k_pack_weight); same arguments otherwise, same workspace query, and the
+ * same result bit for bit as the row-major calls on the unpacked weights.
+ * Errors: as the row-major calls. */
+int r9k_gemm_fp8_block_packed(const uint8_t *aq, const float *as, int64_t M, int64_t K, const uint8_t *wp,
+                              const float *ws, int64_t N, uint16_t *c, void *workspace, size_t ws_bytes,
+                              void *stream);
+int r9k_gemm_fp8_block_qa_packed(const uint16_t *a, int64_t M, int64_t K, const uint8_t *wp, const float *ws,
+                                 int64_t N, uint16_t *c, void *workspace, size_t ws_bytes, void *stream);
 
 /* Dispatch control.  skinny_max_m: the largest M the skinny engine takes
  * (default 255, the pages' boundary; env R9K_FP8_SKINNY_MAXM).  engine:

@@ -126,7 +126,7 @@ def test_gemm_prefill_sampled(r9k, ora):
 
 def test_gemm_reuses_workspace_and_streams(r9k, ora):
     """Two shapes in a row through one explicit workspace, on a side stream:
-    the split-K counters come back to zero after every call."""
+    each call writes what it reads, so reuse gives the same results."""
     import torch
     p1 = Problem(r9k, ora, 8, 4096, 2048, seed=5)
     p2 = Problem(r9k, ora, 3, 1024, 1024, seed=6)
@@ -143,8 +143,6 @@ def test_gemm_reuses_workspace_and_streams(r9k, ora):
     assert_close(ora, host(outs[1]), p2.oracle_full(ora), "stream p2")
     assert_bits_equal(host(outs[0]), host(outs[2]), "p1 twice")
     assert_bits_equal(host(outs[1]), host(outs[3]), "p2 twice")
-    n_cnt = 4 * 16                                                # the counters region is zero again
-    assert int(ws[:n_cnt].sum().item()) == 0
 
 
 def test_gemm_in_hip_graph(r9k, ora):
