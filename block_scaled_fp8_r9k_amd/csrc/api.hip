@@ -7,6 +7,7 @@
 // the pages (R9K_HC_FP8_DECODE_MAXM there, R9K_FP8_SKINNY_MAXM here).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
@@ -90,7 +91,7 @@ GemmWs gemm_ws(int64_t M, int64_t K, int64_t N) {
     GemmWs w;
     const SkinnyCfg c = skinny_config(M, K, N);
     w.part = 0;
-    w.aq = w.part + skinny_partial_bytes(c, M, N);
+    w.aq = w.part + std::max(skinny_partial_bytes(c, M, N), tiled_partial_bytes(tiled_plan(M, K, N), M, N));
     w.as = w.aq + align_up((size_t)(M * K), 256);
     w.total = w.as + align_up((size_t)(M * (K / 128)) * sizeof(float), 256);
     return w;
@@ -107,7 +108,7 @@ int run_gemm(const uint16_t *a, const uint8_t *aq, const float *as, int64_t M, i
     int rc = check_device();
     if (rc) return rc;
     uint8_t *base = (uint8_t *)workspace;
-    const int engine = engine_for(M);
+    int engine = engine_for(M);
     if (engine == R9K_ENGINE_SKINNY) {
         // decode widths: the dedicated weight-streaming kernel when the shape
         // fits it, with the activation quant in its A-load
@@ -116,6 +117,10 @@ int run_gemm(const uint16_t *a, const uint8_t *aq, const float *as, int64_t M, i
             DecodeArgs d{a, aq, as, w, ws, c, M, K, N, packed};
             return launch_result(launch_gemm_decode(d, dc, s));
         }
+        // wider skinny shapes under automatic dispatch: the tiled engine with
+        // its K split is faster from 64 rows on, and at any width for long K
+        // (measured on the MI355X at N = 4096, K = 4096 and 14336)
+        if (g_engine.load() == R9K_ENGINE_AUTO && (M >= 64 || K >= 8192)) engine = R9K_ENGINE_TILED;
     }
     if (engine == R9K_ENGINE_TILED) {
         // the tiled engine reads codes and transposed scales [K/128][M] from
@@ -129,8 +134,8 @@ int run_gemm(const uint16_t *a, const uint8_t *aq, const float *as, int64_t M, i
             rc = launch_result(launch_transpose_scales(as, M, K / 128, as_t, s));
         }
         if (rc) return rc;
-        TiledArgs t{aq, as_t, w, ws, c, M, K, N, packed};
-        return launch_result(launch_gemm_tiled(t, s));
+        TiledArgs t{aq, as_t, w, ws, c, M, K, N, packed, (float *)(base + L.part), 1};
+        return launch_result(launch_gemm_tiled(t, tiled_plan(M, K, N), s));
     }
     if (a && M > g_qa_inload_max_m.load()) {
         // quantise A once per call into the workspace, then run on codes

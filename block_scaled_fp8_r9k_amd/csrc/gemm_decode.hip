@@ -17,8 +17,8 @@
 //   - per K-group one e4m3 16x16x128 MFMA, promoted as acc += P * as * ws;
 //   - the wk K-slices of a tile are summed through LDS in ascending slice order
 //     by the slice-0 wave, rounded to bf16 and stored.
-// Rows M..15 of the MFMA's 16 are never stored, so their LDS contents are left
-// as they are.  MFMA roles: weight rows are the A operand (16 n), activation
+// LDS holds the M activation rows only; the MFMA's rows M..15 read row M - 1
+// again and their outputs are never stored.  MFMA roles: weight rows are the A operand (16 n), activation
 // rows the B operand (16 m); a lane's four outputs are four consecutive n of
 // row l % 16.  K order inside a group: lane quarter q feeds bytes [16q, +16)
 // and [64+16q, +16) for both operands.
@@ -63,8 +63,8 @@ __global__ __launch_bounds__(512) void k_gemm_decode(DecodeArgs p, int wn, int w
     extern __shared__ __align__(16) uint8_t lds[];
     const int64_t K = p.K, N = p.N, G = K / 128;
     const int M = (int)p.M;
-    const int pitch = (int)K + 16;                    // codes [16][K + 16]
-    float *scales = (float *)(lds + 16 * pitch);       // [G][16]
+    const int pitch = (int)K + 16;                    // codes [M][K + 16]
+    float *scales = (float *)(lds + M * pitch);        // [G][16]
     const int tid = threadIdx.x, nthreads = blockDim.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l16 = lane & 15, q = lane >> 4;
@@ -163,7 +163,8 @@ __global__ __launch_bounds__(512) void k_gemm_decode(DecodeArgs p, int wn, int w
 #pragma unroll
     for (int g = 0; g < GS; ++g) {
         const int gg = (int)gbeg + g;
-        const uint8_t *ap = lds + l16 * pitch + gg * 128 + 16 * q;
+        // the MFMA's rows M..15 read row M - 1 again; their outputs are never stored
+        const uint8_t *ap = lds + min(l16, M - 1) * pitch + gg * 128 + 16 * q;
         const v8i af = make_frag(*(const uint4 *)ap, *(const uint4 *)(ap + 64));
         const float sc = scales[gg * 16 + l16] * wsrow[g];
         const v4f pr = mfma_e4m3_16x16x128(make_frag(wr[g][0], wr[g][1]), af, zero);
@@ -186,15 +187,16 @@ __global__ __launch_bounds__(512) void k_gemm_decode(DecodeArgs p, int wn, int w
 // (wn, wk, passes) for a shape.  Measured on the MI355X: weight streaming is
 // fastest with CTAs of 2 column tiles x 2 K slices (1-2 CTAs per compute
 // unit), so wn = 2 when that still leaves at least 256 CTAs (else 1), then the
-// smallest K split (K-groups per wave a power of two, at most 16) that gives at
-// least 4 waves per compute unit, at most 8 per CTA.  The activation side needs
+// smallest K split (K-groups per wave a power of two, at most 16; the split
+// itself any count up to 8, e.g. 7 for K = 14336) that gives at least 4 waves
+// per compute unit, at most 8 per CTA.  The activation side needs
 // PASSES = M * (K/128) / (16 * waves) register passes, at most 8 (two batches
 // of 4).  R9K_DECODE_WN / R9K_DECODE_WK override (tuning).
 DecodeCfg decode_config(int64_t M, int64_t K, int64_t N) {
     DecodeCfg c{0, 0, 0, 0, 0};
     const int64_t G = K / 128, tiles = N / 16;
     if (M < 1 || M > 16) return c;
-    const size_t lds = (size_t)16 * (K + 16) + (size_t)G * 16 * 4;
+    const size_t lds = (size_t)M * (K + 16) + (size_t)G * 16 * 4;
     if (lds > 150 * 1024) return c;
     int wn = (tiles % 2 == 0 && tiles / 2 >= 256) ? 2 : 1;
     if (const char *e = getenv("R9K_DECODE_WN")) {
@@ -204,7 +206,7 @@ DecodeCfg decode_config(int64_t M, int64_t K, int64_t N) {
     int force_wk = 0;
     if (const char *e = getenv("R9K_DECODE_WK")) force_wk = atoi(e);
     int wk = 0;
-    for (int cand : {1, 2, 4, 8}) {
+    for (int cand = 1; cand <= 8; ++cand) {  // any split whose share is a power of two (K = 14336: 7 x 16)
         if (force_wk && cand != force_wk) continue;
         if (G % cand || wn * cand > 8) continue;
         const int64_t gs = G / cand;

@@ -297,9 +297,12 @@ hipError_t launch_gemm_skinny(const SkinnyArgs &a, const SkinnyCfg &c, hipStream
         case 16: e = launch_m<16>(a, c, s); break;
     }
     if (e != hipSuccess || c.ksplit == 1) return e;
-    const int64_t MN = a.M * a.N;
-    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((MN / 4 + 255) / 256)), dim3(256), 0, s, a.part, a.c, MN,
-                       c.ksplit);
+    return launch_splitk_reduce(a.part, a.c, a.M, a.N, c.ksplit, s);
+}
+
+hipError_t launch_splitk_reduce(const float *part, uint16_t *c, int64_t M, int64_t N, int ksplit, hipStream_t s) {
+    const int64_t MN = M * N;
+    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((MN / 4 + 255) / 256)), dim3(256), 0, s, part, c, MN, ksplit);
     return hipGetLastError();
 }
 

@@ -29,6 +29,8 @@
 // and fetches the logical chunk that belongs there: chunk c of row r lives at
 // chunk c ^ ((r >> 1) & 7), so the 16 rows a fragment read touches in one LDS
 // cycle fall on distinct banks.
+#include <algorithm>
+#include <cstdlib>
 #include <mutex>
 
 #include "r9k_device.h"
@@ -135,6 +137,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_gemm_tiled(TiledArgs p) {
     const int wn = wave % WN, wm = wave / WN;
     const int64_t K = p.K, N = p.N, M = p.M, G = K / 128;
     const int64_t ntn = (N + BN - 1) / BN, ntm = (M + BM - 1) / BM;
+    // this CTA's K range: groups gb .. gb + GL - 1 of split blockIdx.y
+    const int ks = blockIdx.y;
+    const int64_t gb = (int64_t)ks * G / p.ksplit, GL = (int64_t)(ks + 1) * G / p.ksplit - gb;
 
     // block -> tile.  Blocks are dealt round-robin to the 8 XCDs; each XCD
     // takes a contiguous range of tiles, walked in groups of GM row tiles, so
@@ -220,17 +225,17 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_gemm_tiled(TiledArgs p) {
 
 #pragma unroll
     for (int k = 0; k < NST - 1; ++k)
-        if (k < G) issue(k, k);
-    for (int64_t g = 0; g < G; ++g) {
-        const int st = (int)(g % NST);
-        // group g's stage has landed: this wave's loads issued after it are
-        // those of groups g + 1 .. g + NST - 2 (three stages: g + 1, if any);
-        // then every wave's, and every wave is done with the stage that
-        // group g + NST - 1 will overwrite
-        if (NST == 3 && g + 1 < G) wait_vm<C::LOADS_PER_STAGE>();
+        if (k < GL) issue(gb + k, k);
+    for (int64_t gl = 0; gl < GL; ++gl) {
+        const int st = (int)(gl % NST);
+        // local group gl's stage has landed: this wave's loads issued after it
+        // are those of groups gl + 1 .. gl + NST - 2 (three stages: gl + 1, if
+        // any); then every wave's, and every wave is done with the stage that
+        // group gl + NST - 1 will overwrite
+        if (NST == 3 && gl + 1 < GL) wait_vm<C::LOADS_PER_STAGE>();
         else wait_vm<0>();
         __syncthreads();
-        if (g + NST - 1 < G) issue(g + NST - 1, (int)((g + NST - 1) % NST));
+        if (gl + NST - 1 < GL) issue(gb + gl + NST - 1, (int)((gl + NST - 1) % NST));
 
         const uint8_t *wt = lds + st * STAGE;
         const uint8_t *at = wt + WBYTES;
@@ -286,10 +291,16 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_gemm_tiled(TiledArgs p) {
     for (int j = 0; j < 4; ++j) {
         const int64_t m = m0 + 64 * wm + 16 * j + l16;
         if (m >= M) continue;
-        uint16_t *crow = p.c + m * N + nbase + 4 * q;
+        if (p.ksplit > 1) {
+            float *prow = p.part + ((int64_t)ks * M + m) * N + nbase + 4 * q;
 #pragma unroll
-        for (int i = 0; i < TN; ++i)
-            *(uint2 *)(crow + 16 * i) = bf16x4_rne(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+            for (int i = 0; i < TN; ++i) *(v4f *)(prow + 16 * i) = acc[i][j];
+        } else {
+            uint16_t *crow = p.c + m * N + nbase + 4 * q;
+#pragma unroll
+            for (int i = 0; i < TN; ++i)
+                *(uint2 *)(crow + 16 * i) = bf16x4_rne(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+        }
     }
 }
 
@@ -306,22 +317,47 @@ static hipError_t launch_cfg(const TiledArgs &a, hipStream_t s) {
     });
     if (attr_err[dev] != hipSuccess) return attr_err[dev];
     const int64_t nblk = ((a.N + C::BN - 1) / C::BN) * ((a.M + C::BM - 1) / C::BM);
-    hipLaunchKernelGGL((k_gemm_tiled<C, PK>), dim3((unsigned)nblk), dim3(C::THREADS), C::SMEM, s, a);
+    hipLaunchKernelGGL((k_gemm_tiled<C, PK>), dim3((unsigned)nblk, (unsigned)a.ksplit), dim3(C::THREADS), C::SMEM, s,
+                       a);
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_tiled(const TiledArgs &a, hipStream_t s) {
-    // the 256 x 256 tile moves a third less data per flop and reads less LDS
-    // per MFMA; below one CTA per compute unit the 256 x 128 tile keeps more
-    // of the chip busy.  R9K_TILED_CFG=b|c forces one (tuning).
-    static const int force = [] {
-        const char *e = getenv("R9K_TILED_CFG");
-        return e ? (int)e[0] : 0;
-    }();
-    const int64_t ctas_c = ((a.N + CfgC::BN - 1) / CfgC::BN) * ((a.M + CfgC::BM - 1) / CfgC::BM);
-    const bool use_c = force ? force == 'c' : ctas_c >= 256;
-    if (a.packed) return use_c ? launch_cfg<CfgC, true>(a, s) : launch_cfg<CfgB, true>(a, s);
-    return use_c ? launch_cfg<CfgC, false>(a, s) : launch_cfg<CfgB, false>(a, s);
+TiledPlan tiled_plan(int64_t M, int64_t K, int64_t N) {
+    TiledPlan t{false, 1};
+    const int64_t G = K / 128;
+    const int64_t ctas_c = ((N + CfgC::BN - 1) / CfgC::BN) * ((M + CfgC::BM - 1) / CfgC::BM);
+    const int64_t ctas_b = ((N + CfgB::BN - 1) / CfgB::BN) * ((M + CfgB::BM - 1) / CfgB::BM);
+    t.big = ctas_c >= 256;
+    if (!t.big && ctas_b < 256) {
+        // split K so that about 256 CTAs run, each with at least two groups
+        int64_t ks = 256 / ctas_b;
+        ks = std::min<int64_t>(ks, G / 2);
+        t.ksplit = (int)std::max<int64_t>(ks, 1);
+    }
+    if (const char *e = getenv("R9K_TILED_CFG")) {  // b|c forces the tile shape (tuning)
+        if (e[0] == 'b') t.big = false;
+        if (e[0] == 'c') t.big = true;
+    }
+    if (t.big) t.ksplit = 1;
+    if (const char *e = getenv("R9K_TILED_KSPLIT")) {  // tuning
+        const int v = atoi(e);
+        if (v >= 1 && v <= G && !t.big) t.ksplit = v;
+    }
+    return t;
+}
+
+size_t tiled_partial_bytes(const TiledPlan &t, int64_t M, int64_t N) {
+    return t.ksplit > 1 ? align_up(sizeof(float) * (size_t)t.ksplit * M * N, 256) : 0;
+}
+
+hipError_t launch_gemm_tiled(const TiledArgs &a, const TiledPlan &plan, hipStream_t s) {
+    TiledArgs b = a;
+    b.ksplit = plan.ksplit;
+    hipError_t e;
+    if (plan.big) e = a.packed ? launch_cfg<CfgC, true>(b, s) : launch_cfg<CfgC, false>(b, s);
+    else e = a.packed ? launch_cfg<CfgB, true>(b, s) : launch_cfg<CfgB, false>(b, s);
+    if (e != hipSuccess || plan.ksplit == 1) return e;
+    return launch_splitk_reduce(b.part, b.c, b.M, b.N, plan.ksplit, s);
 }
 
 }  // namespace r9k

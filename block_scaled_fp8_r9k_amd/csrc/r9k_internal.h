@@ -81,8 +81,20 @@ struct TiledArgs {
     uint16_t *c;
     int64_t M, K, N;
     bool packed;
+    float *part;        // ksplit > 1: fp32 partial sums [ksplit][M][N], summed by a second kernel
+    int ksplit;
 };
-hipError_t launch_gemm_tiled(const TiledArgs &args, hipStream_t s);
+// The tile shape and K split for a shape: CTAs of 256 x 256 when there are
+// enough of them, else 256 columns x 128 rows with the K range split so that
+// about one CTA per compute unit runs (fp32 partials in the workspace).
+struct TiledPlan {
+    bool big;    // 256 x 256 tiles
+    int ksplit;
+};
+TiledPlan tiled_plan(int64_t M, int64_t K, int64_t N);
+size_t tiled_partial_bytes(const TiledPlan &t, int64_t M, int64_t N);
+hipError_t launch_gemm_tiled(const TiledArgs &args, const TiledPlan &plan, hipStream_t s);
+hipError_t launch_splitk_reduce(const float *part, uint16_t *c, int64_t M, int64_t N, int ksplit, hipStream_t s);
 
 // ---- MoE decode (moe.hip) ----
 struct MoeArgs {
