@@ -211,10 +211,11 @@ def bench_prefill(torch, r9k, inputs, dev, reps):
     M, K, N = 4096, 4096, 12288
     a = dev(inputs.activations(1, M, K, outliers=True))
     copies = weight_copies(torch, r9k, dev, inputs.weights(1, N, K), min_bytes=256 << 20, cap=6)
+    copies = [(r9k.pack_weight(wq), ws) for wq, ws in copies]  # fragment order, packed at load
     C = len(copies)
     wsp = torch.zeros(r9k.gemm_fp8_block_workspace(M, K, N), dtype=torch.uint8, device="cuda")
     c_out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    calls = [lambda c=c: r9k.gemm_fp8_block_qa(a, copies[c][0], copies[c][1], c=c_out, workspace=wsp)
+    calls = [lambda c=c: r9k.gemm_fp8_block_qa_packed(a, copies[c][0], copies[c][1], c=c_out, workspace=wsp)
              for c in range(C)]
     for f in calls:
         f()
@@ -224,8 +225,8 @@ def bench_prefill(torch, r9k, inputs, dev, reps):
     ms = tm.run(lambda i: g.replay(), reps) / C
     tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
     log(f"prefill {M}x{K}x{N}: {ms * 1e3:.1f} us, {tflops:.0f} TFLOP/s")
-    return dict(workload=f"M={M}, K={K}, N={N}, fused act quant", us=ms * 1e3, value=tflops, unit="TFLOP/s",
-                peak=FP8_PEAK_TFLOPS, frac=tflops / FP8_PEAK_TFLOPS)
+    return dict(workload=f"M={M}, K={K}, N={N}, fused act quant, fragment-order weights", us=ms * 1e3,
+                value=tflops, unit="TFLOP/s", peak=FP8_PEAK_TFLOPS, frac=tflops / FP8_PEAK_TFLOPS)
 
 
 def bench_mid(torch, r9k, inputs, dev, reps):
@@ -233,12 +234,14 @@ def bench_mid(torch, r9k, inputs, dev, reps):
     for K, N in ((4096, 4096), (14336, 4096)):
         a = dev(inputs.activations(2, 255, K, outliers=True))
         copies = weight_copies(torch, r9k, dev, inputs.weights(2, N, K))
+        copies = [(r9k.pack_weight(wq), ws) for wq, ws in copies]  # fragment order, packed at load
         C = len(copies)
         for M in (32, 64, 128, 255):
             wsp = torch.zeros(r9k.gemm_fp8_block_workspace(M, K, N), dtype=torch.uint8, device="cuda")
             am = a[:M].contiguous()
             c_out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-            calls = [lambda c=c: r9k.gemm_fp8_block_qa(am, copies[c][0], copies[c][1], c=c_out, workspace=wsp)
+            calls = [lambda c=c: r9k.gemm_fp8_block_qa_packed(am, copies[c][0], copies[c][1], c=c_out,
+                                                              workspace=wsp)
                      for c in range(C)]
             for f in calls:
                 f()
@@ -261,6 +264,9 @@ def bench_moe(torch, r9k, inputs, dev, reps):
     q13, s13 = r9k.quant_weight(dev(w13.reshape(E * 2 * I, H)))
     q2, s2 = r9k.quant_weight(dev(w2.reshape(E * H, I)))
     del w13, w2
+    # fragment-order expert weights (packed once at load, not timed)
+    q13 = r9k.pack_weight(q13)
+    q2 = r9k.pack_weight(q2)
     sets = [(q13, s13, q2, s2), (q13.clone(), s13.clone(), q2.clone(), s2.clone())]
     x_d, ids_d, tw_d = dev(x), torch.from_numpy(ids).cuda(), torch.from_numpy(tw).cuda()
     wsp = torch.zeros(r9k.moe_fp8_decode_workspace(T, H, E, I, k), dtype=torch.uint8, device="cuda")
@@ -273,7 +279,7 @@ def bench_moe(torch, r9k, inputs, dev, reps):
         calls = [lambda s=s: r9k.moe_fp8_decode(x_d, ids_d, tw_d, s[0].view(E, 2 * I, H),
                                                 s[1].view(E, 2 * I // 128, H // 128), s[2].view(E, H, I),
                                                 s[3].view(E, H // 128, I // 128), out=out, workspace=wsp,
-                                                fused=fused) for s in sets]
+                                                fused=fused, packed=True) for s in sets]
         for f in calls:
             f()
         g = capture(torch, calls)

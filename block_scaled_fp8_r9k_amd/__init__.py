@@ -63,6 +63,7 @@ def lib() -> ctypes.CDLL:
         L.r9k_moe_fp8_decode.argtypes = [c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_int64, c_void_p,
                                          c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_void_p,
                                          c_size_t, c_int, c_void_p]
+        L.r9k_moe_fp8_decode_packed.argtypes = L.r9k_moe_fp8_decode.argtypes
         v = L.r9k_abi_version()
         if v != ABI_VERSION:
             raise ImportError(f"libr9k.so has ABI version {v}, this binding needs {ABI_VERSION}")
@@ -274,9 +275,9 @@ def moe_ws_offset(T: int, H: int, E: int, I: int, topk: int, which: str) -> int:
 
 
 def moe_fp8_decode(x, topk_ids, topk_w, w13, w13_s, w2, w2_s, out=None, workspace=None, fused: bool = True,
-                   stream=None) -> torch.Tensor:
+                   stream=None, packed: bool = False) -> torch.Tensor:
     """Routed MoE decode: x [T,H] bf16, ids/weights [T,topk], experts w13 [E,2I,H], w2 [E,H,I] (fp8 +
-    block scales) -> out [T,H] bf16."""
+    block scales) -> out [T,H] bf16.  packed: w13 and w2 are pack_weight copies (same shapes)."""
     T, H = x.shape
     topk = topk_ids.shape[1]
     E, twoI, _ = w13.shape
@@ -285,9 +286,9 @@ def moe_fp8_decode(x, topk_ids, topk_w, w13, w13_s, w2, w2_s, out=None, workspac
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     nbytes = moe_fp8_decode_workspace(T, H, E, I, topk)
     wsb = _workspace(workspace, nbytes)
-    _check(lib().r9k_moe_fp8_decode(_ptr(x, BF16, "x"), T, H, _ptr(topk_ids, I32, "topk_ids"),
-                                    _ptr(topk_w, F32, "topk_w"), topk, _ptr(w13, FP8, "w13"),
-                                    _ptr(w13_s, F32, "w13_s"), _ptr(w2, FP8, "w2"), _ptr(w2_s, F32, "w2_s"), E, I,
-                                    _ptr(out, BF16, "out"), _ptr(wsb, FP8, "workspace"), wsb.numel(),
-                                    1 if fused else 0, _stream(stream)), "r9k_moe_fp8_decode")
+    fn = lib().r9k_moe_fp8_decode_packed if packed else lib().r9k_moe_fp8_decode
+    _check(fn(_ptr(x, BF16, "x"), T, H, _ptr(topk_ids, I32, "topk_ids"), _ptr(topk_w, F32, "topk_w"), topk,
+              _ptr(w13, FP8, "w13"), _ptr(w13_s, F32, "w13_s"), _ptr(w2, FP8, "w2"), _ptr(w2_s, F32, "w2_s"), E, I,
+              _ptr(out, BF16, "out"), _ptr(wsb, FP8, "workspace"), wsb.numel(), 1 if fused else 0, _stream(stream)),
+           "r9k_moe_fp8_decode_packed" if packed else "r9k_moe_fp8_decode")
     return out

@@ -298,10 +298,10 @@ int r9k_moe_ws_offset(int64_t T, int64_t H, int64_t E, int64_t I, int64_t topk, 
     return R9K_ERR_ARG;
 }
 
-int r9k_moe_fp8_decode(const uint16_t *x, int64_t T, int64_t H, const int32_t *topk_ids, const float *topk_w,
-                       int64_t topk, const uint8_t *w13, const float *w13_s, const uint8_t *w2, const float *w2_s,
-                       int64_t E, int64_t I, uint16_t *out, void *workspace, size_t ws_bytes, int fused,
-                       void *stream) {
+static int run_moe(const uint16_t *x, int64_t T, int64_t H, const int32_t *topk_ids, const float *topk_w,
+                   int64_t topk, const uint8_t *w13, const float *w13_s, const uint8_t *w2, const float *w2_s,
+                   int64_t E, int64_t I, uint16_t *out, void *workspace, size_t ws_bytes, int fused, void *stream,
+                   bool packed) {
     if (!x || !topk_ids || !topk_w || !w13 || !w13_s || !w2 || !w2_s || !out || !workspace) return R9K_ERR_NULLPTR;
     if (int rc = check_moe_shape(T, H, E, I, topk)) return rc;
     if (fused != 0 && fused != 1) return R9K_ERR_ARG;
@@ -314,8 +314,24 @@ int r9k_moe_fp8_decode(const uint16_t *x, int64_t T, int64_t H, const int32_t *t
     if (int rc = check_device()) return rc;
     uint8_t *b = (uint8_t *)workspace;
     MoeArgs a{x, topk_ids, topk_w, w13, w13_s, w2, w2_s, out, (uint16_t *)(b + L.gu), (uint16_t *)(b + L.h),
-              b + L.hq, (float *)(b + L.hs), (float *)(b + L.y), T, H, E, I, topk};
+              b + L.hq, (float *)(b + L.hs), (float *)(b + L.y), T, H, E, I, topk, packed};
     return launch_result(launch_moe_decode(a, fused == 1, (hipStream_t)stream));
+}
+
+int r9k_moe_fp8_decode(const uint16_t *x, int64_t T, int64_t H, const int32_t *topk_ids, const float *topk_w,
+                       int64_t topk, const uint8_t *w13, const float *w13_s, const uint8_t *w2, const float *w2_s,
+                       int64_t E, int64_t I, uint16_t *out, void *workspace, size_t ws_bytes, int fused,
+                       void *stream) {
+    return run_moe(x, T, H, topk_ids, topk_w, topk, w13, w13_s, w2, w2_s, E, I, out, workspace, ws_bytes, fused,
+                   stream, false);
+}
+
+int r9k_moe_fp8_decode_packed(const uint16_t *x, int64_t T, int64_t H, const int32_t *topk_ids,
+                              const float *topk_w, int64_t topk, const uint8_t *w13p, const float *w13_s,
+                              const uint8_t *w2p, const float *w2_s, int64_t E, int64_t I, uint16_t *out,
+                              void *workspace, size_t ws_bytes, int fused, void *stream) {
+    return run_moe(x, T, H, topk_ids, topk_w, topk, w13p, w13_s, w2p, w2_s, E, I, out, workspace, ws_bytes, fused,
+                   stream, true);
 }
 
 }  // extern "C"

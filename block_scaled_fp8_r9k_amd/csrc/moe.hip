@@ -71,7 +71,9 @@ struct MoeSmem {
 
 // One expert GEMM pass.  NCT = column tiles of 16 per wave (4 for gate_up:
 // 2 gate + 2 up, 2 for down).  Rows are the expert's pairs in tiles of 16.
-template <int MODE, int KC>
+// PK: expert weights in fragment order (r9k_pack_weight of [E * 2I][H] and
+// [E * H][I]; 16-row tiles never straddle two experts), read in 1 KiB runs.
+template <int MODE, int KC, bool PK>
 __global__ __launch_bounds__(256) void k_moe_gemm(MoeArgs p) {
     constexpr bool GATEUP = MODE == GATEUP_STORE || MODE == GATEUP_SILU;
     constexpr int NCT = GATEUP ? 4 : 2;
@@ -145,9 +147,15 @@ __global__ __launch_bounds__(256) void k_moe_gemm(MoeArgs p) {
             for (int g = 0; g < KC; ++g)
 #pragma unroll
                 for (int c = 0; c < NCT; ++c) {
-                    const uint8_t *src = wbase + wrow[c] * K + (g0 + g) * 128 + 16 * q;
-                    wr[g][c][0] = load_nt16(src);
-                    wr[g][c][1] = load_nt16(src + 64);
+                    if (PK) {
+                        const uint8_t *src = wbase + ((wrow[c] - l16) / 16 * G + g0 + g) * 2048 + 16 * lane;
+                        wr[g][c][0] = load_nt16(src);
+                        wr[g][c][1] = load_nt16(src + 1024);
+                    } else {
+                        const uint8_t *src = wbase + wrow[c] * K + (g0 + g) * 128 + 16 * q;
+                        wr[g][c][0] = load_nt16(src);
+                        wr[g][c][1] = load_nt16(src + 64);
+                    }
                 }
 
             // zero rows past the pair count, then fill the valid rows
@@ -289,6 +297,22 @@ MoeLayout moe_layout(int64_t T, int64_t H, int64_t E, int64_t I, int64_t topk) {
     return L;
 }
 
+template <int MODE, bool PK>
+static hipError_t launch_kc(const MoeArgs &a, int kc, dim3 grid, hipStream_t s) {
+    constexpr bool GATEUP = MODE == GATEUP_STORE || MODE == GATEUP_SILU;
+    switch (kc) {
+        case 8: if constexpr (!GATEUP) { hipLaunchKernelGGL((k_moe_gemm<MODE, 8, PK>), grid, dim3(256), 0, s, a); break; }
+                return hipErrorInvalidValue;
+        case 6: if constexpr (!GATEUP) { hipLaunchKernelGGL((k_moe_gemm<MODE, 6, PK>), grid, dim3(256), 0, s, a); break; }
+                return hipErrorInvalidValue;
+        case 4: hipLaunchKernelGGL((k_moe_gemm<MODE, 4, PK>), grid, dim3(256), 0, s, a); break;
+        case 3: hipLaunchKernelGGL((k_moe_gemm<MODE, 3, PK>), grid, dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((k_moe_gemm<MODE, 2, PK>), grid, dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL((k_moe_gemm<MODE, 1, PK>), grid, dim3(256), 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
 template <int MODE>
 static hipError_t launch_gemm_mode(const MoeArgs &a, hipStream_t s) {
     constexpr bool GATEUP = MODE == GATEUP_STORE || MODE == GATEUP_SILU;
@@ -300,17 +324,8 @@ static hipError_t launch_gemm_mode(const MoeArgs &a, hipStream_t s) {
     int kc = 1;
     for (int cand : {8, 6, 4, 3, 2, 1})
         if (cand <= kcmax && G % cand == 0) { kc = cand; break; }
-    switch (kc) {
-        case 8: if constexpr (!GATEUP) { hipLaunchKernelGGL((k_moe_gemm<MODE, 8>), grid, dim3(256), 0, s, a); break; }
-                return hipErrorInvalidValue;
-        case 6: if constexpr (!GATEUP) { hipLaunchKernelGGL((k_moe_gemm<MODE, 6>), grid, dim3(256), 0, s, a); break; }
-                return hipErrorInvalidValue;
-        case 4: hipLaunchKernelGGL((k_moe_gemm<MODE, 4>), grid, dim3(256), 0, s, a); break;
-        case 3: hipLaunchKernelGGL((k_moe_gemm<MODE, 3>), grid, dim3(256), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((k_moe_gemm<MODE, 2>), grid, dim3(256), 0, s, a); break;
-        default: hipLaunchKernelGGL((k_moe_gemm<MODE, 1>), grid, dim3(256), 0, s, a); break;
-    }
-    return hipGetLastError();
+    if (a.packed) return launch_kc<MODE, true>(a, kc, grid, s);
+    return launch_kc<MODE, false>(a, kc, grid, s);
 }
 
 hipError_t launch_moe_decode(const MoeArgs &a, bool fused, hipStream_t s) {

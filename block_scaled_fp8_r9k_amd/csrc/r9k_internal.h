@@ -112,6 +112,7 @@ struct MoeArgs {
     float *hs;      // [P][I/128] (three-launch path)
     float *y;       // [P][H] fp32
     int64_t T, H, E, I, topk;
+    bool packed;    // w13 and w2 in fragment order
 };
 struct MoeLayout {
     size_t gu, h, hq, hs, y, total;

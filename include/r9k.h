@@ -206,6 +206,16 @@ int r9k_moe_fp8_decode(const uint16_t *x, int64_t T, int64_t H, const int32_t *t
                        const float *w2_s, int64_t E, int64_t I, uint16_t *out, void *workspace,
                        size_t ws_bytes, int fused, void *stream);
 
+/* r9k_moe_fp8_decode on fragment-order expert weights: w13p = r9k_pack_weight
+ * of w13 viewed as [E * 2I][H], w2p = r9k_pack_weight of w2 viewed as
+ * [E * H][I] (2I and H are multiples of 128, so no 16-row tile straddles two
+ * experts).  Same arguments, workspace and result bits as the row-major call.
+ * Errors: as r9k_moe_fp8_decode. */
+int r9k_moe_fp8_decode_packed(const uint16_t *x, int64_t T, int64_t H, const int32_t *topk_ids,
+                              const float *topk_w, int64_t topk, const uint8_t *w13p, const float *w13_s,
+                              const uint8_t *w2p, const float *w2_s, int64_t E, int64_t I, uint16_t *out,
+                              void *workspace, size_t ws_bytes, int fused, void *stream);
+
 /* Byte offset inside the MoE workspace of an intermediate (for tests):
  * which = 0 gu [P][2I] bf16, 1 h [P][I] bf16, 2 y [P][H] fp32, 3 hq [P][I] fp8,
  * 4 hs [P][I/128] fp32 (P = T*topk; gu, hq and hs are written by the

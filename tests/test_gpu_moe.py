@@ -50,9 +50,14 @@ class MoeProblem:
         nbytes = r9k.moe_fp8_decode_workspace(T, H, E, I, topk)
         self.ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
 
-    def run(self, r9k, fused, ids_d=None):
-        out = r9k.moe_fp8_decode(self.x_d, self.ids_d if ids_d is None else ids_d, self.w_d, self.w13q,
-                                 self.w13s, self.w2q, self.w2s, workspace=self.ws, fused=fused)
+    def run(self, r9k, fused, ids_d=None, packed=False):
+        w13, w2 = self.w13q, self.w2q
+        if packed:
+            E, twoI, H = w13.shape
+            w13 = r9k.pack_weight(w13.reshape(E * twoI, H)).view(E, twoI, H)
+            w2 = r9k.pack_weight(w2.reshape(E * H, twoI // 2)).view(E, H, twoI // 2)
+        out = r9k.moe_fp8_decode(self.x_d, self.ids_d if ids_d is None else ids_d, self.w_d, w13,
+                                 self.w13s, w2, self.w2s, workspace=self.ws, fused=fused, packed=packed)
         return host(out)
 
     def ws_view(self, r9k, which, dtype, shape):
@@ -131,6 +136,9 @@ def test_moe_decode(r9k, ora, shape):
     assert_bits_equal(p.ws_view(r9k, "h", torch.bfloat16, (P, I)), h, "h fused vs three-launch")
     assert_bits_equal(p.ws_view(r9k, "y", torch.float32, (P, H)), y, "y fused vs three-launch")
     assert_bits_equal(p.run(r9k, True), fused, "moe repeat")
+    # 7. fragment-order expert weights give the same bits, both paths
+    assert_bits_equal(p.run(r9k, True, packed=True), fused, "moe fused, packed weights")
+    assert_bits_equal(p.run(r9k, False, packed=True), unfused, "moe three-launch, packed weights")
 
 
 def test_moe_out_of_range_id_contributes_nothing(r9k, ora):
