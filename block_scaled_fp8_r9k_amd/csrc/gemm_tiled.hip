@@ -43,7 +43,8 @@ namespace {
 // columns, 64 rows), two waves per SIMD so that one wave's LDS and barrier
 // waits hide behind the other's MFMAs.  Two shapes are built:
 //   C: 2 x 4 waves of 8 x 4 tiles, a 256 x 256 CTA tile, two LDS stages;
-//   B: 4 x 2 waves of 4 x 4 tiles, a 256 x 128 CTA tile, three LDS stages.
+//   B: 4 x 2 waves of 4 x 4 tiles, a 256 x 128 CTA tile, three LDS stages;
+//   M1, M2: 64 columns x 128 / 256 rows, for skinny widths with a K split.
 // C reads 0.75 KiB of LDS per MFMA instead of 1 KiB and moves a third less
 // from L2 per flop; B makes twice as many CTAs for shapes too small for C.
 template <int WN_, int WM_, int TN_, int NST_>
@@ -67,6 +68,11 @@ struct Cfg {
 };
 using CfgB = Cfg<4, 2, 4, 3>;
 using CfgC = Cfg<2, 4, 8, 2>;
+// narrow tiles for skinny widths (64 columns; all of M up to 128 or 256 rows),
+// where the K split, not the tile, gives the CTAs: fewer fp32 partials per
+// output than wide tiles split further
+using CfgM1 = Cfg<4, 2, 1, 3>;
+using CfgM2 = Cfg<2, 4, 2, 3>;
 
 // Global -> LDS loads (lane l's bytes land at LDS address `l_addr` + size * l,
 // the address taken from M0).  Issued from inline asm so that the compiler
@@ -322,26 +328,35 @@ static hipError_t launch_cfg(const TiledArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <class C>
+static int64_t ctas_of(int64_t M, int64_t N) {
+    return ((N + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM);
+}
+
 TiledPlan tiled_plan(int64_t M, int64_t K, int64_t N) {
-    TiledPlan t{false, 1};
+    TiledPlan t{TILE_B, 1};
     const int64_t G = K / 128;
-    const int64_t ctas_c = ((N + CfgC::BN - 1) / CfgC::BN) * ((M + CfgC::BM - 1) / CfgC::BM);
-    const int64_t ctas_b = ((N + CfgB::BN - 1) / CfgB::BN) * ((M + CfgB::BM - 1) / CfgB::BM);
-    t.big = ctas_c >= 256;
-    if (!t.big && ctas_b < 256) {
-        // split K so that about 256 CTAs run, each with at least two groups
-        int64_t ks = 256 / ctas_b;
-        ks = std::min<int64_t>(ks, G / 2);
-        t.ksplit = (int)std::max<int64_t>(ks, 1);
+    if (ctas_of<CfgC>(M, N) >= 256) t.shape = TILE_C;
+    else if (ctas_of<CfgB>(M, N) >= 256) t.shape = TILE_B;
+    else if (M <= 256) t.shape = M <= 128 ? TILE_M1 : TILE_M2;
+    if (const char *e = getenv("R9K_TILED_CFG")) {  // b|c|1|2 forces the tile shape (tuning)
+        if (e[0] == 'b') t.shape = TILE_B;
+        if (e[0] == 'c') t.shape = TILE_C;
+        if (e[0] == '1') t.shape = TILE_M1;
+        if (e[0] == '2') t.shape = TILE_M2;
     }
-    if (const char *e = getenv("R9K_TILED_CFG")) {  // b|c forces the tile shape (tuning)
-        if (e[0] == 'b') t.big = false;
-        if (e[0] == 'c') t.big = true;
+    int64_t ctas = 0;
+    switch (t.shape) {
+        case TILE_C: ctas = ctas_of<CfgC>(M, N); break;
+        case TILE_B: ctas = ctas_of<CfgB>(M, N); break;
+        case TILE_M1: ctas = ctas_of<CfgM1>(M, N); break;
+        case TILE_M2: ctas = ctas_of<CfgM2>(M, N); break;
     }
-    if (t.big) t.ksplit = 1;
+    // split K so that about 256 CTAs run, each with at least two groups
+    if (t.shape != TILE_C && ctas < 256) t.ksplit = (int)std::max<int64_t>(std::min<int64_t>(256 / ctas, G / 2), 1);
     if (const char *e = getenv("R9K_TILED_KSPLIT")) {  // tuning
         const int v = atoi(e);
-        if (v >= 1 && v <= G && !t.big) t.ksplit = v;
+        if (v >= 1 && v <= G && t.shape != TILE_C) t.ksplit = v;
     }
     return t;
 }
@@ -353,9 +368,13 @@ size_t tiled_partial_bytes(const TiledPlan &t, int64_t M, int64_t N) {
 hipError_t launch_gemm_tiled(const TiledArgs &a, const TiledPlan &plan, hipStream_t s) {
     TiledArgs b = a;
     b.ksplit = plan.ksplit;
-    hipError_t e;
-    if (plan.big) e = a.packed ? launch_cfg<CfgC, true>(b, s) : launch_cfg<CfgC, false>(b, s);
-    else e = a.packed ? launch_cfg<CfgB, true>(b, s) : launch_cfg<CfgB, false>(b, s);
+    hipError_t e = hipErrorInvalidValue;
+    switch (plan.shape) {
+        case TILE_C: e = a.packed ? launch_cfg<CfgC, true>(b, s) : launch_cfg<CfgC, false>(b, s); break;
+        case TILE_B: e = a.packed ? launch_cfg<CfgB, true>(b, s) : launch_cfg<CfgB, false>(b, s); break;
+        case TILE_M1: e = a.packed ? launch_cfg<CfgM1, true>(b, s) : launch_cfg<CfgM1, false>(b, s); break;
+        case TILE_M2: e = a.packed ? launch_cfg<CfgM2, true>(b, s) : launch_cfg<CfgM2, false>(b, s); break;
+    }
     if (e != hipSuccess || plan.ksplit == 1) return e;
     return launch_splitk_reduce(b.part, b.c, b.M, b.N, plan.ksplit, s);
 }

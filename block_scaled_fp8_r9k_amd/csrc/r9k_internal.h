@@ -85,10 +85,12 @@ struct TiledArgs {
     int ksplit;
 };
 // The tile shape and K split for a shape: CTAs of 256 x 256 when there are
-// enough of them, else 256 columns x 128 rows with the K range split so that
-// about one CTA per compute unit runs (fp32 partials in the workspace).
+// enough of them, else 256 columns x 128 rows, else (skinny widths) 64
+// columns x all rows, with the K range split so that about one CTA per
+// compute unit runs (fp32 partials in the workspace).
+enum TileShape { TILE_C, TILE_B, TILE_M1, TILE_M2 };
 struct TiledPlan {
-    bool big;    // 256 x 256 tiles
+    TileShape shape;
     int ksplit;
 };
 TiledPlan tiled_plan(int64_t M, int64_t K, int64_t N);
