@@ -112,7 +112,7 @@ int run_gemm(const uint16_t *a, const uint8_t *aq, const float *as, int64_t M, i
     if (engine == R9K_ENGINE_SKINNY) {
         // decode widths: the dedicated weight-streaming kernel when the shape
         // fits it, with the activation quant in its A-load
-        const DecodeCfg dc = decode_config(M, K, N);
+        const DecodeCfg dc = decode_config(M, K, N, packed);
         if (dc.wn) {
             DecodeArgs d{a, aq, as, w, ws, c, M, K, N, packed};
             return launch_result(launch_gemm_decode(d, dc, s));

@@ -184,21 +184,25 @@ __global__ __launch_bounds__(512) void k_gemm_decode(DecodeArgs p, int wn, int w
     }
 }
 
-// (wn, wk, passes) for a shape.  Measured on the MI355X: weight streaming is
-// fastest with CTAs of 2 column tiles x 2 K slices (1-2 CTAs per compute
-// unit), so wn = 2 when that still leaves at least 256 CTAs (else 1), then the
-// smallest K split (K-groups per wave a power of two, at most 16; the split
-// itself any count up to 8, e.g. 7 for K = 14336) that gives at least 4 waves
-// per compute unit, at most 8 per CTA.  The activation side needs
-// PASSES = M * (K/128) / (16 * waves) register passes, at most 8 (two batches
-// of 4).  R9K_DECODE_WN / R9K_DECODE_WK override (tuning).
-DecodeCfg decode_config(int64_t M, int64_t K, int64_t N) {
+// (wn, wk, passes) for a shape.  Measured on the MI355X (K = 4096,
+// N = 14336): eight-wave CTAs stream fastest; the activation quant, which
+// every CTA repeats, favours fewer and wider CTAs once M is large.  So
+// wn = 4 from 12 rows on when that leaves at least 192 CTAs, else wn = 2 when
+// that leaves at least 256 CTAs, else 1; then the smallest K split (K-groups
+// per wave a power of two, at most 16; the split itself any count up to 8,
+// e.g. 7 for K = 14336) that gives at least 8 waves per compute unit (4 on
+// row-major weights, whose 16-row load pattern does better with fewer), at
+// most 8 waves per CTA.  The activation side needs PASSES = M * (K/128) /
+// (16 * waves) register passes, at most 8 (two batches of 4).
+// R9K_DECODE_WN / R9K_DECODE_WK override (tuning).
+DecodeCfg decode_config(int64_t M, int64_t K, int64_t N, bool packed) {
     DecodeCfg c{0, 0, 0, 0, 0};
     const int64_t G = K / 128, tiles = N / 16;
     if (M < 1 || M > 16) return c;
     const size_t lds = (size_t)M * (K + 16) + (size_t)G * 16 * 4;
     if (lds > 150 * 1024) return c;
     int wn = (tiles % 2 == 0 && tiles / 2 >= 256) ? 2 : 1;
+    if (M >= 12 && tiles % 4 == 0 && tiles / 4 >= 192) wn = 4;
     if (const char *e = getenv("R9K_DECODE_WN")) {
         const int v = atoi(e);
         if (v >= 1 && v <= 4 && tiles % v == 0) wn = v;
@@ -212,7 +216,7 @@ DecodeCfg decode_config(int64_t M, int64_t K, int64_t N) {
         const int64_t gs = G / cand;
         if (gs > MAX_GS || (gs & (gs - 1))) continue;
         wk = cand;
-        if ((tiles / wn) * wn * cand >= 4 * 256) break;
+        if ((tiles / wn) * wn * cand >= (packed ? 8 : 4) * 256) break;
     }
     if (!wk) return c;
     const int64_t quads = 16 * wn * wk;

@@ -30,7 +30,7 @@ struct DecodeCfg {
     size_t lds;  // dynamic LDS bytes
 };
 // fused: the kernel quantises the activations itself; otherwise it reads codes.
-DecodeCfg decode_config(int64_t M, int64_t K, int64_t N);
+DecodeCfg decode_config(int64_t M, int64_t K, int64_t N, bool packed);
 struct DecodeArgs {
     const uint16_t *a;  // bf16 activations (fused form), or NULL
     const uint8_t *aq;  // pre-quantised codes (split form)
