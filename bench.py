@@ -97,7 +97,7 @@ def weight_copies(torch, r9k, dev, w_bits, min_bytes=ROTATE_BYTES, cap=16):
     return copies
 
 
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_gemm_decode_sweep_k4096_n14336_traffic.md")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_gemm_decode_packed_sweep_k4096_n14336_traffic.md")
 
 
 def kernel_source_hash():
@@ -348,8 +348,8 @@ def main():
         line["hbm_frac"] = line["value"] / HBM_PEAK_GBS
         line["roofline"] = dict(bound="hbm", achieved=d["achieved"], peak=HBM_PEAK_GBS, unit="GB/s",
                                 frac=d["achieved"] / HBM_PEAK_GBS, traffic=traffic_from_profiles(),
-                                kernel="k_gemm_decode (activation quant in the A-load), average over the "
-                                       "sweep's five launches",
+                                kernel="k_gemm_decode (activation quant in the A-load, fragment-order "
+                                       "weights), average over the sweep's five launches",
                                 bytes_per_launch=d["bytes_avg"], us_per_launch=d["us_avg"])
         line["per_m"] = {str(M): v for M, v in d["per_m"].items()}
         if not args.no_cpu_baseline:
