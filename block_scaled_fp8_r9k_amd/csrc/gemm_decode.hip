@@ -1,4 +1,4 @@
-// Engine (a), decode widths (1 <= M <= 16): the weight-streaming skinny GEMM.
+// Engine (a), decode widths (1 <= M <= 32): the weight-streaming skinny GEMM.
 //
 // The r9700-stack release v0.3.1 notes ("What changed for someone running
 // it") describe the decode GEMMs as the step's largest weight stream and move
@@ -53,8 +53,11 @@ constexpr int MAX_GS = 16;  // K-groups per wave: 32 x 16-byte loads per lane
 // is one contiguous run and every 16-byte load instruction reads 1 KiB of
 // consecutive bytes; the registers receive exactly what the row-major loads
 // would give them.
-template <bool QA, bool PK, int GS, int PASSES>
+//
+// MT: row tiles of 16 (M <= 16 * MT); each weight fragment feeds MT MFMAs.
+template <bool QA, bool PK, int GS, int PASSES, int MT>
 __global__ __launch_bounds__(512) void k_gemm_decode(DecodeArgs p, int wn, int wk) {
+    constexpr int SR = 16 * MT;                      // scale row stride
     constexpr int PB = PASSES < 4 ? PASSES : 4;      // passes per activation batch
     constexpr int NB = PASSES / PB;                  // activation batches (1 or 2)
     constexpr int NCH = GS < 4 ? GS : 4;             // weight chunks
@@ -64,7 +67,7 @@ __global__ __launch_bounds__(512) void k_gemm_decode(DecodeArgs p, int wn, int w
     const int64_t K = p.K, N = p.N, G = K / 128;
     const int M = (int)p.M;
     const int pitch = (int)K + 16;                    // codes [M][K + 16]
-    float *scales = (float *)(lds + M * pitch);        // [G][16]
+    float *scales = (float *)(lds + M * pitch);        // [G][16 MT]
     const int tid = threadIdx.x, nthreads = blockDim.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l16 = lane & 15, q = lane >> 4;
@@ -115,7 +118,7 @@ __global__ __launch_bounds__(512) void k_gemm_decode(DecodeArgs p, int wn, int w
                 uint4 *dst = (uint4 *)(lds + r * pitch + g * 128 + sub * 32);
                 dst[0] = codes[0];
                 dst[1] = codes[1];
-                if (sub == 0) scales[g * 16 + r] = sc;
+                if (sub == 0) scales[g * SR + r] = sc;
             }
         }
     };
@@ -155,32 +158,52 @@ __global__ __launch_bounds__(512) void k_gemm_decode(DecodeArgs p, int wn, int w
     }
     __syncthreads();
 
-    // ---- MFMA per group and promotion; the block scales are uniform per wave
-    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    // ---- MFMA per group and row tile, and promotion; the weight block scale is
+    // uniform per wave
+    v4f acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
     const int64_t nb = __builtin_amdgcn_readfirstlane((int)(n0 / 128));
     const float *wsrow = p.ws + nb * G + gbeg;
 #pragma unroll
     for (int g = 0; g < GS; ++g) {
         const int gg = (int)gbeg + g;
-        // the MFMA's rows M..15 read row M - 1 again; their outputs are never stored
-        const uint8_t *ap = lds + min(l16, M - 1) * pitch + gg * 128 + 16 * q;
-        const v8i af = make_frag(*(const uint4 *)ap, *(const uint4 *)(ap + 64));
-        const float sc = scales[gg * 16 + l16] * wsrow[g];
-        const v4f pr = mfma_e4m3_16x16x128(make_frag(wr[g][0], wr[g][1]), af, zero);
+        const v8i wf = make_frag(wr[g][0], wr[g][1]);
+        const float wsg = wsrow[g];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(pr[i], sc, acc[i]);
+        for (int mt = 0; mt < MT; ++mt) {
+            // the MFMA's rows past M read row M - 1 again; their outputs are never stored
+            const int row = min(16 * mt + l16, M - 1);
+            const uint8_t *ap = lds + row * pitch + gg * 128 + 16 * q;
+            const v8i af = make_frag(*(const uint4 *)ap, *(const uint4 *)(ap + 64));
+            const float sc = scales[gg * SR + row] * wsg;
+            const v4f pr = mfma_e4m3_16x16x128(wf, af, zero);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[mt][i] = __builtin_fmaf(pr[i], sc, acc[mt][i]);
+        }
     }
 
     // ---- sum the K slices in ascending order, round, store
     __syncthreads();                                   // every wave is done reading the codes
-    v4f *red = (v4f *)lds;                             // [wave][64 lanes]
-    if (slice > 0) red[wave * 64 + lane] = acc;
+    v4f *red = (v4f *)lds;                             // [wave][MT][64 lanes]
+    if (slice > 0) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) red[(wave * MT + mt) * 64 + lane] = acc[mt];
+    }
     __syncthreads();
     if (slice == 0) {
-        for (int s = 1; s < wk; ++s) acc += red[(s * wn + ct) * 64 + lane];
-        if (l16 < M)
-            *(uint2 *)(p.c + (int64_t)l16 * N + n0 + 4 * q) = bf16x4_rne(acc[0], acc[1], acc[2], acc[3]);
+        for (int s = 1; s < wk; ++s) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt] += red[((s * wn + ct) * MT + mt) * 64 + lane];
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int row = 16 * mt + l16;
+            if (row < M)
+                *(uint2 *)(p.c + (int64_t)row * N + n0 + 4 * q) =
+                    bf16x4_rne(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
+        }
     }
 }
 
@@ -196,10 +219,11 @@ __global__ __launch_bounds__(512) void k_gemm_decode(DecodeArgs p, int wn, int w
 // (16 * waves) register passes, at most 8 (two batches of 4).
 // R9K_DECODE_WN / R9K_DECODE_WK override (tuning).
 DecodeCfg decode_config(int64_t M, int64_t K, int64_t N, bool packed) {
-    DecodeCfg c{0, 0, 0, 0, 0};
+    DecodeCfg c{0, 0, 0, 0, 0, 0};
     const int64_t G = K / 128, tiles = N / 16;
-    if (M < 1 || M > 16) return c;
-    const size_t lds = (size_t)M * (K + 16) + (size_t)G * 16 * 4;
+    if (M < 1 || M > 32) return c;
+    const int mt = M > 16 ? 2 : 1;
+    const size_t lds = (size_t)M * (K + 16) + (size_t)G * 16 * mt * 4;
     if (lds > 150 * 1024) return c;
     int wn = (tiles % 2 == 0 && tiles / 2 >= 256) ? 2 : 1;
     if (M >= 12 && tiles % 4 == 0 && tiles / 4 >= 192) wn = 4;
@@ -229,48 +253,54 @@ DecodeCfg decode_config(int64_t M, int64_t K, int64_t N, bool packed) {
     c.wk = wk;
     c.gs = (int)(G / wk);
     c.passes = passes;
-    // the slice reduction reuses the codes region: one 1 KiB row of v4f per wave
-    c.lds = std::max(lds, (size_t)wn * wk * 64 * 16);
+    // the slice reduction reuses the codes region: MT 1 KiB rows of v4f per wave
+    c.lds = std::max(lds, (size_t)wn * wk * mt * 64 * 16);
+    c.mt = mt;
     return c;
 }
 
 // one instantiation: its 160 KiB dynamic-LDS limit is set once per device
-template <bool QA, bool PK, int GS, int PS>
+template <bool QA, bool PK, int GS, int PS, int MT>
 static hipError_t launch_one(const DecodeArgs &a, const DecodeCfg &c, hipStream_t s, dim3 grid, dim3 block) {
     static std::once_flag once[64];
     static hipError_t attr_err[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     std::call_once(once[dev], [&] {
-        attr_err[dev] = hipFuncSetAttribute((const void *)k_gemm_decode<QA, PK, GS, PS>,
+        attr_err[dev] = hipFuncSetAttribute((const void *)k_gemm_decode<QA, PK, GS, PS, MT>,
                                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     });
     if (attr_err[dev] != hipSuccess) return attr_err[dev];
-    hipLaunchKernelGGL((k_gemm_decode<QA, PK, GS, PS>), grid, block, c.lds, s, a, c.wn, c.wk);
+    hipLaunchKernelGGL((k_gemm_decode<QA, PK, GS, PS, MT>), grid, block, c.lds, s, a, c.wn, c.wk);
     return hipGetLastError();
 }
 
-template <bool QA, bool PK, int GS>
+template <bool QA, bool PK, int GS, int MT>
 static hipError_t launch_ps(const DecodeArgs &a, const DecodeCfg &c, hipStream_t s, dim3 grid, dim3 block) {
     switch (c.passes) {
-        case 1: return launch_one<QA, PK, GS, 1>(a, c, s, grid, block);
-        case 2: return launch_one<QA, PK, GS, 2>(a, c, s, grid, block);
-        case 4: return launch_one<QA, PK, GS, 4>(a, c, s, grid, block);
+        case 1: return launch_one<QA, PK, GS, 1, MT>(a, c, s, grid, block);
+        case 2: return launch_one<QA, PK, GS, 2, MT>(a, c, s, grid, block);
+        case 4: return launch_one<QA, PK, GS, 4, MT>(a, c, s, grid, block);
         case 8:
-            if constexpr (GS >= 2) return launch_one<QA, PK, GS, 8>(a, c, s, grid, block);
+            if constexpr (GS >= 2) return launch_one<QA, PK, GS, 8, MT>(a, c, s, grid, block);
             break;
     }
     return hipErrorInvalidValue;
 }
 
+template <bool QA, bool PK, int GS>
+static hipError_t launch_mt(const DecodeArgs &a, const DecodeCfg &c, hipStream_t s, dim3 grid, dim3 block) {
+    return c.mt == 2 ? launch_ps<QA, PK, GS, 2>(a, c, s, grid, block) : launch_ps<QA, PK, GS, 1>(a, c, s, grid, block);
+}
+
 template <bool QA, bool PK>
 static hipError_t launch_gs(const DecodeArgs &a, const DecodeCfg &c, hipStream_t s, dim3 grid, dim3 block) {
     switch (c.gs) {
-        case 1: return launch_ps<QA, PK, 1>(a, c, s, grid, block);
-        case 2: return launch_ps<QA, PK, 2>(a, c, s, grid, block);
-        case 4: return launch_ps<QA, PK, 4>(a, c, s, grid, block);
-        case 8: return launch_ps<QA, PK, 8>(a, c, s, grid, block);
-        case 16: return launch_ps<QA, PK, 16>(a, c, s, grid, block);
+        case 1: return launch_mt<QA, PK, 1>(a, c, s, grid, block);
+        case 2: return launch_mt<QA, PK, 2>(a, c, s, grid, block);
+        case 4: return launch_mt<QA, PK, 4>(a, c, s, grid, block);
+        case 8: return launch_mt<QA, PK, 8>(a, c, s, grid, block);
+        case 16: return launch_mt<QA, PK, 16>(a, c, s, grid, block);
     }
     return hipErrorInvalidValue;
 }

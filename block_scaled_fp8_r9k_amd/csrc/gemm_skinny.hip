@@ -194,14 +194,37 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(SkinnyArgs p, int ksplit, i
     }
 }
 
-// C[m][n] = bf16(sum over splits, ascending, of part[ks][m][n]); 4 columns a thread.
+// C[m][n] = bf16(sum over splits, ascending, of part[ks][m][n]); 8 columns a
+// thread.  The partials of up to four splits are loaded before they are added,
+// so that each thread keeps several loads in flight; the additions still go in
+// ascending split order.
 __global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__ part, uint16_t *__restrict__ c,
                                                        int64_t MN, int ksplit) {
-    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
     if (i >= MN) return;
-    v4f sum = *(const v4f *)(part + i);
-    for (int k = 1; k < ksplit; ++k) sum += *(const v4f *)(part + (int64_t)k * MN + i);
-    *(uint2 *)(c + i) = bf16x4_rne(sum[0], sum[1], sum[2], sum[3]);
+    v4f s0 = *(const v4f *)(part + i), s1 = *(const v4f *)(part + i + 4);
+    int k = 1;
+    for (; k + 4 <= ksplit; k += 4) {
+        v4f x[4][2];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float *pk = part + (int64_t)(k + u) * MN + i;
+            x[u][0] = *(const v4f *)pk;
+            x[u][1] = *(const v4f *)(pk + 4);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            s0 += x[u][0];
+            s1 += x[u][1];
+        }
+    }
+    for (; k < ksplit; ++k) {
+        const float *pk = part + (int64_t)k * MN + i;
+        s0 += *(const v4f *)pk;
+        s1 += *(const v4f *)(pk + 4);
+    }
+    uint2 lo = bf16x4_rne(s0[0], s0[1], s0[2], s0[3]), hi = bf16x4_rne(s1[0], s1[1], s1[2], s1[3]);
+    *(uint4 *)(c + i) = make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
 // ---- configuration ----------------------------------------------------------
@@ -302,7 +325,7 @@ hipError_t launch_gemm_skinny(const SkinnyArgs &a, const SkinnyCfg &c, hipStream
 
 hipError_t launch_splitk_reduce(const float *part, uint16_t *c, int64_t M, int64_t N, int ksplit, hipStream_t s) {
     const int64_t MN = M * N;
-    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((MN / 4 + 255) / 256)), dim3(256), 0, s, part, c, MN, ksplit);
+    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((MN / 8 + 255) / 256)), dim3(256), 0, s, part, c, MN, ksplit);
     return hipGetLastError();
 }
 

@@ -21,13 +21,14 @@ hipError_t launch_pack_weight(const uint8_t *wq, int64_t N, int64_t K, uint8_t *
 hipError_t launch_quant_weight(const uint16_t *w, int64_t N, int64_t K, uint8_t *wq, float *ws, hipStream_t s);
 hipError_t launch_encode_e4m3(const float *x, int64_t n, uint8_t *codes, hipStream_t s);
 
-// ---- decode engine, 1 <= M <= 16 (gemm_decode.hip) ----
+// ---- decode engine, 1 <= M <= 32 (gemm_decode.hip) ----
 struct DecodeCfg {
     int wn;      // 16-column tiles per CTA (0: the shape does not fit this engine)
     int wk;      // K slices per column tile (waves per CTA = wn * wk)
     int gs;      // K-groups per wave: (K / 128) / wk
     int passes;  // activation groups per lane quad
     size_t lds;  // dynamic LDS bytes
+    int mt;      // row tiles of 16 (1 or 2)
 };
 // fused: the kernel quantises the activations itself; otherwise it reads codes.
 DecodeCfg decode_config(int64_t M, int64_t K, int64_t N, bool packed);

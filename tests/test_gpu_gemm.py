@@ -175,3 +175,18 @@ def test_gemm_in_hip_graph(r9k, ora):
         assert_bits_equal(host(cd), eager_d, f"graph decode replay {rep}")
         assert_bits_equal(host(cp), eager_p, f"graph prefill replay {rep}")
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("M,K,N", [(17, 4096, 2048), (24, 4096, 1024), (32, 4096, 2048), (32, 2048, 14336),
+                                   (8, 14336, 1024)])
+def test_gemm_decode_two_row_tiles(r9k, ora, M, K, N):
+    """The decode kernel's widths past 16 rows (two row tiles) and K=14336 at 8 rows, full output,
+    both weight layouts."""
+    say("decode widths", M, K, N)
+    p = Problem(r9k, ora, M, K, N, seed=M + 3)
+    c64 = p.oracle_full(ora)
+    got = p.run(r9k, 0, fused=True)
+    assert_close(ora, got, c64, f"decode {M}x{K}x{N}")
+    wp = r9k.pack_weight(p.wq_d)
+    assert_bits_equal(host(r9k.gemm_fp8_block_qa_packed(p.a_d, wp, p.ws_d)), got, "packed == row-major")
+    assert_bits_equal(p.run(r9k, 0, fused=False), got, "split == fused")
