@@ -20,7 +20,7 @@ from ctypes import POINTER, c_char_p, c_int, c_int64, c_size_t, c_void_p
 
 import torch
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 ENGINE_AUTO, ENGINE_SKINNY, ENGINE_TILED = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -58,6 +58,7 @@ def lib() -> ctypes.CDLL:
         L.r9k_pack_weight.argtypes = [c_void_p, c_int64, c_int64, c_void_p, c_void_p]
         L.r9k_set_dispatch.argtypes = [c_int, c_int]
         L.r9k_get_dispatch.argtypes = [POINTER(c_int), POINTER(c_int)]
+        L.r9k_gemm_fp8_block_plan.argtypes = [c_int64, c_int64, c_int64, c_int, POINTER(c_int), POINTER(c_int)]
         L.r9k_moe_fp8_decode_workspace.argtypes = [c_int64] * 5 + [POINTER(c_size_t)]
         L.r9k_moe_ws_offset.argtypes = [c_int64] * 5 + [c_int, POINTER(c_size_t)]
         L.r9k_moe_fp8_decode.argtypes = [c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_int64, c_void_p,
@@ -257,6 +258,17 @@ def get_dispatch() -> tuple[int, int]:
     m, e = c_int(0), c_int(0)
     _check(lib().r9k_get_dispatch(ctypes.byref(m), ctypes.byref(e)), "r9k_get_dispatch")
     return m.value, e.value
+
+
+KERNEL_NONE, KERNEL_DECODE, KERNEL_SKINNY, KERNEL_TILED = 0, 1, 2, 3
+
+
+def gemm_fp8_block_plan(M: int, K: int, N: int, packed: bool = False) -> tuple[int, int]:
+    """(kernel, ksplit) that a GEMM call of this shape runs (host only)."""
+    k, s = c_int(0), c_int(0)
+    _check(lib().r9k_gemm_fp8_block_plan(M, K, N, int(bool(packed)), ctypes.byref(k), ctypes.byref(s)),
+           "r9k_gemm_fp8_block_plan")
+    return k.value, s.value
 
 
 # -------------------------------------------------------------------- moe ----

@@ -91,13 +91,44 @@ GemmWs gemm_ws(int64_t M, int64_t K, int64_t N) {
     GemmWs w;
     const SkinnyCfg c = skinny_config(M, K, N);
     w.part = 0;
-    w.aq = w.part + std::max(skinny_partial_bytes(c, M, N), tiled_partial_bytes(tiled_plan(M, K, N), M, N));
+    w.aq = w.part + std::max({skinny_partial_bytes(c, M, N), tiled_partial_bytes(tiled_plan(M, K, N), M, N),
+                              decode_partial_bytes(M, K, N)});
     w.as = w.aq + align_up((size_t)(M * K), 256);
     w.total = w.as + align_up((size_t)(M * (K / 128)) * sizeof(float), 256);
     return w;
 }
 
 int launch_result(hipError_t e) { return e == hipSuccess ? R9K_OK : R9K_ERR_LAUNCH; }
+
+// Which kernel a GEMM call runs, with its configuration: the dispatcher's
+// whole decision, shared by the launch path and r9k_gemm_fp8_block_plan.
+struct GemmRoute {
+    int kernel;  // R9K_KERNEL_*
+    DecodeCfg dc;
+    TiledPlan tp;
+};
+GemmRoute route_gemm(int64_t M, int64_t K, int64_t N, bool packed) {
+    GemmRoute r{R9K_KERNEL_SKINNY, DecodeCfg{0, 0, 0, 0, 0, 0, 0}, TiledPlan{TILE_C, 1}};
+    int engine = engine_for(M);
+    if (engine == R9K_ENGINE_SKINNY) {
+        // decode widths: the dedicated weight-streaming kernel when the shape
+        // fits it, with the activation quant in its A-load
+        r.dc = decode_config(M, K, N, packed);
+        if (r.dc.wn) {
+            r.kernel = R9K_KERNEL_DECODE;
+            return r;
+        }
+        // wider skinny shapes under automatic dispatch: the tiled engine with
+        // its K split is faster from 64 rows on, and at any width for long K
+        // (measured on the MI355X at N = 4096, K = 4096 and 14336)
+        if (g_engine.load() == R9K_ENGINE_AUTO && (M >= 64 || K >= 8192)) engine = R9K_ENGINE_TILED;
+    }
+    if (engine == R9K_ENGINE_TILED) {
+        r.kernel = R9K_KERNEL_TILED;
+        r.tp = tiled_plan(M, K, N);
+    }
+    return r;
+}
 
 int run_gemm(const uint16_t *a, const uint8_t *aq, const float *as, int64_t M, int64_t K, const uint8_t *w,
              const float *ws, int64_t N, uint16_t *c, void *workspace, size_t ws_bytes, hipStream_t s,
@@ -108,21 +139,12 @@ int run_gemm(const uint16_t *a, const uint8_t *aq, const float *as, int64_t M, i
     int rc = check_device();
     if (rc) return rc;
     uint8_t *base = (uint8_t *)workspace;
-    int engine = engine_for(M);
-    if (engine == R9K_ENGINE_SKINNY) {
-        // decode widths: the dedicated weight-streaming kernel when the shape
-        // fits it, with the activation quant in its A-load
-        const DecodeCfg dc = decode_config(M, K, N, packed);
-        if (dc.wn) {
-            DecodeArgs d{a, aq, as, w, ws, c, M, K, N, packed};
-            return launch_result(launch_gemm_decode(d, dc, s));
-        }
-        // wider skinny shapes under automatic dispatch: the tiled engine with
-        // its K split is faster from 64 rows on, and at any width for long K
-        // (measured on the MI355X at N = 4096, K = 4096 and 14336)
-        if (g_engine.load() == R9K_ENGINE_AUTO && (M >= 64 || K >= 8192)) engine = R9K_ENGINE_TILED;
+    const GemmRoute route = route_gemm(M, K, N, packed);
+    if (route.kernel == R9K_KERNEL_DECODE) {
+        DecodeArgs d{a, aq, as, w, ws, c, M, K, N, packed, (float *)(base + L.part)};
+        return launch_result(launch_gemm_decode(d, route.dc, s));
     }
-    if (engine == R9K_ENGINE_TILED) {
+    if (route.kernel == R9K_KERNEL_TILED) {
         // the tiled engine reads codes and transposed scales [K/128][M] from
         // the workspace: quantise A once per call, or transpose the caller's scales
         float *as_t = (float *)(base + L.as);
@@ -135,7 +157,7 @@ int run_gemm(const uint16_t *a, const uint8_t *aq, const float *as, int64_t M, i
         }
         if (rc) return rc;
         TiledArgs t{aq, as_t, w, ws, c, M, K, N, packed, (float *)(base + L.part), 1};
-        return launch_result(launch_gemm_tiled(t, tiled_plan(M, K, N), s));
+        return launch_result(launch_gemm_tiled(t, route.tp, s));
     }
     if (a && M > g_qa_inload_max_m.load()) {
         // quantise A once per call into the workspace, then run on codes
@@ -251,6 +273,23 @@ int r9k_pack_weight(const uint8_t *wq, int64_t N, int64_t K, uint8_t *wp, void *
     if (plo < hi && lo < plo + (uintptr_t)(N * K)) return R9K_ERR_ARG;  // in place is not supported
     if (int rc = check_device()) return rc;
     return launch_result(launch_pack_weight(wq, N, K, wp, (hipStream_t)stream));
+}
+
+int r9k_gemm_fp8_block_plan(int64_t M, int64_t K, int64_t N, int packed, int *kernel, int *ksplit) {
+    if (!kernel || !ksplit) return R9K_ERR_NULLPTR;
+    if (int rc = check_gemm_shape(M, K, N)) return rc;
+    if (packed != 0 && packed != 1) return R9K_ERR_ARG;
+    if (M == 0) {
+        *kernel = R9K_KERNEL_NONE;
+        *ksplit = 0;
+        return R9K_OK;
+    }
+    const GemmRoute r = route_gemm(M, K, N, packed != 0);
+    *kernel = r.kernel;
+    *ksplit = r.kernel == R9K_KERNEL_DECODE ? r.dc.ksplit
+              : r.kernel == R9K_KERNEL_TILED ? r.tp.ksplit
+                                              : skinny_config(M, K, N).ksplit;
+    return R9K_OK;
 }
 
 int r9k_set_dispatch(int skinny_max_m, int engine) {

@@ -1,4 +1,4 @@
-// Engine (a), decode widths (1 <= M <= 32): the weight-streaming skinny GEMM.
+// Engine (a), decode widths (1 <= M <= 64): the weight-streaming skinny GEMM.
 //
 // The r9700-stack release v0.3.1 notes ("What changed for someone running
 // it") describe the decode GEMMs as the step's largest weight stream and move
@@ -55,6 +55,12 @@ constexpr int MAX_GS = 16;  // K-groups per wave: 32 x 16-byte loads per lane
 // would give them.
 //
 // MT: row tiles of 16 (M <= 16 * MT); each weight fragment feeds MT MFMAs.
+//
+// K split (gridDim.y = ksplit > 1): CTA (x, ks) covers K-groups
+// [ks * wk * GS, (ks + 1) * wk * GS) only, quantises just those groups of
+// the activations into LDS, and writes fp32 partial sums part[ks][m][n] that a
+// second kernel adds in ascending ks.  Used where all of K does not fit in LDS
+// or where every CTA quantising all of K would cost more than the stream.
 template <bool QA, bool PK, int GS, int PASSES, int MT>
 __global__ __launch_bounds__(512) void k_gemm_decode(DecodeArgs p, int wn, int wk) {
     constexpr int SR = 16 * MT;                      // scale row stride
@@ -66,19 +72,22 @@ __global__ __launch_bounds__(512) void k_gemm_decode(DecodeArgs p, int wn, int w
     extern __shared__ __align__(16) uint8_t lds[];
     const int64_t K = p.K, N = p.N, G = K / 128;
     const int M = (int)p.M;
-    const int pitch = (int)K + 16;                    // codes [M][K + 16]
-    float *scales = (float *)(lds + M * pitch);        // [G][16 MT]
+    const int GC = wk * GS;                           // K-groups of this CTA
+    const int64_t g0 = (int64_t)blockIdx.y * GC;      // its first group
+    const int pitch = GC * 128 + 16;                  // codes [M][GC * 128 + 16]
+    float *scales = (float *)(lds + M * pitch);        // [GC][16 MT]
     const int tid = threadIdx.x, nthreads = blockDim.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l16 = lane & 15, q = lane >> 4;
     const int ct = wave % wn, slice = wave / wn;
     const int64_t n0 = ((int64_t)blockIdx.x * wn + ct) * 16;  // first column of this wave's tile
-    const int64_t gbeg = (int64_t)slice * GS;
+    const int lbeg = slice * GS;                      // first local group of this wave
+    const int64_t gbeg = g0 + lbeg;                   // ... as a global group
 
-    // activation task (row r, group g) per lane quad, 32 values a lane; quads
-    // past M * G load task 0 again and discard it
+    // activation task (row r, local group g) per lane quad, 32 values a lane;
+    // quads past M * GC load task 0 again and discard it
     const int quads = nthreads >> 2, quad = tid >> 2, sub = tid & 3;
-    const int tasks = M * (int)G;
+    const int tasks = M * GC;
     uint4 av[PB][QA ? 4 : 2];
     float sv[PB];
     auto load_act = [&](int batch) {
@@ -86,16 +95,16 @@ __global__ __launch_bounds__(512) void k_gemm_decode(DecodeArgs p, int wn, int w
         for (int j = 0; j < PB; ++j) {
             int task = quad + quads * (batch * PB + j);
             task = task < tasks ? task : 0;
-            const int r = task / (int)G, g = task % (int)G;
+            const int r = task / GC, g = task % GC;
             if (QA) {
-                const uint4 *src = (const uint4 *)(p.a + (int64_t)r * K + g * 128 + sub * 32);
+                const uint4 *src = (const uint4 *)(p.a + (int64_t)r * K + (g0 + g) * 128 + sub * 32);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) av[j][i] = src[i];
             } else {
-                const uint4 *src = (const uint4 *)(p.aq + (int64_t)r * K + g * 128 + sub * 32);
+                const uint4 *src = (const uint4 *)(p.aq + (int64_t)r * K + (g0 + g) * 128 + sub * 32);
                 av[j][0] = src[0];
                 av[j][1] = src[1];
-                sv[j] = p.as[(int64_t)r * G + g];
+                sv[j] = p.as[(int64_t)r * G + g0 + g];
             }
         }
     };
@@ -104,7 +113,7 @@ __global__ __launch_bounds__(512) void k_gemm_decode(DecodeArgs p, int wn, int w
         for (int j = 0; j < PB; ++j) {
             const int task = quad + quads * (batch * PB + j);
             if (task < tasks) {  // uniform across the 4 lanes of a quad
-                const int r = task / (int)G, g = task % (int)G;
+                const int r = task / GC, g = task % GC;
                 uint4 codes[2];
                 float sc;
                 if (QA) {
@@ -168,7 +177,7 @@ __global__ __launch_bounds__(512) void k_gemm_decode(DecodeArgs p, int wn, int w
     const float *wsrow = p.ws + nb * G + gbeg;
 #pragma unroll
     for (int g = 0; g < GS; ++g) {
-        const int gg = (int)gbeg + g;
+        const int gg = lbeg + g;  // local group
         const v8i wf = make_frag(wr[g][0], wr[g][1]);
         const float wsg = wsrow[g];
 #pragma unroll
@@ -200,31 +209,57 @@ __global__ __launch_bounds__(512) void k_gemm_decode(DecodeArgs p, int wn, int w
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const int row = 16 * mt + l16;
-            if (row < M)
+            if (row >= M) continue;
+            if (gridDim.y > 1)
+                *(v4f *)(p.part + ((int64_t)blockIdx.y * M + row) * N + n0 + 4 * q) = acc[mt];
+            else
                 *(uint2 *)(p.c + (int64_t)row * N + n0 + 4 * q) =
                     bf16x4_rne(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
         }
     }
 }
 
-// (wn, wk, passes) for a shape.  Measured on the MI355X (K = 4096,
-// N = 14336): eight-wave CTAs stream fastest; the activation quant, which
-// every CTA repeats, favours fewer and wider CTAs once M is large.  So
-// wn = 4 from 12 rows on when that leaves at least 192 CTAs, else wn = 2 when
-// that leaves at least 256 CTAs, else 1; then the smallest K split (K-groups
-// per wave a power of two, at most 16; the split itself any count up to 8,
-// e.g. 7 for K = 14336) that gives at least 8 waves per compute unit (4 on
-// row-major weights, whose 16-row load pattern does better with fewer), at
-// most 8 waves per CTA.  The activation side needs PASSES = M * (K/128) /
-// (16 * waves) register passes, at most 8 (two batches of 4).
-// R9K_DECODE_WN / R9K_DECODE_WK override (tuning).
-DecodeCfg decode_config(int64_t M, int64_t K, int64_t N, bool packed) {
-    DecodeCfg c{0, 0, 0, 0, 0, 0};
+// Is (wn, wk, gs, ksplit) a valid launch for M rows?  Fills c if so.
+static bool decode_fits(int64_t M, int64_t K, int64_t N, int wn, int wk, int64_t gs, int64_t ksplit, DecodeCfg &c) {
     const int64_t G = K / 128, tiles = N / 16;
-    if (M < 1 || M > 32) return c;
-    const int mt = M > 16 ? 2 : 1;
-    const size_t lds = (size_t)M * (K + 16) + (size_t)G * 16 * mt * 4;
-    if (lds > 150 * 1024) return c;
+    if (tiles % wn || wn * wk > 8 || gs < 1 || gs > MAX_GS || (gs & (gs - 1))) return false;
+    if ((int64_t)wk * gs * ksplit != G) return false;
+    const int mt = (int)((M + 15) / 16);
+    const int64_t gc = wk * gs;
+    const size_t lds = (size_t)M * (gc * 128 + 16) + (size_t)gc * 16 * mt * 4;
+    const size_t red = (size_t)wn * wk * mt * 64 * 16;  // the slice reduction reuses the codes region
+    if (std::max(lds, red) > 150 * 1024) return false;
+    const int64_t quads = 16 * wn * wk;
+    int passes = 1;
+    while (passes * quads < M * gc) passes *= 2;
+    if (passes > 8) return false;
+    const int64_t nch = gs < 4 ? gs : 4;
+    if ((passes < 4 ? 1 : passes / 4) > nch) return false;  // each activation batch follows a weight chunk
+    c = DecodeCfg{wn, wk, (int)gs, passes, std::max(lds, red), mt, (int)ksplit};
+    return true;
+}
+
+// (wn, wk, gs, ksplit) for a shape, M <= 64.  Measured on the MI355X (K = 4096,
+// N = 14336): eight-wave CTAs stream fastest; the activation quant, which
+// every CTA repeats, favours fewer and wider CTAs once M is large.
+//  1. All of K in one CTA (ksplit = 1): wn = 4 from 12 rows on when that leaves
+//     at least 192 CTAs, else wn = 2 when that leaves at least 256 CTAs, else
+//     1; then the smallest K split into waves (K-groups per wave a power of
+//     two, at most 16; the split any count up to 8, e.g. 7 for K = 14336) that
+//     gives at least 8 waves per compute unit (4 on row-major weights, whose
+//     16-row load pattern does better with fewer).  Taken when it fits and the
+//     CTAs together quantise at most 2^24 activation values.
+//  2. Else a K split across CTAs: CTAs of 4 x 2 waves (fewer column tiles if
+//     N is narrow), the largest K-groups per wave that still gives at least
+//     256 CTAs, with the split's partial sums reduced by a second kernel.
+// The activation side needs PASSES = M * (its K-groups) / (16 * waves)
+// register passes, at most 8 (two batches of 4).
+// R9K_DECODE_WN / R9K_DECODE_WK override step 1 (tuning).
+DecodeCfg decode_config(int64_t M, int64_t K, int64_t N, bool packed) {
+    DecodeCfg c{0, 0, 0, 0, 0, 0, 0};
+    const int64_t G = K / 128, tiles = N / 16;
+    if (M < 1 || M > 64) return c;
+    // 1. all of K per CTA
     int wn = (tiles % 2 == 0 && tiles / 2 >= 256) ? 2 : 1;
     if (M >= 12 && tiles % 4 == 0 && tiles / 4 >= 192) wn = 4;
     if (const char *e = getenv("R9K_DECODE_WN")) {
@@ -233,30 +268,42 @@ DecodeCfg decode_config(int64_t M, int64_t K, int64_t N, bool packed) {
     }
     int force_wk = 0;
     if (const char *e = getenv("R9K_DECODE_WK")) force_wk = atoi(e);
-    int wk = 0;
-    for (int cand = 1; cand <= 8; ++cand) {  // any split whose share is a power of two (K = 14336: 7 x 16)
+    DecodeCfg best{0, 0, 0, 0, 0, 0, 0};
+    for (int cand = 1; cand <= 8; ++cand) {
         if (force_wk && cand != force_wk) continue;
-        if (G % cand || wn * cand > 8) continue;
-        const int64_t gs = G / cand;
-        if (gs > MAX_GS || (gs & (gs - 1))) continue;
-        wk = cand;
+        if (G % cand) continue;
+        DecodeCfg t;
+        if (!decode_fits(M, K, N, wn, cand, G / cand, 1, t)) continue;
+        best = t;
         if ((tiles / wn) * wn * cand >= (packed ? 8 : 4) * 256) break;
     }
-    if (!wk) return c;
-    const int64_t quads = 16 * wn * wk;
-    int passes = 1;
-    while (passes * quads < M * G) passes *= 2;
-    if (passes > 8) return c;
-    const int64_t gs = G / wk, nch = gs < 4 ? gs : 4;
-    if ((passes < 4 ? 1 : passes / 4) > nch) return c;  // each activation batch follows a weight chunk
-    c.wn = wn;
-    c.wk = wk;
-    c.gs = (int)(G / wk);
-    c.passes = passes;
-    // the slice reduction reuses the codes region: MT 1 KiB rows of v4f per wave
-    c.lds = std::max(lds, (size_t)wn * wk * mt * 64 * 16);
-    c.mt = mt;
-    return c;
+    if (best.wn && ((tiles / best.wn) * M * K <= (int64_t(1) << 24) || force_wk)) return best;
+    // 2. a K split across CTAs
+    const int wn2 = tiles % 4 == 0 && tiles / 4 >= 64 ? 4 : tiles % 2 == 0 && tiles / 2 >= 64 ? 2 : 1;
+    const int wk2 = 8 / wn2 >= 2 ? 2 : 1;
+    DecodeCfg split{0, 0, 0, 0, 0, 0, 0};
+    for (int64_t gs = MAX_GS; gs >= 1; gs /= 2) {
+        if (G % (wk2 * gs)) continue;
+        const int64_t ks = G / (wk2 * gs);
+        if (ks < 2) continue;
+        DecodeCfg t;
+        if (!decode_fits(M, K, N, wn2, wk2, gs, ks, t)) continue;
+        split = t;
+        if ((tiles / wn2) * ks >= 256) break;
+    }
+    // every n-tile CTA quantises its own copy of the activation slice: past
+    // 2^25 such elements (M = 64 at K = 14336, N = 4096) the tiled engine is faster
+    if (split.wn && (tiles / split.wn) * M * K <= (int64_t(1) << 25)) return split;
+    return best.wn && (tiles / best.wn) * M * K <= (int64_t(1) << 26) ? best : c;
+}
+
+size_t decode_partial_bytes(int64_t M, int64_t K, int64_t N) {
+    size_t b = 0;
+    for (bool packed : {false, true}) {
+        const DecodeCfg c = decode_config(M, K, N, packed);
+        if (c.wn && c.ksplit > 1) b = std::max(b, sizeof(float) * (size_t)c.ksplit * M * N);
+    }
+    return align_up(b, 256);
 }
 
 // one instantiation: its 160 KiB dynamic-LDS limit is set once per device
@@ -290,7 +337,13 @@ static hipError_t launch_ps(const DecodeArgs &a, const DecodeCfg &c, hipStream_t
 
 template <bool QA, bool PK, int GS>
 static hipError_t launch_mt(const DecodeArgs &a, const DecodeCfg &c, hipStream_t s, dim3 grid, dim3 block) {
-    return c.mt == 2 ? launch_ps<QA, PK, GS, 2>(a, c, s, grid, block) : launch_ps<QA, PK, GS, 1>(a, c, s, grid, block);
+    switch (c.mt) {
+        case 1: return launch_ps<QA, PK, GS, 1>(a, c, s, grid, block);
+        case 2: return launch_ps<QA, PK, GS, 2>(a, c, s, grid, block);
+        case 3: return launch_ps<QA, PK, GS, 3>(a, c, s, grid, block);
+        case 4: return launch_ps<QA, PK, GS, 4>(a, c, s, grid, block);
+    }
+    return hipErrorInvalidValue;
 }
 
 template <bool QA, bool PK>
@@ -306,10 +359,13 @@ static hipError_t launch_gs(const DecodeArgs &a, const DecodeCfg &c, hipStream_t
 }
 
 hipError_t launch_gemm_decode(const DecodeArgs &a, const DecodeCfg &c, hipStream_t s) {
-    const dim3 grid((unsigned)(a.N / 16 / c.wn));
+    const dim3 grid((unsigned)(a.N / 16 / c.wn), (unsigned)c.ksplit);
     const dim3 block((unsigned)(64 * c.wn * c.wk));
-    if (a.a) return a.packed ? launch_gs<true, true>(a, c, s, grid, block) : launch_gs<true, false>(a, c, s, grid, block);
-    return a.packed ? launch_gs<false, true>(a, c, s, grid, block) : launch_gs<false, false>(a, c, s, grid, block);
+    hipError_t e;
+    if (a.a) e = a.packed ? launch_gs<true, true>(a, c, s, grid, block) : launch_gs<true, false>(a, c, s, grid, block);
+    else e = a.packed ? launch_gs<false, true>(a, c, s, grid, block) : launch_gs<false, false>(a, c, s, grid, block);
+    if (e != hipSuccess || c.ksplit == 1) return e;
+    return launch_splitk_reduce(a.part, a.c, a.M, a.N, c.ksplit, s);
 }
 
 }  // namespace r9k

@@ -21,17 +21,20 @@ hipError_t launch_pack_weight(const uint8_t *wq, int64_t N, int64_t K, uint8_t *
 hipError_t launch_quant_weight(const uint16_t *w, int64_t N, int64_t K, uint8_t *wq, float *ws, hipStream_t s);
 hipError_t launch_encode_e4m3(const float *x, int64_t n, uint8_t *codes, hipStream_t s);
 
-// ---- decode engine, 1 <= M <= 32 (gemm_decode.hip) ----
+// ---- decode engine, 1 <= M <= 64 (gemm_decode.hip) ----
 struct DecodeCfg {
     int wn;      // 16-column tiles per CTA (0: the shape does not fit this engine)
     int wk;      // K slices per column tile (waves per CTA = wn * wk)
     int gs;      // K-groups per wave: (K / 128) / wk
     int passes;  // activation groups per lane quad
     size_t lds;  // dynamic LDS bytes
-    int mt;      // row tiles of 16 (1 or 2)
+    int mt;      // row tiles of 16 (1 to 4)
+    int ksplit;  // CTAs along K (> 1: fp32 partials in the workspace, then a reduce)
 };
 // fused: the kernel quantises the activations itself; otherwise it reads codes.
 DecodeCfg decode_config(int64_t M, int64_t K, int64_t N, bool packed);
+// Workspace the decode engine needs for its partial sums under either layout.
+size_t decode_partial_bytes(int64_t M, int64_t K, int64_t N);
 struct DecodeArgs {
     const uint16_t *a;  // bf16 activations (fused form), or NULL
     const uint8_t *aq;  // pre-quantised codes (split form)
@@ -41,6 +44,7 @@ struct DecodeArgs {
     uint16_t *c;
     int64_t M, K, N;
     bool packed;
+    float *part;        // fp32 partials [ksplit][M][N] when the config splits K
 };
 hipError_t launch_gemm_decode(const DecodeArgs &args, const DecodeCfg &cfg, hipStream_t s);
 

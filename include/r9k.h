@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define R9K_ABI_VERSION 2
+#define R9K_ABI_VERSION 3
 
 /* Return codes. */
 #define R9K_OK 0
@@ -171,6 +171,23 @@ int r9k_gemm_fp8_block_qa_packed(const uint16_t *a, int64_t M, int64_t K, const 
 #define R9K_ENGINE_TILED 2
 int r9k_set_dispatch(int skinny_max_m, int engine);
 int r9k_get_dispatch(int *skinny_max_m, int *engine);
+
+/* The kernel a GEMM call of this shape runs under the current dispatch
+ * setting (host only, launches nothing, needs no device): kernel receives
+ * R9K_KERNEL_DECODE (the whole-row weight-streaming kernel of the decode
+ * widths), R9K_KERNEL_SKINNY (the split-K skinny kernel), R9K_KERNEL_TILED
+ * (the LDS-tiled MFMA GEMM) or R9K_KERNEL_NONE (M = 0: nothing is launched);
+ * ksplit receives the number of CTAs that share one output tile along K
+ * (1: no K split, and no reduction launch follows).  packed (0 or 1) says
+ * whether the weight is in the fragment order of r9k_pack_weight; the same
+ * answer holds with and without the activation quant in the call.
+ * Errors: NULLPTR (kernel, ksplit); SHAPE as for r9k_gemm_fp8_block; ARG if
+ * packed is neither 0 nor 1. */
+#define R9K_KERNEL_NONE 0
+#define R9K_KERNEL_DECODE 1
+#define R9K_KERNEL_SKINNY 2
+#define R9K_KERNEL_TILED 3
+int r9k_gemm_fp8_block_plan(int64_t M, int64_t K, int64_t N, int packed, int *kernel, int *ksplit);
 
 /* ------------------------------------------------------------------------ */
 /* MoE decode                                                                */

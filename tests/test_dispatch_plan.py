@@ -1,0 +1,96 @@
+"""The dispatcher's decision on the host: which kernel a GEMM call of a given
+shape runs, with its K split, through r9k_gemm_fp8_block_plan (launches
+nothing, needs no device).  The workspace the library asks for must cover the
+fp32 partials of every K split it plans.
+"""
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def r9k():
+    import block_scaled_fp8_r9k_amd as m
+    m.set_dispatch(255, m.ENGINE_AUTO)
+    yield m
+    m.set_dispatch(255, m.ENGINE_AUTO)
+
+
+def test_kernel_codes_match_header(r9k):
+    text = open(os.path.join(ROOT, "include", "r9k.h")).read()
+    d = {k: int(v) for k, v in re.findall(r"#define\s+(R9K_KERNEL_\w+)\s+(\d+)", text)}
+    assert d == {"R9K_KERNEL_NONE": r9k.KERNEL_NONE, "R9K_KERNEL_DECODE": r9k.KERNEL_DECODE,
+                 "R9K_KERNEL_SKINNY": r9k.KERNEL_SKINNY, "R9K_KERNEL_TILED": r9k.KERNEL_TILED}
+
+
+@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 16])
+def test_decode_sweep_streams_whole_rows(r9k, M, packed):
+    # single-token to 16-row decode on the 4096 -> 14336 projection: one pass
+    # over the weight, no K split
+    assert r9k.gemm_fp8_block_plan(M, 4096, 14336, packed) == (r9k.KERNEL_DECODE, 1)
+
+
+@pytest.mark.parametrize("M,K,N", [(32, 4096, 4096), (17, 4096, 4096), (64, 4096, 4096), (32, 14336, 4096),
+                                   (16, 14336, 4096), (8, 14336, 4096)])
+def test_decode_k_split(r9k, M, K, N):
+    for packed in (False, True):
+        kern, ks = r9k.gemm_fp8_block_plan(M, K, N, packed)
+        assert kern == r9k.KERNEL_DECODE and ks >= 2, (M, K, N, packed, kern, ks)
+        assert (K // 128) % ks == 0
+
+
+@pytest.mark.parametrize("M,K,N", [(64, 14336, 4096), (128, 4096, 4096), (255, 14336, 4096), (256, 4096, 4096),
+                                   (4096, 4096, 12288)])
+def test_wide_shapes_go_tiled(r9k, M, K, N):
+    kern, ks = r9k.gemm_fp8_block_plan(M, K, N)
+    assert kern == r9k.KERNEL_TILED and ks >= 1
+
+
+def test_prefill_has_no_k_split(r9k):
+    # 16 x 48 tiles of 256 x 256 already fill the chip
+    assert r9k.gemm_fp8_block_plan(4096, 4096, 12288) == (r9k.KERNEL_TILED, 1)
+
+
+def test_empty_call_plans_nothing(r9k):
+    assert r9k.gemm_fp8_block_plan(0, 4096, 4096) == (r9k.KERNEL_NONE, 0)
+
+
+def test_forced_engines(r9k):
+    try:
+        r9k.set_dispatch(255, r9k.ENGINE_TILED)
+        assert r9k.gemm_fp8_block_plan(1, 4096, 14336)[0] == r9k.KERNEL_TILED
+        r9k.set_dispatch(0, r9k.ENGINE_AUTO)           # the skinny engine takes no width
+        assert r9k.gemm_fp8_block_plan(1, 4096, 14336)[0] == r9k.KERNEL_TILED
+        r9k.set_dispatch(255, r9k.ENGINE_SKINNY)
+        # a shape the decode kernel does not take stays on the skinny kernel
+        assert r9k.gemm_fp8_block_plan(200, 4096, 4096)[0] == r9k.KERNEL_SKINNY
+        assert r9k.gemm_fp8_block_plan(4, 4096, 4096)[0] == r9k.KERNEL_DECODE
+    finally:
+        r9k.set_dispatch(255, r9k.ENGINE_AUTO)
+
+
+@pytest.mark.parametrize("M", [1, 5, 16, 17, 32, 48, 64, 65, 100, 128, 200, 255, 256, 300, 1024])
+@pytest.mark.parametrize("K,N", [(4096, 4096), (14336, 4096), (4096, 14336), (512, 1024), (1280, 384)])
+def test_workspace_covers_partials(r9k, M, K, N):
+    ws = r9k.gemm_fp8_block_workspace(M, K, N)
+    for packed in (False, True):
+        kern, ks = r9k.gemm_fp8_block_plan(M, K, N, packed)
+        assert kern in (r9k.KERNEL_DECODE, r9k.KERNEL_SKINNY, r9k.KERNEL_TILED)
+        assert 1 <= ks <= K // 128
+        if ks > 1:
+            assert ws >= 4 * ks * M * N, (M, K, N, packed, ks, ws)
+
+
+def test_plan_argument_checks(r9k):
+    L = r9k.lib()
+    from ctypes import byref, c_int
+    k, s = c_int(), c_int()
+    assert L.r9k_gemm_fp8_block_plan(1, 4096, 4096, 0, None, byref(s)) == -1
+    assert L.r9k_gemm_fp8_block_plan(1, 4000, 4096, 0, byref(k), byref(s)) == -2
+    assert L.r9k_gemm_fp8_block_plan(1, 4096, 4000, 0, byref(k), byref(s)) == -2
+    assert L.r9k_gemm_fp8_block_plan(-1, 4096, 4096, 0, byref(k), byref(s)) == -2
+    assert L.r9k_gemm_fp8_block_plan(1, 4096, 4096, 2, byref(k), byref(s)) == -7

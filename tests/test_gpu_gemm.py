@@ -190,3 +190,22 @@ def test_gemm_decode_two_row_tiles(r9k, ora, M, K, N):
     wp = r9k.pack_weight(p.wq_d)
     assert_bits_equal(host(r9k.gemm_fp8_block_qa_packed(p.a_d, wp, p.ws_d)), got, "packed == row-major")
     assert_bits_equal(p.run(r9k, 0, fused=False), got, "split == fused")
+
+
+@pytest.mark.parametrize("M,K,N", [(17, 4096, 4096), (32, 4096, 4096), (64, 4096, 4096), (16, 14336, 4096),
+                                   (32, 14336, 4096), (8, 14336, 4096)])
+def test_gemm_decode_k_split(r9k, ora, M, K, N):
+    """Decode-kernel shapes that split K across CTAs (fp32 partials + ordered reduce), full output,
+    both weight layouts, fused == split form."""
+    for packed in (False, True):
+        kern, ks = r9k.gemm_fp8_block_plan(M, K, N, packed)
+        assert kern == r9k.KERNEL_DECODE and ks > 1, (packed, kern, ks)
+    say("decode k-split", M, K, N)
+    p = Problem(r9k, ora, M, K, N, seed=M + 11)
+    c64 = p.oracle_full(ora)
+    got = p.run(r9k, 0, fused=True)
+    assert_close(ora, got, c64, f"decode k-split {M}x{K}x{N}")
+    wp = r9k.pack_weight(p.wq_d)
+    assert_bits_equal(host(r9k.gemm_fp8_block_qa_packed(p.a_d, wp, p.ws_d)), got, "packed == row-major")
+    assert_bits_equal(p.run(r9k, 0, fused=False), got, "split == fused")
+    assert_bits_equal(p.run(r9k, 0, fused=True), got, "repeat")
