@@ -11,24 +11,25 @@
 // widths the fused entry point quantises A once per call instead of once per
 // column tile, which would cost more VALU time than the MFMAs.
 //
-// CTA tile: 128 rows of A x 256 columns (two weight block rows), 4 waves, one
-// per SIMD, so that each wave has the whole register file (the 128 fp32
-// accumulators, the fragments and the MFMA results in flight).  Wave w owns
-// columns 128 (w & 1) .. +127 (one weight block row, so one weight scale per
-// group) and rows 64 (w >> 1) .. +63: 8 x 4 MFMA tiles of 16 x 16 x 128,
-// computed as C^T = W A^T so that a lane's four outputs of a tile share one
-// row of A, and with it one activation scale.  The promotion is then one
-// multiply per row tile and one FMA per output per group.
+// Work split: C^T = W A^T, so that a lane's four outputs of an MFMA tile
+// share one row of A, and with it one activation scale; the promotion is one
+// multiply per row tile and one FMA per output per group.  Each wave owns TN
+// column tiles of 16 (all inside one weight block row: one weight scale per
+// group) by four row tiles of 16, two waves per SIMD; the CTA shapes are
+// listed with Cfg below.  Per group a wave keeps its four A fragments in
+// registers and streams its weight fragments from LDS two column tiles ahead,
+// and each MFMA is issued right after the promotion FMAs of the product it
+// replaces, so that one register set holds every product in flight.
 //
-// A stage holds one group: the W tile [256 rows][128 bytes], the A tile
-// [128 rows][128 bytes] and the wave's 64 activation scales; three stages
-// (147 KiB of LDS), filled two groups ahead.  Everything moves from global
-// memory straight into LDS (global_load_lds, no register staging), so one
-// wait on the wave's load counter covers a stage.  A 16-byte load instruction
-// fills 1 KiB of LDS, 8 rows; lane l writes physical chunk l % 8 of its row
-// and fetches the logical chunk that belongs there: chunk c of row r lives at
-// chunk c ^ ((r >> 1) & 7), so the 16 rows a fragment read touches in one LDS
-// cycle fall on distinct banks.
+// A stage holds one group: the W tile [BN rows][128 bytes], the A tile
+// [BM rows][128 bytes] and the scales; two or three stages, filled one or two
+// groups ahead.  Everything moves from global memory straight into LDS
+// (global_load_lds, no register staging), so one wait on the wave's load
+// counter covers a stage.  A 16-byte load instruction fills 1 KiB of LDS, 8
+// rows; lane l writes physical chunk l % 8 of its row and fetches the logical
+// chunk that belongs there: chunk c of row r lives at chunk c ^ ((r >> 1) & 7),
+// so the 16 rows a fragment read touches in one LDS cycle fall on distinct
+// banks.
 #include <algorithm>
 #include <cstdlib>
 #include <mutex>
@@ -101,23 +102,25 @@ __device__ __forceinline__ v8i frag2(const uint8_t *p0, const uint8_t *p1) {
     return make_frag(*(const uint4 *)p0, *(const uint4 *)p1);
 }
 
-// pc = the fp8 MFMA of a and b (unit block exponents); acc += pp * sc, for the
-// products pp of an earlier MFMA.  One asm block, so that the compiler keeps
-// the issue order: each block's FMAs read a result that several MFMAs issued
-// before have long produced, and run while this block's MFMA executes.  The
-// caller guarantees that distance (at least four MFMAs), which also covers
-// the wait the hardware needs before VALU reads an MFMA result.
-__device__ __forceinline__ void mfma_promote(v4f &pc, const v8i &a, const v8i &b, int e127, const v4f &pp,
-                                             float sc, v4f &acc) {
+// acc += pr * sc, then pr = the fp8 MFMA of a and b (unit block exponents).
+// Two volatile asm statements, which the compiler keeps in this order: the
+// FMAs read the product that an MFMA four calls earlier wrote into pr (long
+// done: the caller keeps that distance, which also covers the wait the
+// hardware needs before VALU reads an MFMA result), at issue, so that this
+// call's MFMA may overwrite the same registers; one register set thus holds
+// every product in flight.  The FMAs run while the previous MFMA executes.
+__device__ __forceinline__ void promote_mfma(v4f &pr, const v8i &a, const v8i &b, int e127, float sc, v4f &acc) {
     float a0 = acc[0], a1 = acc[1], a2 = acc[2], a3 = acc[3];
     asm volatile(
-        "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %5, %6, 0, %7, %7 op_sel_hi:[0,0,0]\n\t"
-        "v_fmac_f32 %1, %8, %12\n\t"
-        "v_fmac_f32 %2, %9, %12\n\t"
-        "v_fmac_f32 %3, %10, %12\n\t"
-        "v_fmac_f32 %4, %11, %12"
-        : "=&v"(pc), "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3)
-        : "v"(a), "v"(b), "v"(e127), "v"(pp[0]), "v"(pp[1]), "v"(pp[2]), "v"(pp[3]), "v"(sc));
+        "v_fmac_f32 %0, %4, %8\n\t"
+        "v_fmac_f32 %1, %5, %8\n\t"
+        "v_fmac_f32 %2, %6, %8\n\t"
+        "v_fmac_f32 %3, %7, %8"
+        : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3)
+        : "v"(pr[0]), "v"(pr[1]), "v"(pr[2]), "v"(pr[3]), "v"(sc));
+    asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, 0, %3, %3 op_sel_hi:[0,0,0]"
+                 : "=&v"(pr)
+                 : "v"(a), "v"(b), "v"(e127));
     acc = v4f{a0, a1, a2, a3};
 }
 
@@ -219,12 +222,12 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_gemm_tiled(TiledArgs p) {
     for (int i = 0; i < TN; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-    // products and scales of the previous column tile, zero before the first
-    v4f pp[4];
+    // products of the previous column tile and their scales, zero before the first
+    v4f pr[4];
     float scp[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        pp[j] = v4f{0.f, 0.f, 0.f, 0.f};
+        pr[j] = v4f{0.f, 0.f, 0.f, 0.f};
         scp[j] = 0.f;
     }
     const int e127 = 127;  // E8M0 block exponent 0: unit scale
@@ -246,38 +249,32 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_gemm_tiled(TiledArgs p) {
         const uint8_t *wt = lds + st * STAGE;
         const uint8_t *at = wt + WBYTES;
         const float *sl = (const float *)(at + ABYTES + wave * 512);
+        // the weight fragments of column tiles 0 and 1; tile i + 2's is read
+        // during tile i, into the registers tile i - 1 used
+        v8i wq[3];
+        wq[0] = frag2(wt + wfo, wt + wfo2);
+        if (TN > 1) wq[1] = frag2(wt + wfo + 2048, wt + wfo2 + 2048);
+        v8i af[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) af[j] = frag2(wt + afo + 2048 * j, wt + afo2 + 2048 * j);
         const float wsg = sl[64 + lane];
         float sc[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) sc[j] = sl[16 * j + l16] * wsg;
-        v8i af[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) af[j] = frag2(wt + afo + 2048 * j, wt + afo2 + 2048 * j);
 
         // Column tile i's MFMAs run together with the promotion of tile
         // i - 1 (tile 0's with the previous group's last tile), so an FMA
-        // reads a product four MFMAs old.
-        // With eight column tiles the next tile's fragment is read only after
-        // this tile's first block (its offset passes through an empty asm, so
-        // the compiler cannot hoist all eight reads and run out of registers).
-        v8i wf = frag2(wt + wfo, wt + wfo2);
+        // reads a product four MFMAs old.  The fragment offsets are constants
+        // from one stage base, so every read takes its offset in the
+        // instruction and costs no VALU work.
 #pragma unroll
         for (int i = 0; i < TN; ++i) {
-            v4f pc[4];
-            v8i wfn;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                if (i == 0) mfma_promote(pc[j], wf, af[j], e127, pp[j], scp[j], acc[TN - 1][j]);
-                else mfma_promote(pc[j], wf, af[j], e127, pp[j], sc[j], acc[i - 1][j]);
-                if (j == 0 && i + 1 < TN) {
-                    int o1 = wfo + 2048 * (i + 1), o2 = wfo2 + 2048 * (i + 1);
-                    if (TN > 4) asm volatile("" : "+v"(o1), "+v"(o2));
-                    wfn = frag2(wt + o1, wt + o2);
-                }
+                if (i == 0) promote_mfma(pr[j], wq[0], af[j], e127, scp[j], acc[TN - 1][j]);
+                else promote_mfma(pr[j], wq[i % 3], af[j], e127, sc[j], acc[i - 1][j]);
+                if (j == 0 && i + 2 < TN) wq[(i + 2) % 3] = frag2(wt + wfo + 2048 * (i + 2), wt + wfo2 + 2048 * (i + 2));
             }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) pp[j] = pc[j];
-            if (i + 1 < TN) wf = wfn;
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) scp[j] = sc[j];
@@ -287,7 +284,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_gemm_tiled(TiledArgs p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[TN - 1][j][e] = __builtin_fmaf(pp[j][e], scp[j], acc[TN - 1][j][e]);
+        for (int e = 0; e < 4; ++e) acc[TN - 1][j][e] = __builtin_fmaf(pr[j][e], scp[j], acc[TN - 1][j][e]);
 
     // lane holds, per tile (i, j), row m = m0 + 64 wm + 16 j + l16 and the four
     // columns n = n0 + TN 16 wn + 16 i + 4 q .. +3
