@@ -88,7 +88,11 @@ __global__ __launch_bounds__(512) void k_gemm_decode(DecodeArgs p, int wn, int w
     // quads past M * GC load task 0 again and discard it
     const int quads = nthreads >> 2, quad = tid >> 2, sub = tid & 3;
     const int tasks = M * GC;
-    uint4 av[PB][QA ? 4 : 2];
+    // fused: bf16 values (four uint4 a lane); codes path: e4m3 codes (two
+    // 16-byte vectors) and the group scale.  The codes are held as plain
+    // vectors: copied as uint4 aggregates they would stay in scratch memory.
+    uint4 av[PB][QA ? 4 : 1];
+    u32x4 cv[PB][QA ? 1 : 2];
     float sv[PB];
     auto load_act = [&](int batch) {
 #pragma unroll
@@ -96,14 +100,14 @@ __global__ __launch_bounds__(512) void k_gemm_decode(DecodeArgs p, int wn, int w
             int task = quad + quads * (batch * PB + j);
             task = task < tasks ? task : 0;
             const int r = task / GC, g = task % GC;
-            if (QA) {
+            if constexpr (QA) {
                 const uint4 *src = (const uint4 *)(p.a + (int64_t)r * K + (g0 + g) * 128 + sub * 32);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) av[j][i] = src[i];
             } else {
-                const uint4 *src = (const uint4 *)(p.aq + (int64_t)r * K + (g0 + g) * 128 + sub * 32);
-                av[j][0] = src[0];
-                av[j][1] = src[1];
+                const u32x4 *src = (const u32x4 *)(p.aq + (int64_t)r * K + (g0 + g) * 128 + sub * 32);
+                cv[j][0] = src[0];
+                cv[j][1] = src[1];
                 sv[j] = p.as[(int64_t)r * G + g0 + g];
             }
         }
@@ -114,19 +118,19 @@ __global__ __launch_bounds__(512) void k_gemm_decode(DecodeArgs p, int wn, int w
             const int task = quad + quads * (batch * PB + j);
             if (task < tasks) {  // uniform across the 4 lanes of a quad
                 const int r = task / GC, g = task % GC;
-                uint4 codes[2];
+                u32x4 *dst = (u32x4 *)(lds + r * pitch + g * 128 + sub * 32);
                 float sc;
-                if (QA) {
+                if constexpr (QA) {
                     uint4 v[4] = {av[j][0], av[j][1], av[j][2], av[j][3]};
+                    uint4 codes[2];
                     quant_group4(v, codes, sc);
+                    dst[0] = u32x4{codes[0].x, codes[0].y, codes[0].z, codes[0].w};
+                    dst[1] = u32x4{codes[1].x, codes[1].y, codes[1].z, codes[1].w};
                 } else {
-                    codes[0] = av[j][0];
-                    codes[1] = av[j][1];
+                    dst[0] = cv[j][0];
+                    dst[1] = cv[j][1];
                     sc = sv[j];
                 }
-                uint4 *dst = (uint4 *)(lds + r * pitch + g * 128 + sub * 32);
-                dst[0] = codes[0];
-                dst[1] = codes[1];
                 if (sub == 0) scales[g * SR + r] = sc;
             }
         }

@@ -264,21 +264,36 @@ __global__ __launch_bounds__(256) void k_moe_silu_quant(MoeArgs p) {
 }
 
 // out[t][n] = bf16(sum_j w[t][j] * y[t*topk + j][n]), j ascending, fp32 fma.
-// Pairs whose expert id is out of range contribute nothing.  4 columns per thread.
+// Pairs whose expert id is out of range contribute nothing.  4 columns per
+// thread; the slots' loads go out 8 at a time, so that the sum waits for one
+// round trip per 8 slots (a slot past topk, or with an invalid id, reads an
+// existing y row and discards it).
 __global__ __launch_bounds__(256) void k_moe_combine(MoeArgs p) {
+    constexpr int SL = 8;
     const int64_t H = p.H, topk = p.topk;
     const int64_t t = blockIdx.y;
     const int64_t n = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (n >= H) return;
     v4f acc = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t jj = 0; jj < topk; ++jj) {
-        const int64_t pr = t * topk + jj;
-        const int32_t e = p.ids[pr];
-        if (e < 0 || e >= p.E) continue;
-        const float w = p.tw[pr];
-        const v4f y = *(const v4f *)(p.y + pr * H + n);
+    for (int64_t j0 = 0; j0 < topk; j0 += SL) {
+        bool use[SL];
+        float w[SL];
+        v4f y[SL];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(w, y[i], acc[i]);
+        for (int jj = 0; jj < SL; ++jj) {
+            const int64_t j = j0 + jj;
+            const int64_t pr = t * topk + (j < topk ? j : topk - 1);
+            const int32_t e = p.ids[pr];
+            use[jj] = j < topk && e >= 0 && e < p.E;
+            w[jj] = p.tw[pr];
+            y[jj] = *(const v4f *)(p.y + pr * H + n);
+        }
+#pragma unroll
+        for (int jj = 0; jj < SL; ++jj)
+            if (use[jj]) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(w[jj], y[jj][i], acc[i]);
+            }
     }
     *(uint2 *)(p.out + t * H + n) = bf16x4_rne(acc[0], acc[1], acc[2], acc[3]);
 }
