@@ -25,7 +25,7 @@ LIB = os.path.join(HERE, "libr9k.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 CFLAGS = [
-    "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
+    "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "--offload-arch=gfx950",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",
     "-mllvm", "-amdgpu-mfma-vgpr-form",

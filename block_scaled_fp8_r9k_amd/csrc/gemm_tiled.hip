@@ -335,7 +335,13 @@ TiledPlan tiled_plan(int64_t M, int64_t K, int64_t N) {
     const int64_t G = K / 128;
     if (ctas_of<CfgC>(M, N) >= 256) t.shape = TILE_C;
     else if (ctas_of<CfgB>(M, N) >= 256) t.shape = TILE_B;
-    else if (M <= 256) t.shape = M <= 128 ? TILE_M1 : TILE_M2;
+    else if (M <= 256) {
+        // 64-column tiles, except for long K above 128 rows, where the 256 x 128
+        // tile split about 8 ways takes 10-12% less time (measured on the MI355X
+        // at N = 4096, K = 14336, M = 192 and 255)
+        if (M > 128 && G >= 64) t.shape = TILE_B;
+        else t.shape = M <= 128 ? TILE_M1 : TILE_M2;
+    }
     if (const char *e = getenv("R9K_TILED_CFG")) {  // b|c|1|2 forces the tile shape (tuning)
         if (e[0] == 'b') t.shape = TILE_B;
         if (e[0] == 'c') t.shape = TILE_C;

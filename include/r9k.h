@@ -54,6 +54,12 @@
 extern "C" {
 #endif
 
+/* Every function declared here is exported from libr9k.so; the library's
+ * internal symbols are not (it is built with hidden visibility). */
+#if defined(__GNUC__) || defined(__clang__)
+#pragma GCC visibility push(default)
+#endif
+
 #define R9K_ABI_VERSION 3
 
 /* Return codes. */
@@ -238,6 +244,10 @@ int r9k_moe_fp8_decode_packed(const uint16_t *x, int64_t T, int64_t H, const int
  * 4 hs [P][I/128] fp32 (P = T*topk; gu, hq and hs are written by the
  * three-launch path only).  Host only.  Errors: NULLPTR; SHAPE; ARG. */
 int r9k_moe_ws_offset(int64_t T, int64_t H, int64_t E, int64_t I, int64_t topk, int which, size_t *offset);
+
+#if defined(__GNUC__) || defined(__clang__)
+#pragma GCC visibility pop
+#endif
 
 #ifdef __cplusplus
 }
