@@ -260,7 +260,12 @@ def bench_mid(torch, r9k, inputs, dev, reps):
 
 def bench_moe(torch, r9k, inputs, dev, reps):
     T, H, E, I, k = 16, 2048, 128, 768, 8
-    x, ids, tw, w13, w2 = inputs.moe_inputs(0, T, H, E, I, k)
+    x, logits, w13, w2 = inputs.moe_inputs(0, T, H, E, I)
+    # routing (not timed): top-k of the softmax, weights renormalised over the top-k
+    pr = torch.softmax(torch.from_numpy(logits).double(), dim=1)
+    pk, idk = torch.topk(pr, k, dim=1)
+    ids = idk.to(torch.int32).numpy()
+    tw = (pk / pk.sum(dim=1, keepdim=True)).float().numpy()
     q13, s13 = r9k.quant_weight(dev(w13.reshape(E * 2 * I, H)))
     q2, s2 = r9k.quant_weight(dev(w2.reshape(E * H, I)))
     del w13, w2

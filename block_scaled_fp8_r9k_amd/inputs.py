@@ -1,19 +1,17 @@
 """Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
 
 This module holds none of the method's arithmetic: it draws random numbers,
-rounds them to bf16 with torch's own conversion, picks outlier channels and
-routes MoE tokens (routing is the caller's job; the library consumes ids and
-weights).  Quantisation, GEMMs and everything else the method computes happen
-in the GPU library or in the oracle, each on its own.
+rounds them to bf16 with torch's own conversion and picks outlier channels.
+Quantisation, GEMMs, MoE routing and everything else the method computes
+happen in the GPU library or in the oracle, each on its own.
 
 Recipe (the workloads of the release pages' decode/prefill GEMMs):
   * activations: z ~ N(0, 1) in fp32; a fixed set of round(0.01 * K) channels
     (the same for every row) is multiplied by 20 before rounding to bf16;
   * weights: fp32(0.02 * z), rounded to bf16; quantised per 128x128 block by
     whichever side consumes them;
-  * MoE: router logits ~ N(0, 1) in fp32, softmax in fp64, the top-k by
-    probability (ties to the lower expert id), weights renormalised over the
-    top-k and rounded to fp32.
+  * MoE: router logits ~ N(0, 1) in fp32 (the routing itself, top-k with
+    renormalised softmax weights, is a step of the method).
 Streams: numpy PCG64 seeded from SeedSequence([seed, tag]), one tag per tensor.
 """
 from __future__ import annotations
@@ -53,29 +51,21 @@ def weights(seed: int, N: int, K: int, tag: int = TAG_W, sub: int = 0) -> np.nda
     return to_bf16_bits(z * np.float32(0.02))
 
 
-def route(logits: np.ndarray, topk: int) -> tuple[np.ndarray, np.ndarray]:
-    """Softmax (fp64) -> top-k ids (ties to the lower id) -> weights renormalised, fp32."""
-    l = np.asarray(logits, np.float64)
-    p = np.exp(l - l.max(axis=1, keepdims=True))
-    p /= p.sum(axis=1, keepdims=True)
-    # stable sort on -p keeps the lower id first among equal probabilities
-    ids = np.argsort(-p, axis=1, kind="stable")[:, :topk].astype(np.int32)
-    pk = np.take_along_axis(p, ids.astype(np.int64), axis=1)
-    w = (pk / pk.sum(axis=1, keepdims=True)).astype(np.float32)
-    return ids, w
-
-
-def moe_inputs(seed: int, T: int, H: int, E: int, I: int, topk: int, outliers: bool = True):
-    """x [T,H] bf16, ids [T,k] i32, w [T,k] f32, w13 [E,2I,H] bf16, w2 [E,H,I] bf16."""
-    x = activations(seed, T, H, outliers=outliers, tag=TAG_X)
-    logits = rng(seed, TAG_LOGITS).standard_normal((T, E), dtype=np.float32)
-    ids, w = route(logits, topk)
+def moe_inputs(seed: int, T: int, H: int, E: int, I: int):
+    """x [T,H] bf16, router logits [T,E] f32, w13 [E,2I,H] bf16, w2 [E,H,I] bf16."""
+    x = activations(seed, T, H, outliers=True, tag=TAG_X)
+    logits = router_logits(seed, T, E)
     w13 = np.empty((E, 2 * I, H), np.uint16)
     w2 = np.empty((E, H, I), np.uint16)
     for e in range(E):
         w13[e] = weights(seed, 2 * I, H, tag=TAG_W13, sub=e)
         w2[e] = weights(seed, H, I, tag=TAG_W2, sub=e)
-    return x, ids, w, w13, w2
+    return x, logits, w13, w2
+
+
+def router_logits(seed: int, T: int, E: int) -> np.ndarray:
+    """Router logits [T, E] fp32, N(0, 1)."""
+    return rng(seed, TAG_LOGITS).standard_normal((T, E), dtype=np.float32)
 
 
 def quant_edge_groups() -> np.ndarray:

@@ -71,6 +71,8 @@ def lib():
         L.ora_moe_silu_mul.argtypes = [u16p, c_int64, c_int64, u16p]
         L.ora_moe_down_from_h.argtypes = [u16p, c_int64, c_int64, i32p, f32p, c_int64, u8p, f32p, c_int64, c_int64,
                                           u16p, u8p, f32p, f64p, c_int]
+        L.ora_moe_route.argtypes = [f32p, c_int64, c_int64, c_int64, i32p, f32p]
+        L.ora_moe_fold.argtypes = [f64p, i32p, f32p, c_int64, c_int64, c_int64, c_int64, u16p, f32p, u16p]
         _lib = L
     return _lib
 
@@ -242,6 +244,31 @@ def moe_down_from_h(h, ids, w, w2q, w2s, intermediates: bool = False):
                               _p(w2s, c_float), E, I, _p(out, c_uint16), _p(hq, c_uint8), _p(hs, c_float),
                               _p(y, c_double), threads())
     return (out, dict(hq=hq, hs=hs, y=y)) if intermediates else out
+
+
+def moe_route(logits, topk: int):
+    """Routing: logits [T, E] fp32 -> (ids [T, topk] int32, weights [T, topk] fp32); see ora_moe_route."""
+    logits = np.ascontiguousarray(logits, np.float32)
+    T, E = logits.shape
+    ids = np.empty((T, topk), np.int32)
+    w = np.empty((T, topk), np.float32)
+    lib().ora_moe_route(_p(logits, c_float), T, E, topk, _p(ids, c_int32), _p(w, c_float))
+    return ids, w
+
+
+def moe_fold(y, ids, w, E: int, shared=None, shared_w=None):
+    """out [T, H] bf16 bits = the routed sum of y [T*topk, H] plus the shared term; see ora_moe_fold."""
+    ids = np.ascontiguousarray(ids, np.int32)
+    w = np.ascontiguousarray(w, np.float32)
+    T, topk = ids.shape
+    y = np.ascontiguousarray(y, np.float64).reshape(T * topk, -1)
+    H = y.shape[1]
+    s = None if shared is None else _u16(shared)
+    g = None if shared_w is None else np.ascontiguousarray(shared_w, np.float32)
+    out = np.empty((T, H), np.uint16)
+    lib().ora_moe_fold(_p(y, c_double), _p(ids, c_int32), _p(w, c_float), T, topk, H, E,
+                       _p(s, c_uint16), _p(g, c_float), _p(out, c_uint16))
+    return out
 
 
 # ------------------------------------------------------------ comparison ----

@@ -419,3 +419,64 @@ void ora_moe_down_from_h(const uint16_t *h_in, int64_t T, int64_t H, const int32
     moe_run(&c, out, nthreads);
     free(dummy_x);
 }
+
+/* ------------------------------------------------------------------------ */
+/* MoE routing and the routed sum with the shared expert                     */
+/* ------------------------------------------------------------------------ */
+
+/* Routing of T tokens over E experts (release v0.3.0, "What changed for
+ * someone running it": one-launch MoE routing).  Token t's experts are its
+ * topk largest logits, a larger logit first and equal logits in ascending
+ * expert id; the softmax is increasing in the logit, so these are the experts
+ * of the topk largest probabilities.  Their weights are those probabilities
+ * renormalised over the chosen experts, in which the softmax's denominator
+ * cancels:
+ *   w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0),  i, j over the chosen slots,
+ * l_0 the largest logit, in binary64, rounded once to fp32.
+ * Logits must be finite.  ids and w are [T][topk]. */
+void ora_moe_route(const float *logits, int64_t T, int64_t E, int64_t topk, int32_t *ids, float *w) {
+    char *taken = (char *)malloc((size_t)E);
+    double *ex = (double *)malloc(sizeof(double) * (size_t)topk);
+    for (int64_t t = 0; t < T; ++t) {
+        const float *row = logits + t * E;
+        int32_t *id = ids + t * topk;
+        memset(taken, 0, (size_t)E);
+        for (int64_t j = 0; j < topk; ++j) {
+            int64_t best = -1;
+            for (int64_t e = 0; e < E; ++e)  /* strict >: the lower id wins a tie */
+                if (!taken[e] && (best < 0 || row[e] > row[best])) best = e;
+            taken[best] = 1;
+            id[j] = (int32_t)best;
+        }
+        const double l0 = (double)row[id[0]];
+        double sum = 0.0;
+        for (int64_t j = 0; j < topk; ++j) {
+            ex[j] = exp((double)row[id[j]] - l0);
+            sum += ex[j];
+        }
+        for (int64_t j = 0; j < topk; ++j) w[t * topk + j] = (float)(ex[j] / sum);
+    }
+    free(taken);
+    free(ex);
+}
+
+/* The routed sum with the shared expert added (release v0.3.0, same section:
+ * the fused top-k sum with the shared expert):
+ *   out[t][n] = bf16( sum_j w[t][j] * y[t*topk + j][n]  +  g[t] * s[t][n] )
+ * with j ascending over the slots whose id lies in [0, E), binary64, rounded
+ * once; g[t] = shared_w[t], or 1 when shared_w is NULL; the shared term is
+ * absent when s is NULL.  y is [T*topk][H] binary64, s [T][H] bf16. */
+void ora_moe_fold(const double *y, const int32_t *ids, const float *w, int64_t T, int64_t topk, int64_t H,
+                  int64_t E, const uint16_t *s, const float *shared_w, uint16_t *out) {
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t n = 0; n < H; ++n) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < topk; ++j) {
+                const int32_t e = ids[t * topk + j];
+                if (e < 0 || e >= E) continue;
+                acc += (double)w[t * topk + j] * y[(t * topk + j) * H + n];
+            }
+            if (s) acc += (shared_w ? (double)shared_w[t] : 1.0) * (double)ora_bf16_value(s[t * H + n]);
+            out[t * H + n] = ora_bf16_round(acc);
+        }
+}

@@ -27,8 +27,9 @@ class MoeProblem:
     def __init__(self, r9k, ora, T, H, E, I, topk, seed=0):
         import torch
         self.T, self.H, self.E, self.I, self.topk = T, H, E, I, topk
-        x, ids, w, w13, w2 = inputs.moe_inputs(seed, T, H, E, I, topk)
-        self.x, self.ids, self.w = x, ids, w
+        x, logits, w13, w2 = inputs.moe_inputs(seed, T, H, E, I)
+        ids, w = ora.moe_route(logits, topk)
+        self.x, self.logits, self.ids, self.w = x, logits, ids, w
         q13, s13, q2, s2 = [], [], [], []
         for e in range(E):
             a, b = ora.quant_weight(w13[e]); q13.append(a); s13.append(b)

@@ -1,4 +1,4 @@
-"""Pins for the oracle's MoE decode and for the harness routing (CPU only).
+"""Pins for the oracle's MoE decode, routing and routed sum (CPU only).
 
 MoE decode, per (token t, slot j) with expert e = ids[t,j]:
   gu = bf16(block GEMM of quant(x[t]) against w13[e]),  gate = gu[:I], up = gu[I:]
@@ -7,6 +7,10 @@ MoE decode, per (token t, slot j) with expert e = ids[t,j]:
   out[t] = bf16(sum_j w[t,j] * y(t,j)), j ascending.
 silu's exp is the one step these pins cannot reach exactly (binary64 exp): the
 silu value itself is parity unpinned beyond the output tolerance.
+
+Routing: the top-k logits (a larger logit first, ties to the lower id), with
+weights exp(l_j - l_0) / sum_i exp(l_i - l_0) over the chosen slots.  The
+routed sum with the shared expert: out[t] = bf16(sum_j w y + g s).
 """
 import math
 from fractions import Fraction
@@ -19,9 +23,16 @@ from tests import exact
 from tests.test_oracle_gemm import _E4, _bf16_bits_exact
 
 
-def _small(seed, T=2, H=256, E=4, I=128, topk=2):
-    x, ids, w, w13, w2 = inputs.moe_inputs(seed, T, H, E, I, topk)
+def _routed(seed, T, H, E, I, topk):
+    import oracle
+    oracle.build(force=False)
+    x, logits, w13, w2 = inputs.moe_inputs(seed, T, H, E, I)
+    ids, w = oracle.moe_route(logits, topk)
     return x, ids, w, w13, w2
+
+
+def _small(seed, T=2, H=256, E=4, I=128, topk=2):
+    return _routed(seed, T, H, E, I, topk)
 
 
 def _quant_experts(ora, w13, w2):
@@ -97,7 +108,7 @@ def test_moe_bruteforce_exact(ora):
     """H = I = 128, E = 4, top-2, T = 2 with exact rationals everywhere except
     silu's exp (binary64)."""
     T, H, E, I, k = 2, 128, 4, 128, 2
-    x, ids, w, w13, w2 = inputs.moe_inputs(64, T, H, E, I, k)
+    x, ids, w, w13, w2 = _routed(64, T, H, E, I, k)
     q13, s13, q2, s2 = _quant_experts(ora, w13, w2)
     out, inter = ora.moe_decode(x, ids, w, q13, s13, q2, s2, intermediates=True)
     for t in range(T):
@@ -133,17 +144,92 @@ def test_moe_bruteforce_exact(ora):
         assert want == out[t].tolist()
 
 
-def test_route_invariants():
+def test_route_invariants(ora):
     r = np.random.default_rng(5)
     logits = r.standard_normal((64, 128)).astype(np.float32)
-    ids, w = inputs.route(logits, 8)
+    ids, w = ora.moe_route(logits, 8)
     assert ids.shape == (64, 8) and w.dtype == np.float32
     for t in range(64):
         assert len(set(ids[t].tolist())) == 8                     # distinct experts
         assert ids[t, 0] == int(np.argmax(logits[t]))               # the argmax is chosen first
         assert abs(float(np.sum(w[t].astype(np.float64))) - 1.0) <= 8 * 2.0 ** -24
         assert np.all(np.diff(w[t]) <= 0)                           # ordered by probability
+        # the chosen logits are the 8 largest: nothing left out is larger than the smallest chosen
+        rest = np.delete(logits[t], ids[t])
+        assert np.all(rest <= logits[t, ids[t, -1]])
     # ties go to the lower expert id
     tie = np.zeros((1, 16), np.float32)
-    ids_t, w_t = inputs.route(tie, 4)
+    ids_t, w_t = ora.moe_route(tie, 4)
     assert ids_t[0].tolist() == [0, 1, 2, 3] and np.all(w_t == np.float32(0.25))
+    # ties between some experts only: lower ids first among equals, larger logits before them
+    lt = np.array([[0.5, 2.0, 0.5, 2.0, -1.0, 0.5]], np.float32)
+    assert ora.moe_route(lt, 4)[0][0].tolist() == [1, 3, 0, 2]
+
+
+def test_route_worked_example(ora):
+    """Logits (0, ln 3): the weights of a top-2 are 1/4 and 3/4, the larger first."""
+    lt = np.array([[0.0, math.log(3.0), -5.0]], np.float32)
+    ids, w = ora.moe_route(lt, 2)
+    assert ids[0].tolist() == [1, 0]
+    l0, l1 = float(lt[0, 1]), float(lt[0, 0])
+    e = math.exp(l1 - l0)
+    assert w[0].tolist() == [np.float32(1.0 / (1.0 + e)), np.float32(e / (1.0 + e))]
+    assert abs(float(w[0, 0]) - 0.75) < 1e-7 and abs(float(w[0, 1]) - 0.25) < 1e-7
+    # top-1: the single weight is exactly 1
+    ids1, w1 = ora.moe_route(np.random.default_rng(1).standard_normal((9, 33)).astype(np.float32), 1)
+    assert np.all(w1 == np.float32(1.0))
+
+
+def test_route_all_experts_is_the_softmax(ora):
+    """topk = E: the weights are the softmax of the logits, in descending order (scipy's softmax)."""
+    from scipy.special import softmax
+    lt = np.random.default_rng(2).standard_normal((12, 24)).astype(np.float32)
+    ids, w = ora.moe_route(lt, 24)
+    p = softmax(lt.astype(np.float64), axis=1)
+    for t in range(12):
+        assert sorted(ids[t].tolist()) == list(range(24))
+        np.testing.assert_allclose(w[t].astype(np.float64), p[t, ids[t]], rtol=2e-7, atol=0)
+
+
+def test_route_shift_invariance(ora):
+    """Adding a constant to every logit of a token changes neither the experts nor (beyond rounding) the weights."""
+    # logits on a 2^-10 grid below 8 in magnitude, so that adding 0.5 is exact in fp32
+    z = np.random.default_rng(3).standard_normal((20, 64))
+    lt = (np.round(np.clip(z, -7, 7) * 1024) / 1024).astype(np.float32)
+    ids, w = ora.moe_route(lt, 8)
+    ids2, w2 = ora.moe_route(lt + np.float32(0.5), 8)
+    assert np.array_equal(ids, ids2)
+    np.testing.assert_allclose(w2, w, rtol=4e-7, atol=0)
+
+
+def test_fold_reduces_to_the_routed_sum(ora):
+    """No shared expert: the routed sum of ora_moe_decode's own y is its output, bit for bit."""
+    T, H, E, I, k = 3, 256, 4, 128, 2
+    x, ids, w, w13, w2 = _routed(7, T, H, E, I, k)
+    q13, s13, q2, s2 = _quant_experts(ora, w13, w2)
+    out, inter = ora.moe_decode(x, ids, w, q13, s13, q2, s2, intermediates=True)
+    assert np.array_equal(ora.moe_fold(inter["y"], ids, w, E), out)
+
+
+def test_fold_shared_term_closed_forms(ora):
+    """y = 0: out = bf16(g * s); g = 1 by default; an out-of-range id adds nothing."""
+    T, H, k, E = 4, 128, 3, 8
+    r = np.random.default_rng(4)
+    ids = r.integers(0, E, (T, k)).astype(np.int32)
+    w = r.random((T, k)).astype(np.float32)
+    s = inputs.to_bf16_bits(r.standard_normal((T, H)).astype(np.float32))
+    g = r.random(T).astype(np.float32)
+    y0 = np.zeros((T * k, H))
+    sv = ora.bf16_value(s).astype(np.float64)
+    assert np.array_equal(ora.moe_fold(y0, ids, w, E, shared=s), s)
+    want = ora.bf16_round(sv * g[:, None].astype(np.float64))
+    assert np.array_equal(ora.moe_fold(y0, ids, w, E, shared=s, shared_w=g), want)
+    # one slot out of range: the same as its weight set to zero
+    y = r.standard_normal((T * k, H))
+    ids_bad = ids.copy(); ids_bad[1, 2] = E
+    w_zero = w.copy(); w_zero[1, 2] = 0.0
+    assert np.array_equal(ora.moe_fold(y, ids_bad, w, E, shared=s, shared_w=g),
+                          ora.moe_fold(y, ids, w_zero, E, shared=s, shared_w=g))
+    # the routed part plus the shared part, rounded once, against an independent fp64 sum
+    ref = (np.einsum("tj,tjh->th", w.astype(np.float64), y.reshape(T, k, H)) + g[:, None] * sv)
+    assert np.array_equal(ora.moe_fold(y, ids, w, E, shared=s, shared_w=g), ora.bf16_round(ref))
