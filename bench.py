@@ -261,11 +261,9 @@ def bench_mid(torch, r9k, inputs, dev, reps):
 def bench_moe(torch, r9k, inputs, dev, reps):
     T, H, E, I, k = 16, 2048, 128, 768, 8
     x, logits, w13, w2 = inputs.moe_inputs(0, T, H, E, I)
-    # routing (not timed): top-k of the softmax, weights renormalised over the top-k
-    pr = torch.softmax(torch.from_numpy(logits).double(), dim=1)
-    pk, idk = torch.topk(pr, k, dim=1)
-    ids = idk.to(torch.int32).numpy()
-    tw = (pk / pk.sum(dim=1, keepdim=True)).float().numpy()
+    logits_d = torch.from_numpy(logits).cuda()
+    ids_d, tw_d = r9k.moe_route(logits_d, k)  # the library's one-launch routing
+    ids = ids_d.cpu().numpy()
     q13, s13 = r9k.quant_weight(dev(w13.reshape(E * 2 * I, H)))
     q2, s2 = r9k.quant_weight(dev(w2.reshape(E * H, I)))
     del w13, w2
@@ -273,13 +271,21 @@ def bench_moe(torch, r9k, inputs, dev, reps):
     q13 = r9k.pack_weight(q13)
     q2 = r9k.pack_weight(q2)
     sets = [(q13, s13, q2, s2), (q13.clone(), s13.clone(), q2.clone(), s2.clone())]
-    x_d, ids_d, tw_d = dev(x), torch.from_numpy(ids).cuda(), torch.from_numpy(tw).cuda()
+    x_d = dev(x)
+    shared_d = dev(inputs.activations(1, T, H, outliers=False))  # a stand-in for the shared expert's output
     wsp = torch.zeros(r9k.moe_fp8_decode_workspace(T, H, E, I, k), dtype=torch.uint8, device="cuda")
     out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
     touched = len(np.unique(ids))
     per_expert = 2 * I * H + 4 * (2 * I // 128) * (H // 128) + H * I + 4 * (H // 128) * (I // 128)
     nbytes = touched * per_expert + 2 * T * H * 2 + T * k * 8
     res = {}
+    # routing alone: a graph of back-to-back launches
+    rcalls = [lambda: r9k.moe_route(logits_d, k, ids=ids_d, w=tw_d)] * 20
+    g = capture(torch, rcalls)
+    tm = Timer(torch)
+    tm.run(lambda i: g.replay(), 1)
+    res["route"] = dict(us=tm.run(lambda i: g.replay(), reps) / len(rcalls) * 1e3, T=T, E=E, topk=k)
+    log(f"moe route T={T} E={E} top-{k}: {res['route']['us']:.2f} us")
     for fused in (True, False):
         calls = [lambda s=s: r9k.moe_fp8_decode(x_d, ids_d, tw_d, s[0].view(E, 2 * I, H),
                                                 s[1].view(E, 2 * I // 128, H // 128), s[2].view(E, H, I),
@@ -294,6 +300,19 @@ def bench_moe(torch, r9k, inputs, dev, reps):
         gbs = nbytes / (ms * 1e-3) / 1e9
         log(f"moe fused={fused}: {ms * 1e3:.1f} us, {gbs:.0f} GB/s over {touched} touched experts")
         res["fused" if fused else "three_launch"] = dict(us=ms * 1e3, GBs=gbs, hbm_frac=gbs / HBM_PEAK_GBS)
+    # the fused path with the shared expert's term folded into the combine
+    calls = [lambda s=s: r9k.moe_fp8_decode(x_d, ids_d, tw_d, s[0].view(E, 2 * I, H),
+                                            s[1].view(E, 2 * I // 128, H // 128), s[2].view(E, H, I),
+                                            s[3].view(E, H // 128, I // 128), out=out, workspace=wsp,
+                                            fused=True, packed=True, shared=shared_d) for s in sets]
+    for f in calls:
+        f()
+    g = capture(torch, calls)
+    tm = Timer(torch)
+    tm.run(lambda i: g.replay(), 1)
+    ms = tm.run(lambda i: g.replay(), reps) / len(sets)
+    res["fused_shared"] = dict(us=ms * 1e3, GBs=nbytes / (ms * 1e-3) / 1e9)
+    log(f"moe fused with the shared expert's term: {ms * 1e3:.1f} us")
     res.update(workload=f"T={T}, H={H}, E={E}, I={I}, top-{k}", touched_experts=touched, bytes=nbytes)
     return res
 

@@ -20,7 +20,7 @@ from ctypes import POINTER, c_char_p, c_int, c_int64, c_size_t, c_void_p
 
 import torch
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 ENGINE_AUTO, ENGINE_SKINNY, ENGINE_TILED = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
                                          c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_void_p,
                                          c_size_t, c_int, c_void_p]
         L.r9k_moe_fp8_decode_packed.argtypes = L.r9k_moe_fp8_decode.argtypes
+        L.r9k_moe_fp8_decode_ex.argtypes = L.r9k_moe_fp8_decode.argtypes[:15] + [POINTER(MoeOpts), c_void_p]
+        L.r9k_moe_route.argtypes = [c_void_p, c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p]
         v = L.r9k_abi_version()
         if v != ABI_VERSION:
             raise ImportError(f"libr9k.so has ABI version {v}, this binding needs {ABI_VERSION}")
@@ -286,10 +288,29 @@ def moe_ws_offset(T: int, H: int, E: int, I: int, topk: int, which: str) -> int:
     return b.value
 
 
+class MoeOpts(ctypes.Structure):
+    """r9k_moe_opts."""
+    _fields_ = [("fused", c_int), ("packed", c_int), ("shared", c_void_p), ("shared_w", c_void_p)]
+
+
+def moe_route(logits, topk: int, ids=None, w=None, stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """One-launch routing: logits [T,E] fp32 -> (topk ids [T,topk] int32, renormalised weights [T,topk] fp32)."""
+    T, E = logits.shape
+    if ids is None:
+        ids = torch.empty((T, topk), dtype=torch.int32, device=logits.device)
+    if w is None:
+        w = torch.empty((T, topk), dtype=torch.float32, device=logits.device)
+    _check(lib().r9k_moe_route(_ptr(logits, F32, "logits"), T, E, topk, _ptr(ids, I32, "ids"), _ptr(w, F32, "w"),
+                               _stream(stream)), "r9k_moe_route")
+    return ids, w
+
+
 def moe_fp8_decode(x, topk_ids, topk_w, w13, w13_s, w2, w2_s, out=None, workspace=None, fused: bool = True,
-                   stream=None, packed: bool = False) -> torch.Tensor:
+                   stream=None, packed: bool = False, shared=None, shared_w=None) -> torch.Tensor:
     """Routed MoE decode: x [T,H] bf16, ids/weights [T,topk], experts w13 [E,2I,H], w2 [E,H,I] (fp8 +
-    block scales) -> out [T,H] bf16.  packed: w13 and w2 are pack_weight copies (same shapes)."""
+    block scales) -> out [T,H] bf16.  packed: w13 and w2 are pack_weight copies (same shapes).
+    shared [T,H] bf16 (and its per-token weight shared_w [T] fp32): the shared expert's output, added in the
+    combine (r9k_moe_fp8_decode_ex)."""
     T, H = x.shape
     topk = topk_ids.shape[1]
     E, twoI, _ = w13.shape
@@ -298,6 +319,15 @@ def moe_fp8_decode(x, topk_ids, topk_w, w13, w13_s, w2, w2_s, out=None, workspac
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     nbytes = moe_fp8_decode_workspace(T, H, E, I, topk)
     wsb = _workspace(workspace, nbytes)
+    if shared is not None or shared_w is not None:
+        opts = MoeOpts(1 if fused else 0, 1 if packed else 0, _ptr(shared, BF16, "shared"),
+                       _ptr(shared_w, F32, "shared_w"))
+        _check(lib().r9k_moe_fp8_decode_ex(
+            _ptr(x, BF16, "x"), T, H, _ptr(topk_ids, I32, "topk_ids"), _ptr(topk_w, F32, "topk_w"), topk,
+            _ptr(w13, FP8, "w13"), _ptr(w13_s, F32, "w13_s"), _ptr(w2, FP8, "w2"), _ptr(w2_s, F32, "w2_s"), E, I,
+            _ptr(out, BF16, "out"), _ptr(wsb, FP8, "workspace"), wsb.numel(), ctypes.byref(opts), _stream(stream)),
+            "r9k_moe_fp8_decode_ex")
+        return out
     fn = lib().r9k_moe_fp8_decode_packed if packed else lib().r9k_moe_fp8_decode
     _check(fn(_ptr(x, BF16, "x"), T, H, _ptr(topk_ids, I32, "topk_ids"), _ptr(topk_w, F32, "topk_w"), topk,
               _ptr(w13, FP8, "w13"), _ptr(w13_s, F32, "w13_s"), _ptr(w2, FP8, "w2"), _ptr(w2_s, F32, "w2_s"), E, I,

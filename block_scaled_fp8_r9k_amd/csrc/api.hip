@@ -340,20 +340,22 @@ int r9k_moe_ws_offset(int64_t T, int64_t H, int64_t E, int64_t I, int64_t topk, 
 static int run_moe(const uint16_t *x, int64_t T, int64_t H, const int32_t *topk_ids, const float *topk_w,
                    int64_t topk, const uint8_t *w13, const float *w13_s, const uint8_t *w2, const float *w2_s,
                    int64_t E, int64_t I, uint16_t *out, void *workspace, size_t ws_bytes, int fused, void *stream,
-                   bool packed) {
+                   bool packed, const uint16_t *shared, const float *shared_w) {
     if (!x || !topk_ids || !topk_w || !w13 || !w13_s || !w2 || !w2_s || !out || !workspace) return R9K_ERR_NULLPTR;
     if (int rc = check_moe_shape(T, H, E, I, topk)) return rc;
     if (fused != 0 && fused != 1) return R9K_ERR_ARG;
     if (!aligned16(x) || !aligned16(topk_ids) || !aligned16(topk_w) || !aligned16(w13) || !aligned16(w13_s) ||
-        !aligned16(w2) || !aligned16(w2_s) || !aligned16(out) || !aligned16(workspace))
+        !aligned16(w2) || !aligned16(w2_s) || !aligned16(out) || !aligned16(workspace) ||
+        (shared && !aligned16(shared)) || (shared_w && !aligned16(shared_w)))
         return R9K_ERR_ALIGN;
+    if (shared_w && !shared) return R9K_ERR_NULLPTR;  // a weight for a term that is not there
     if (T == 0) return R9K_OK;
     const MoeLayout L = moe_layout(T, H, E, I, topk);
     if (ws_bytes < L.total) return R9K_ERR_WORKSPACE;
     if (int rc = check_device()) return rc;
     uint8_t *b = (uint8_t *)workspace;
     MoeArgs a{x, topk_ids, topk_w, w13, w13_s, w2, w2_s, out, (uint16_t *)(b + L.gu), (uint16_t *)(b + L.h),
-              b + L.hq, (float *)(b + L.hs), (float *)(b + L.y), T, H, E, I, topk, packed};
+              b + L.hq, (float *)(b + L.hs), (float *)(b + L.y), T, H, E, I, topk, packed, shared, shared_w};
     return launch_result(launch_moe_decode(a, fused == 1, (hipStream_t)stream));
 }
 
@@ -362,7 +364,7 @@ int r9k_moe_fp8_decode(const uint16_t *x, int64_t T, int64_t H, const int32_t *t
                        int64_t E, int64_t I, uint16_t *out, void *workspace, size_t ws_bytes, int fused,
                        void *stream) {
     return run_moe(x, T, H, topk_ids, topk_w, topk, w13, w13_s, w2, w2_s, E, I, out, workspace, ws_bytes, fused,
-                   stream, false);
+                   stream, false, nullptr, nullptr);
 }
 
 int r9k_moe_fp8_decode_packed(const uint16_t *x, int64_t T, int64_t H, const int32_t *topk_ids,
@@ -370,7 +372,27 @@ int r9k_moe_fp8_decode_packed(const uint16_t *x, int64_t T, int64_t H, const int
                               const uint8_t *w2p, const float *w2_s, int64_t E, int64_t I, uint16_t *out,
                               void *workspace, size_t ws_bytes, int fused, void *stream) {
     return run_moe(x, T, H, topk_ids, topk_w, topk, w13p, w13_s, w2p, w2_s, E, I, out, workspace, ws_bytes, fused,
-                   stream, true);
+                   stream, true, nullptr, nullptr);
+}
+
+int r9k_moe_fp8_decode_ex(const uint16_t *x, int64_t T, int64_t H, const int32_t *topk_ids, const float *topk_w,
+                          int64_t topk, const uint8_t *w13, const float *w13_s, const uint8_t *w2,
+                          const float *w2_s, int64_t E, int64_t I, uint16_t *out, void *workspace,
+                          size_t ws_bytes, const r9k_moe_opts *opts, void *stream) {
+    if (!opts) return R9K_ERR_NULLPTR;
+    if (opts->packed != 0 && opts->packed != 1) return R9K_ERR_ARG;
+    return run_moe(x, T, H, topk_ids, topk_w, topk, w13, w13_s, w2, w2_s, E, I, out, workspace, ws_bytes,
+                   opts->fused, stream, opts->packed == 1, opts->shared, opts->shared_w);
+}
+
+int r9k_moe_route(const float *logits, int64_t T, int64_t E, int64_t topk, int32_t *topk_ids, float *topk_w,
+                  void *stream) {
+    if (!logits || !topk_ids || !topk_w) return R9K_ERR_NULLPTR;
+    if (T < 0 || T > MAX_DIM || E < 1 || E > 65536 || topk < 1 || topk > E || topk > 64) return R9K_ERR_SHAPE;
+    if (!aligned16(logits) || !aligned16(topk_ids) || !aligned16(topk_w)) return R9K_ERR_ALIGN;
+    if (T == 0) return R9K_OK;
+    if (int rc = check_device()) return rc;
+    return launch_result(launch_moe_route(logits, T, E, (int)topk, topk_ids, topk_w, (hipStream_t)stream));
 }
 
 }  // extern "C"

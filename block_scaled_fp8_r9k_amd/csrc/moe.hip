@@ -295,7 +295,126 @@ __global__ __launch_bounds__(256) void k_moe_combine(MoeArgs p) {
                 for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(w[jj], y[jj][i], acc[i]);
             }
     }
+    if (p.shared) {  // the shared expert's term, g * s, added before the one rounding
+        const float g = p.shared_w ? p.shared_w[t] : 1.0f;
+        const uint2 sv = *(const uint2 *)(p.shared + t * H + n);
+        acc[0] = __builtin_fmaf(g, bf16_lo(sv.x), acc[0]);
+        acc[1] = __builtin_fmaf(g, bf16_hi(sv.x), acc[1]);
+        acc[2] = __builtin_fmaf(g, bf16_lo(sv.y), acc[2]);
+        acc[3] = __builtin_fmaf(g, bf16_hi(sv.y), acc[3]);
+    }
     *(uint2 *)(p.out + t * H + n) = bf16x4_rne(acc[0], acc[1], acc[2], acc[3]);
+}
+
+// MoE routing in one launch (release v0.3.0, "What changed for someone running
+// it": one-launch MoE routing), one wave per token.  The experts are the topk
+// largest logits, a larger logit first and equal logits in ascending expert id
+// (the softmax is increasing, so these are the topk largest probabilities).
+// Round j takes the first expert, in that order, among those after round
+// j - 1's choice, so nothing needs marking: each lane scans its strided share
+// of the logits (the first 8 per lane held in registers), then the wave keeps
+// the first of the 64 candidates.  Lane j keeps choice j (topk <= 64).  The
+// weights are the probabilities renormalised over the chosen experts, in
+// which the softmax's denominator cancels: w_j = exp(l_j - l_0) / sum_i
+// exp(l_i - l_0), in fp32.
+namespace {
+constexpr int ROUTE_RV = 8;  // logits a lane holds in registers (E <= 512 needs no reload)
+
+// (v, e) comes first: the larger logit, or the lower id among equal ones
+__device__ __forceinline__ bool route_first(float v, int e, float bv, int be) {
+    return v > bv || (v == bv && e < be);
+}
+__device__ __forceinline__ void route_keep(float v, int e, float &bv, int &be) {
+    if (route_first(v, e, bv, be)) {
+        bv = v;
+        be = e;
+    }
+}
+// One DPP step of the wave reduction: the partner lane's candidate, kept if it comes first.
+template <int CTRL>
+__device__ __forceinline__ void route_dpp(float &bv, int &be) {
+    const float ov = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(bv), CTRL, 0xF, 0xF, false));
+    const int oe = __builtin_amdgcn_mov_dpp(be, CTRL, 0xF, 0xF, false);
+    route_keep(ov, oe, bv, be);
+}
+template <int CTRL>
+__device__ __forceinline__ float sum_dpp(float x) {
+    return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror: after
+// these every lane of a 16-lane row holds the row's result
+constexpr int DPP_Q1 = 0xB1, DPP_Q2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+}  // namespace
+
+__global__ __launch_bounds__(256) void k_moe_route(const float *__restrict__ logits, int64_t T, int64_t E, int topk,
+                                                   int32_t *__restrict__ ids, float *__restrict__ w) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;  // uniform across the wave
+    const float *row = logits + t * E;
+    float lv[ROUTE_RV];
+#pragma unroll
+    for (int r = 0; r < ROUTE_RV; ++r) {
+        const int64_t e = lane + 64 * r;
+        lv[r] = e < E ? row[e] : 0.0f;
+    }
+    float pv = __builtin_inff();  // the previous choice; every expert comes after (+inf, -1)
+    int pe = -1;
+    float my_v = 0.0f;
+    int my_e = 0;
+    for (int j = 0; j < topk; ++j) {
+        float bv = -__builtin_inff();
+        int be = 0x7fffffff;
+        auto consider = [&](float v, int e) {
+            if ((v < pv || (v == pv && e > pe)) && route_first(v, e, bv, be)) {
+                bv = v;
+                be = e;
+            }
+        };
+#pragma unroll
+        for (int r = 0; r < ROUTE_RV; ++r)
+            if (lane + 64 * r < E) consider(lv[r], lane + 64 * r);
+        for (int64_t e = lane + 64 * ROUTE_RV; e < E; e += 64) consider(row[e], (int)e);
+        route_dpp<DPP_Q1>(bv, be);
+        route_dpp<DPP_Q2>(bv, be);
+        route_dpp<DPP_HALF_MIRROR>(bv, be);
+        route_dpp<DPP_MIRROR>(bv, be);
+        float cv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 0));
+        int ce = __builtin_amdgcn_readlane(be, 0);
+#pragma unroll
+        for (int rr = 16; rr < 64; rr += 16)
+            route_keep(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), rr)),
+                       __builtin_amdgcn_readlane(be, rr), cv, ce);
+        pv = cv;
+        pe = ce;
+        if (lane == j) {
+            my_v = cv;
+            my_e = ce;
+        }
+    }
+    const float l0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), 0));
+    const float ex = lane < topk ? expf(my_v - l0) : 0.0f;
+    // the sum over the chosen slots: the same value in every lane of a row,
+    // then the four rows added in a fixed order
+    float rs = sum_dpp<DPP_Q1>(ex);
+    rs = sum_dpp<DPP_Q2>(rs);
+    rs = sum_dpp<DPP_HALF_MIRROR>(rs);
+    rs = sum_dpp<DPP_MIRROR>(rs);
+    const float s01 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rs), 0)) +
+                      __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rs), 16));
+    const float s23 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rs), 32)) +
+                      __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rs), 48));
+    const float sum = s01 + s23;
+    if (lane < topk) {
+        ids[t * topk + lane] = my_e;
+        w[t * topk + lane] = ex / sum;
+    }
+}
+
+hipError_t launch_moe_route(const float *logits, int64_t T, int64_t E, int topk, int32_t *ids, float *w,
+                            hipStream_t s) {
+    hipLaunchKernelGGL(k_moe_route, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, logits, T, E, topk, ids, w);
+    return hipGetLastError();
 }
 
 MoeLayout moe_layout(int64_t T, int64_t H, int64_t E, int64_t I, int64_t topk) {

@@ -120,12 +120,16 @@ struct MoeArgs {
     float *y;       // [P][H] fp32
     int64_t T, H, E, I, topk;
     bool packed;    // w13 and w2 in fragment order
+    const uint16_t *shared;  // NULL, or the shared expert's output [T][H] bf16, added in the combine
+    const float *shared_w;   // NULL (weight 1), or the shared term's weight per token [T]
 };
 struct MoeLayout {
     size_t gu, h, hq, hs, y, total;
 };
 MoeLayout moe_layout(int64_t T, int64_t H, int64_t E, int64_t I, int64_t topk);
 hipError_t launch_moe_decode(const MoeArgs &args, bool fused, hipStream_t s);
+hipError_t launch_moe_route(const float *logits, int64_t T, int64_t E, int topk, int32_t *ids, float *w,
+                            hipStream_t s);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

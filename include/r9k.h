@@ -60,7 +60,7 @@ extern "C" {
 #pragma GCC visibility push(default)
 #endif
 
-#define R9K_ABI_VERSION 3
+#define R9K_ABI_VERSION 4
 
 /* Return codes. */
 #define R9K_OK 0
@@ -72,7 +72,8 @@ extern "C" {
 #define R9K_ERR_WORKSPACE (-6) /* the workspace is smaller than the query returned */
 #define R9K_ERR_ARG (-7)       /* an enumerated argument has an unknown value */
 
-/* The ABI version this library implements (R9K_ABI_VERSION).  Callers refuse
+/* The ABI version this library implements (R9K_ABI_VERSION; 4 added the MoE
+ * routing and the shared-expert fold).  Callers refuse
  * a library whose version differs from the header they were built against,
  * the convention of the pages' plugin, which refuses an older library. */
 int r9k_abi_version(void);
@@ -238,6 +239,44 @@ int r9k_moe_fp8_decode_packed(const uint16_t *x, int64_t T, int64_t H, const int
                               const float *topk_w, int64_t topk, const uint8_t *w13p, const float *w13_s,
                               const uint8_t *w2p, const float *w2_s, int64_t E, int64_t I, uint16_t *out,
                               void *workspace, size_t ws_bytes, int fused, void *stream);
+
+/* Options of r9k_moe_fp8_decode_ex. */
+typedef struct r9k_moe_opts {
+    int fused;                /* 1: the fused path, 0: the three-launch path (as for r9k_moe_fp8_decode) */
+    int packed;               /* 1: w13 and w2 in fragment order (as for r9k_moe_fp8_decode_packed), 0: row-major */
+    const uint16_t *shared;   /* NULL, or the shared expert's output s [T][H] bf16 (device) */
+    const float *shared_w;    /* NULL (weight 1), or its weight g [T] fp32 (device); needs shared */
+} r9k_moe_opts;
+
+/* r9k_moe_fp8_decode with the shared expert folded into the combine: the
+ * fused top-k sum with the shared expert (release v0.3.0, "What changed for
+ * someone running it").  With opts->shared set,
+ *   out[t][n] = bf16( sum_j topk_w[t][j] * y(t,j)[n]  +  g[t] * s[t][n] ),
+ * j ascending in fp32, the shared term added last, one rounding; g[t] =
+ * shared_w[t], or 1 when shared_w is NULL.  Without it, the same result bits
+ * as r9k_moe_fp8_decode (opts->packed = 0) or r9k_moe_fp8_decode_packed (1).
+ * The caller computes s (e.g. with r9k_gemm_fp8_block_qa) and g.
+ * Errors: as r9k_moe_fp8_decode; NULLPTR also for opts, or for shared_w
+ * without shared; ALIGN also for shared and shared_w; ARG for a fused or
+ * packed flag other than 0 or 1. */
+int r9k_moe_fp8_decode_ex(const uint16_t *x, int64_t T, int64_t H, const int32_t *topk_ids, const float *topk_w,
+                          int64_t topk, const uint8_t *w13, const float *w13_s, const uint8_t *w2,
+                          const float *w2_s, int64_t E, int64_t I, uint16_t *out, void *workspace,
+                          size_t ws_bytes, const r9k_moe_opts *opts, void *stream);
+
+/* MoE routing in one launch (release v0.3.0, "What changed for someone running
+ * it": one-launch MoE routing).  For each token t, the topk experts with the
+ * largest logits[t][e], a larger logit first and equal logits in ascending e
+ * (the softmax is increasing, so these are the topk largest probabilities);
+ * their weights are the softmax probabilities renormalised over the chosen
+ * experts, w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0) with l_0 the largest
+ * logit, in fp32 with HIP's expf.  The output feeds r9k_moe_fp8_decode.
+ *   logits [T][E] fp32 (finite) -> topk_ids [T][topk] int32, topk_w [T][topk] fp32.
+ * One wave per token, no workspace.
+ * Errors: NULLPTR; SHAPE if T < 0, E < 1, E > 65536, topk < 1, topk > E or
+ * topk > 64; ALIGN; DEVICE; LAUNCH.  T = 0 launches nothing. */
+int r9k_moe_route(const float *logits, int64_t T, int64_t E, int64_t topk, int32_t *topk_ids, float *topk_w,
+                  void *stream);
 
 /* Byte offset inside the MoE workspace of an intermediate (for tests):
  * which = 0 gu [P][2I] bf16, 1 h [P][I] bf16, 2 y [P][H] fp32, 3 hq [P][I] fp8,

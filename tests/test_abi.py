@@ -144,6 +144,35 @@ def test_moe_checks(L):
     assert f(*bad, 1, S) == 0                                           # T == 0
 
 
+def test_moe_route_and_ex_checks(L):
+    import block_scaled_fp8_r9k_amd as r9k
+    f = L.r9k_moe_route
+    assert f(NUL, 16, 128, 8, B16, C16, S) == -1
+    assert f(A16, 16, 128, 8, NUL, C16, S) == -1
+    assert f(A16, 16, 128, 0, B16, C16, S) == -2                        # topk < 1
+    assert f(A16, 16, 8, 9, B16, C16, S) == -2                          # topk > E
+    assert f(A16, 16, 128, 65, B16, C16, S) == -2                       # topk > 64
+    assert f(A16, 16, 0, 1, B16, C16, S) == -2                          # E < 1
+    assert f(A16, -1, 128, 8, B16, C16, S) == -2
+    assert f(ODD, 16, 128, 8, B16, C16, S) == -3
+    assert f(A16, 0, 128, 8, B16, C16, S) == 0                          # T == 0: nothing to do
+    big = 1 << 32
+    args = [A16, 16, 2048, B16, C16, 8, A16, B16, C16, A16, 128, 768, B16, C16, big]
+    g = L.r9k_moe_fp8_decode_ex
+    assert g(*args, None, S) == -1                                      # no options
+    o = r9k.MoeOpts(2, 0, None, None)
+    assert g(*args, ctypes.byref(o), S) == -7                           # fused must be 0 or 1
+    o = r9k.MoeOpts(1, 2, None, None)
+    assert g(*args, ctypes.byref(o), S) == -7                           # packed must be 0 or 1
+    o = r9k.MoeOpts(1, 0, None, 0x40000)
+    assert g(*args, ctypes.byref(o), S) == -1                           # a weight without the shared term
+    o = r9k.MoeOpts(1, 0, 0x40008, None)
+    assert g(*args, ctypes.byref(o), S) == -3                           # misaligned shared output
+    o = r9k.MoeOpts(1, 1, 0x40000, 0x50000)
+    bad = list(args); bad[1] = 0
+    assert g(*bad, ctypes.byref(o), S) == 0                             # T == 0
+
+
 def _gpu_present():
     try:
         import torch

@@ -162,3 +162,74 @@ def test_moe_out_of_range_id_contributes_nothing(r9k, ora):
     ysum = np.einsum("tj,tjh->th", w0.astype(np.float64), y)
     got = p.run(r9k, True, ids_d=dev(ids))
     assert_close(ora, got, ysum, "moe with invalid ids")
+
+
+def _logits(kind, T, E, seed):
+    r = np.random.default_rng(seed)
+    z = r.standard_normal((T, E))
+    if kind == "ties":        # multiples of 0.5: many equal logits
+        z = np.round(z * 2) / 2
+    elif kind == "spread":    # differences far past fp32 exp's range
+        z = z * 40
+    elif kind == "const":
+        z = np.zeros((T, E))
+    return z.astype(np.float32)
+
+
+@pytest.mark.parametrize("T,E,topk", [(16, 128, 8), (1, 8, 8), (5, 64, 1), (300, 256, 8), (7, 1000, 16),
+                                      (3, 64, 64), (33, 65, 5)])
+@pytest.mark.parametrize("kind", ["normal", "ties", "spread", "const"])
+def test_moe_route(r9k, ora, T, E, topk, kind):
+    """One-launch routing against the oracle: ids bit for bit (ties to the lower id), weights to fp32
+    rounding of exp and the renormalisation."""
+    import torch
+    say("route", T, E, topk, kind)
+    lt = _logits(kind, T, E, seed=T * 1000 + E + topk)
+    ids_o, w_o = ora.moe_route(lt, topk)
+    ids_d, w_d = r9k.moe_route(torch.from_numpy(lt).cuda(), topk)
+    ids_g, w_g = host(ids_d), host(w_d)
+    assert_bits_equal(ids_g, ids_o, f"route ids {kind}")
+    err = np.abs(w_g.astype(np.float64) - w_o.astype(np.float64))
+    assert np.all(err <= 4e-6 * np.abs(w_o.astype(np.float64)) + 1e-37), f"route weights {kind}: {err.max()}"
+    ids2, w2 = r9k.moe_route(torch.from_numpy(lt).cuda(), topk)
+    assert_bits_equal(host(ids2), ids_g, "route repeat ids")
+    assert_bits_equal(host(w2), w_g, "route repeat weights")
+
+
+@pytest.mark.parametrize("shape", [(16, 2048, 128, 768, 8), (4, 256, 4, 128, 2)])
+def test_moe_shared_fold(r9k, ora, shape):
+    """The routed sum with the shared expert's term in the combine: against the oracle's sum of the GPU's
+    own y; the fused and three-launch paths and both weight layouts give the same bits."""
+    import torch
+    T, H, E, I, k = shape
+    say("moe shared fold", shape)
+    p = MoeProblem(r9k, ora, T, H, E, I, k, seed=5)
+    r = np.random.default_rng(6)
+    s = inputs.to_bf16_bits(r.standard_normal((T, H)).astype(np.float32))
+    g = r.random(T).astype(np.float32)
+    s_d, g_d = dev(s), torch.from_numpy(g).cuda()
+    args = (p.x_d, p.ids_d, p.w_d, p.w13q, p.w13s, p.w2q, p.w2s)
+    out = host(r9k.moe_fp8_decode(*args, workspace=p.ws, fused=True, shared=s_d, shared_w=g_d))
+    y = p.ws_view(r9k, "y", torch.float32, (T * k, H)).astype(np.float64)
+    want = ora.moe_fold(y, p.ids, p.w, E, shared=s, shared_w=g)
+    o = ora.bf16_value(want).astype(np.float64)
+    mag = np.einsum("tj,tjh->th", np.abs(p.w.astype(np.float64)), np.abs(y).reshape(T, k, H)) \
+        + np.abs(g[:, None] * ora.bf16_value(s).astype(np.float64))
+    bound = ora.bf16_ulp(o) + 2.0 ** -20 * mag
+    assert np.all(np.abs(ora.bf16_value(out).astype(np.float64) - o) <= bound), "shared fold"
+    unf = host(r9k.moe_fp8_decode(*args, workspace=p.ws, fused=False, shared=s_d, shared_w=g_d))
+    assert_bits_equal(unf, out, "shared fold: three-launch vs fused")
+    w13p = r9k.pack_weight(p.w13q.reshape(E * 2 * I, H)).view(E, 2 * I, H)
+    w2p = r9k.pack_weight(p.w2q.reshape(E * H, I)).view(E, H, I)
+    pk = host(r9k.moe_fp8_decode(p.x_d, p.ids_d, p.w_d, w13p, p.w13s, w2p, p.w2s, workspace=p.ws, fused=True,
+                                 packed=True, shared=s_d, shared_w=g_d))
+    assert_bits_equal(pk, out, "shared fold: packed vs row-major")
+    # no weight means weight 1
+    one = host(r9k.moe_fp8_decode(*args, workspace=p.ws, fused=True, shared=s_d))
+    ones = host(r9k.moe_fp8_decode(*args, workspace=p.ws, fused=True, shared=s_d,
+                                   shared_w=torch.ones(T, dtype=torch.float32, device="cuda")))
+    assert_bits_equal(one, ones, "shared fold: default weight 1")
+    # a zero shared term leaves the routed sum's value
+    plain = host(r9k.moe_fp8_decode(*args, workspace=p.ws, fused=True))
+    zero = host(r9k.moe_fp8_decode(*args, workspace=p.ws, fused=True, shared=torch.zeros_like(s_d)))
+    assert np.array_equal(ora.bf16_value(zero), ora.bf16_value(plain)), "shared fold: zero term"
