@@ -72,6 +72,7 @@ def lib():
         L.ora_moe_down_from_h.argtypes = [u16p, c_int64, c_int64, i32p, f32p, c_int64, u8p, f32p, c_int64, c_int64,
                                           u16p, u8p, f32p, f64p, c_int]
         L.ora_moe_route.argtypes = [f32p, c_int64, c_int64, c_int64, i32p, f32p]
+        L.ora_gemm_block_bf16a.argtypes = [u16p, c_int64, c_int64, u8p, f32p, c_int64, u16p, f64p, c_int]
         L.ora_moe_fold.argtypes = [f64p, i32p, f32p, c_int64, c_int64, c_int64, c_int64, u16p, f32p, u16p]
         _lib = L
     return _lib
@@ -185,6 +186,21 @@ def gemm_block_qa(a_bf16, wq, ws, want_f64: bool = False):
     """The fused form: activation quant then the block GEMM (one definition for every M)."""
     aq, as_ = quant_act(a_bf16)
     return gemm_block(aq, as_, wq, ws, want_f64)
+
+
+def gemm_block_bf16a(a_bf16, wq, ws, want_f64: bool = False):
+    """The bf16-activation variant: C = bf16(sum_g ws * sum_k a * dec(w)), no activation quant; see
+    ora_gemm_block_bf16a."""
+    a = _u16(a_bf16)
+    wq = np.ascontiguousarray(wq, np.uint8)
+    ws = np.ascontiguousarray(ws, np.float32)
+    M, K = a.shape
+    N = wq.shape[0]
+    c = np.empty((M, N), np.uint16)
+    c64 = np.empty((M, N), np.float64) if want_f64 else None
+    lib().ora_gemm_block_bf16a(_p(a, c_uint16), M, K, _p(wq, c_uint8), _p(ws, c_float), N, _p(c, c_uint16),
+                               _p(c64, c_double), threads())
+    return (c, c64) if want_f64 else c
 
 
 # ------------------------------------------------------------------- moe ----

@@ -480,3 +480,47 @@ void ora_moe_fold(const double *y, const int32_t *ids, const float *w, int64_t T
             out[t * H + n] = ora_bf16_round(acc);
         }
 }
+
+/* ------------------------------------------------------------------------ */
+/* The bf16-activation variant: fp8 block weights against unquantised bf16    */
+/* activations                                                                */
+/* ------------------------------------------------------------------------ */
+
+/* Release v0.3.1, "What changed for someone running it": the decode GEMMs of
+ * fp8 weights run against the unquantised bf16 activations.  With the weight
+ * block scales applied per 128-K group, as in the block GEMM:
+ *   C[m][n] = bf16( sum_g ws[n/128][g] * sum_{k in g} a[m][k] * dec(wq[n][k]) )
+ * in binary64 (k and g ascending), rounded once.  A bf16 x e4m3 product is
+ * exact in binary64; the sums are not exact in general (bf16 exponents span
+ * more than binary64's precision), their error is of binary64's rounding. */
+struct gemm_bf16a_ctx {
+    const uint16_t *a; int64_t M, K;
+    const uint8_t *wq; const float *ws; int64_t N;
+    uint16_t *c; double *c64;
+};
+static void gemm_bf16a_range(int64_t lo, int64_t hi, void *p) {
+    struct gemm_bf16a_ctx *c = (struct gemm_bf16a_ctx *)p;
+    const double *T = e4m3_table();
+    const int64_t K = c->K, G = K / 128;
+    for (int64_t idx = lo; idx < hi; ++idx) {
+        const int64_t m = idx / c->N, n = idx % c->N;
+        const uint16_t *arow = c->a + m * K;
+        const uint8_t *wrow = c->wq + n * K;
+        const float *wsrow = c->ws + (n / 128) * G;
+        double acc = 0.0;
+        for (int64_t g = 0; g < G; ++g) {
+            double P = 0.0;
+            for (int k = 0; k < 128; ++k) P += (double)ora_bf16_value(arow[128 * g + k]) * T[wrow[128 * g + k]];
+            acc += P * (double)wsrow[g];
+        }
+        if (c->c64) c->c64[idx] = acc;
+        if (c->c) c->c[idx] = ora_bf16_round(acc);
+    }
+}
+/* a [M][K] bf16, wq [N][K], ws [N/128][K/128] -> c [M][N] bf16 and (if c64 is
+ * not NULL) the unrounded binary64 values. */
+void ora_gemm_block_bf16a(const uint16_t *a, int64_t M, int64_t K, const uint8_t *wq, const float *ws, int64_t N,
+                          uint16_t *c, double *c64, int nthreads) {
+    struct gemm_bf16a_ctx ctx = {a, M, K, wq, ws, N, c, c64};
+    parallel_for(M * N, nthreads, gemm_bf16a_range, &ctx);
+}
