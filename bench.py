@@ -21,9 +21,11 @@ The same line carries:
   prefill       M=4096, K=4096, N=12288: fp8 TFLOP/s vs 5.03 PFLOP/s dense;
   mid           M in {32,64,128,255} at (K,N) = (4096,4096) and (14336,4096);
   moe           16 tokens, hidden 2048, 128 experts of 768, top-8: GB/s over
-                the bytes of the experts the routing touches.
+                the bytes of the experts the routing touches, plus the
+                routing kernel and the fused path with a shared expert;
+  bf16a         the decode sweep on the bf16-activation variant (no quant).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only decode,prefill,mid,moe]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only decode,prefill,mid,moe,bf16a]
                        [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -186,6 +188,33 @@ def bench_decode(torch, r9k, inputs, dev, steps, warmup, packed=True):
                 bytes_avg=bytes_avg, a_bits=a_bits, w_bits=w_bits)
 
 
+def bench_bf16a(torch, r9k, inputs, dev, reps):
+    """The bf16-activation variant over the decode sweep (fragment-order weights, rotated as for the
+    headline): per-launch time and GB/s of the same algorithmic bytes."""
+    K, N = DECODE_K, DECODE_N
+    a = dev(inputs.activations(0, max(DECODE_M), K, outliers=True))
+    copies = weight_copies(torch, r9k, dev, inputs.weights(0, N, K))
+    copies = [(r9k.pack_weight(wq), ws) for wq, ws in copies]
+    C = len(copies)
+    res = {}
+    for M in DECODE_M:
+        a_m = a[:M].contiguous()
+        c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        calls = [lambda w=w, s=s: r9k.gemm_fp8_block_bf16a(a_m, w, s, c=c, packed=True) for w, s in copies] * 2
+        for f in calls:
+            f()
+        g = capture(torch, calls)
+        tm = Timer(torch)
+        tm.run(lambda i: g.replay(), 2)
+        ms = tm.run(lambda i: g.replay(), reps) / len(calls)
+        res[str(M)] = dict(us=ms * 1e3, GBs=gemm_bytes(M, K, N) / (ms * 1e-3) / 1e9)
+        log(f"bf16a M={M}: {ms * 1e3:.2f} us/launch, {res[str(M)]['GBs']:.0f} GB/s")
+    del copies
+    torch.cuda.empty_cache()
+    return dict(workload=f"M in {list(DECODE_M)}, K={K}, N={N}, bf16 activations (no quant), fragment-order "
+                         f"weights", per_m=res)
+
+
 def cpu_baseline(ora, a_bits, w_bits, step_bytes):
     """The oracle (exact fp64 group sums, one bf16 rounding) on one full step:
     activation quant + GEMM for every M of the sweep; weight quant is setup."""
@@ -334,7 +363,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--only", default="decode,prefill,mid,moe")
+    ap.add_argument("--only", default="decode,prefill,mid,moe,bf16a")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -387,6 +416,8 @@ def main():
         line["mid"] = bench_mid(torch, r9k, inputs, dev, reps)
     if "moe" in which:
         line["moe"] = bench_moe(torch, r9k, inputs, dev, reps)
+    if "bf16a" in which:
+        line["bf16a"] = bench_bf16a(torch, r9k, inputs, dev, reps)
     line["copy_GBs_context"] = copy_bandwidth(torch)
     line["kernel_source_hash"] = kernel_source_hash()
     print(json.dumps(line), flush=True)

@@ -20,7 +20,7 @@ from ctypes import POINTER, c_char_p, c_int, c_int64, c_size_t, c_void_p
 
 import torch
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 ENGINE_AUTO, ENGINE_SKINNY, ENGINE_TILED = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -67,6 +67,9 @@ def lib() -> ctypes.CDLL:
         L.r9k_moe_fp8_decode_packed.argtypes = L.r9k_moe_fp8_decode.argtypes
         L.r9k_moe_fp8_decode_ex.argtypes = L.r9k_moe_fp8_decode.argtypes[:15] + [POINTER(MoeOpts), c_void_p]
         L.r9k_moe_route.argtypes = [c_void_p, c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p]
+        L.r9k_gemm_fp8_block_bf16a.argtypes = [c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_int64, c_void_p,
+                                               c_void_p]
+        L.r9k_gemm_fp8_block_bf16a_packed.argtypes = L.r9k_gemm_fp8_block_bf16a.argtypes
         v = L.r9k_abi_version()
         if v != ABI_VERSION:
             raise ImportError(f"libr9k.so has ABI version {v}, this binding needs {ABI_VERSION}")
@@ -209,6 +212,19 @@ def gemm_fp8_block_qa(a, w, ws, c=None, workspace=None, stream=None) -> torch.Te
     _check(lib().r9k_gemm_fp8_block_qa(_ptr(a, BF16, "a"), M, K, _ptr(w, FP8, "w"), _ptr(ws, F32, "ws"), N,
                                        _ptr(c, BF16, "c"), _ptr(wsb, FP8, "workspace"), wsb.numel(),
                                        _stream(stream)), "r9k_gemm_fp8_block_qa")
+    return c
+
+
+def gemm_fp8_block_bf16a(a, w, ws, c=None, stream=None, packed: bool = False) -> torch.Tensor:
+    """The bf16-activation variant at decode widths (M <= 16): a [M,K] bf16 (not quantised), w [N,K] fp8 codes
+    (or their pack_weight copy when packed), ws [N/128,K/128] -> C [M,N] bf16."""
+    M, K = a.shape
+    N = w.shape[0]
+    if c is None:
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    fn = lib().r9k_gemm_fp8_block_bf16a_packed if packed else lib().r9k_gemm_fp8_block_bf16a
+    _check(fn(_ptr(a, BF16, "a"), M, K, _ptr(w, FP8, "w"), _ptr(ws, F32, "ws"), N, _ptr(c, BF16, "c"),
+              _stream(stream)), "r9k_gemm_fp8_block_bf16a_packed" if packed else "r9k_gemm_fp8_block_bf16a")
     return c
 
 

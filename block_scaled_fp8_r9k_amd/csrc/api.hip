@@ -265,6 +265,29 @@ int r9k_gemm_fp8_block_qa_packed(const uint16_t *a, int64_t M, int64_t K, const 
     return run_gemm(a, nullptr, nullptr, M, K, wp, ws, N, c, workspace, ws_bytes, (hipStream_t)stream, true);
 }
 
+static int run_bf16a(const uint16_t *a, int64_t M, int64_t K, const uint8_t *w, const float *ws, int64_t N,
+                     uint16_t *c, void *stream, bool packed) {
+    if (!a || !w || !ws || !c) return R9K_ERR_NULLPTR;
+    if (int rc = check_gemm_shape(M, K, N)) return rc;
+    if (M > 16) return R9K_ERR_SHAPE;
+    if (!aligned16(a) || !aligned16(w) || !aligned16(ws) || !aligned16(c)) return R9K_ERR_ALIGN;
+    if (M == 0) return R9K_OK;
+    const Bf16aCfg cfg = bf16a_config(M, K, N);
+    if (!cfg.wn) return R9K_ERR_SHAPE;
+    if (int rc = check_device()) return rc;
+    return launch_result(launch_gemm_bf16a(Bf16aArgs{a, w, ws, c, M, K, N, packed}, cfg, (hipStream_t)stream));
+}
+
+int r9k_gemm_fp8_block_bf16a(const uint16_t *a, int64_t M, int64_t K, const uint8_t *w, const float *ws, int64_t N,
+                             uint16_t *c, void *stream) {
+    return run_bf16a(a, M, K, w, ws, N, c, stream, false);
+}
+
+int r9k_gemm_fp8_block_bf16a_packed(const uint16_t *a, int64_t M, int64_t K, const uint8_t *wp, const float *ws,
+                                    int64_t N, uint16_t *c, void *stream) {
+    return run_bf16a(a, M, K, wp, ws, N, c, stream, true);
+}
+
 int r9k_pack_weight(const uint8_t *wq, int64_t N, int64_t K, uint8_t *wp, void *stream) {
     if (!wq || !wp) return R9K_ERR_NULLPTR;
     if (N <= 0 || K <= 0 || N % 128 || K % 128 || N > MAX_DIM || K > MAX_DIM) return R9K_ERR_SHAPE;

@@ -103,6 +103,23 @@ size_t tiled_partial_bytes(const TiledPlan &t, int64_t M, int64_t N);
 hipError_t launch_gemm_tiled(const TiledArgs &args, const TiledPlan &plan, hipStream_t s);
 hipError_t launch_splitk_reduce(const float *part, uint16_t *c, int64_t M, int64_t N, int ksplit, hipStream_t s);
 
+// ---- bf16-activation variant at decode widths (gemm_bf16a.hip) ----
+struct Bf16aArgs {
+    const uint16_t *a;  // [M][K] bf16
+    const uint8_t *w;   // [N][K] codes, or their fragment-order copy
+    const float *ws;    // [N/128][K/128]
+    uint16_t *c;        // [M][N] bf16
+    int64_t M, K, N;
+    bool packed;
+};
+struct Bf16aCfg {
+    int wn;  // 16-column tiles per CTA (0: the shape does not fit)
+    int wk;  // K slices per tile (waves per CTA = wn * wk)
+    int gs;  // K-groups per wave
+};
+Bf16aCfg bf16a_config(int64_t M, int64_t K, int64_t N);
+hipError_t launch_gemm_bf16a(const Bf16aArgs &args, const Bf16aCfg &cfg, hipStream_t s);
+
 // ---- MoE decode (moe.hip) ----
 struct MoeArgs {
     const uint16_t *x;

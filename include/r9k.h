@@ -60,7 +60,7 @@ extern "C" {
 #pragma GCC visibility push(default)
 #endif
 
-#define R9K_ABI_VERSION 4
+#define R9K_ABI_VERSION 5
 
 /* Return codes. */
 #define R9K_OK 0
@@ -73,7 +73,7 @@ extern "C" {
 #define R9K_ERR_ARG (-7)       /* an enumerated argument has an unknown value */
 
 /* The ABI version this library implements (R9K_ABI_VERSION; 4 added the MoE
- * routing and the shared-expert fold).  Callers refuse
+ * routing and the shared-expert fold, 5 the bf16-activation variant).  Callers refuse
  * a library whose version differs from the header they were built against,
  * the convention of the pages' plugin, which refuses an older library. */
 int r9k_abi_version(void);
@@ -178,6 +178,27 @@ int r9k_gemm_fp8_block_qa_packed(const uint16_t *a, int64_t M, int64_t K, const 
 #define R9K_ENGINE_TILED 2
 int r9k_set_dispatch(int skinny_max_m, int engine);
 int r9k_get_dispatch(int *skinny_max_m, int *engine);
+
+/* The bf16-activation variant at decode widths (release v0.3.1, "What changed
+ * for someone running it": the decode GEMMs of fp8 weights run as bf16
+ * matrix products against the unquantised activations), with the weight block
+ * scales applied per 128-K group:
+ *   C[m][n] = bf16( sum_g ws[n/128][g] * sum_{k in g} a[m][k] * dec(w[n][k]) ),
+ * fp32 accumulation.  No activation quant: a [M][K] bf16 is used as given.
+ * w [N][K] codes (row-major) and ws [N/128][K/128] as for r9k_gemm_fp8_block.
+ * No workspace; every CTA covers all of K.
+ * Errors: NULLPTR; SHAPE if M < 0 or M > 16, if K or N is not a positive
+ * multiple of 128, or if K/128 is not wk * gs with wk <= 8 and gs one of 1, 2,
+ * 4, 8, 16 (every K/128 up to 8; even ones up to 16; multiples of 4 up to 32,
+ * of 8 up to 64, of 16 up to 128: K = 4096, 7168 and 14336 among them);
+ * ALIGN; DEVICE; LAUNCH.  M = 0 launches nothing. */
+int r9k_gemm_fp8_block_bf16a(const uint16_t *a, int64_t M, int64_t K, const uint8_t *w, const float *ws, int64_t N,
+                             uint16_t *c, void *stream);
+
+/* r9k_gemm_fp8_block_bf16a on fragment-order weights (r9k_pack_weight); the
+ * same result bits.  Errors: as r9k_gemm_fp8_block_bf16a. */
+int r9k_gemm_fp8_block_bf16a_packed(const uint16_t *a, int64_t M, int64_t K, const uint8_t *wp, const float *ws,
+                                    int64_t N, uint16_t *c, void *stream);
 
 /* The kernel a GEMM call of this shape runs under the current dispatch
  * setting (host only, launches nothing, needs no device): kernel receives
