@@ -83,14 +83,13 @@ using CfgM2 = Cfg<2, 4, 2, 3>;
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t *p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)p;
 }
-// The global address is a wave-uniform base (SGPRs) plus a 32-bit lane offset.
+// The global address is a wave-uniform base (SGPRs) plus a 32-bit lane offset;
+// the LDS address goes in M0, which the compiler sets from the operand.
 __device__ __forceinline__ void load_lds16(const void *base, uint32_t off, uint32_t l_addr) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(l_addr)
-                 : "memory", "m0");
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(l_addr) : "memory");
 }
 __device__ __forceinline__ void load_lds4(const void *base, uint32_t off, uint32_t l_addr) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(l_addr)
-                 : "memory", "m0");
+    asm volatile("global_load_lds_dword %0, %1" ::"v"(off), "s"(base), "{m0}"(l_addr) : "memory");
 }
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
