@@ -17,21 +17,25 @@ namespace r9k {
 // lane, 64 groups per 256-thread block.
 // With `transposed`, the scale of row m, group g goes to as[g*M + m] instead
 // (the tiled engine reads the scales of 256 consecutive rows per group).
+// Group gid walks the groups in the order of the scale array, so that a
+// block's 64 scale stores are contiguous: row-major [M][G] takes the groups of
+// a row in turn, the transposed [G][M] the rows of a group.
 __global__ __launch_bounds__(256) void k_quant_act(const uint4 *__restrict__ a, uint4 *__restrict__ aq,
                                                    float *__restrict__ as, int64_t ngroups, int64_t G, int64_t M,
                                                    bool transposed) {
     const int64_t gid = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
     const int l = threadIdx.x & 3;
     if (gid >= ngroups) return;  // uniform across the 4 lanes of a group
+    const int64_t grp = transposed ? (gid % M) * G + gid / M : gid;  // row-major group index m * G + g
     uint4 v[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = a[gid * 16 + l * 4 + i];
+    for (int i = 0; i < 4; ++i) v[i] = a[grp * 16 + l * 4 + i];
     uint4 codes[2];
     float s;
     quant_group4(v, codes, s);
-    aq[gid * 8 + l * 2] = codes[0];
-    aq[gid * 8 + l * 2 + 1] = codes[1];
-    if (l == 0) as[transposed ? (gid % G) * M + gid / G : gid] = s;
+    aq[grp * 8 + l * 2] = codes[0];
+    aq[grp * 8 + l * 2 + 1] = codes[1];
+    if (l == 0) as[gid] = s;
 }
 
 hipError_t launch_quant_act(const uint16_t *a, int64_t M, int64_t K, uint8_t *aq, float *as, hipStream_t s,
