@@ -18,7 +18,9 @@ The same line carries:
                 `traffic` is the HBM bytes per launch that the committed
                 rocprofv3 counter summary measured on the same kernel source;
   cpu_baseline  the CPU oracle timed on one full step of the same inputs;
-  prefill       M=4096, K=4096, N=12288: fp8 TFLOP/s vs 5.03 PFLOP/s dense;
+  prefill       M=4096, K=4096, N=12288: fp8 TFLOP/s vs 5.03 PFLOP/s dense, for
+                the fused call and (its `roofline`) for the GEMM kernel on
+                codes quantised beforehand;
   mid           M in {32,64,128,255} at (K,N) = (4096,4096) and (14336,4096);
   moe           16 tokens, hidden 2048, 128 experts of 768, top-8: GB/s over
                 the bytes of the experts the routing touches, plus the
@@ -100,31 +102,34 @@ def weight_copies(torch, r9k, dev, w_bits, min_bytes=ROTATE_BYTES, cap=16):
 
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_gemm_decode_packed_sweep_k4096_n14336_traffic.md")
+PREFILL_COUNTERS = os.path.join(ROOT, "profiles", "k_gemm_tiled_prefill_m4096_k4096_n12288_counters.md")
 
 
-def kernel_source_hash():
-    """Hash of the sources that make up the decode kernel and its launch."""
+def kernel_source_hash(kernel_file="gemm_decode.hip"):
+    """Hash of the sources that make up one kernel (the decode kernel by
+    default) and its launch."""
     h = hashlib.sha256()
-    for f in ("gemm_decode.hip", "r9k_device.h", "r9k_internal.h", "api.hip"):
+    for f in (kernel_file, "r9k_device.h", "r9k_internal.h", "api.hip"):
         with open(os.path.join(ROOT, "block_scaled_fp8_r9k_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles():
-    """HBM bytes per launch of the decode kernel over the sweep, from the
-    committed rocprofv3 counter summary (lines `source_hash: ...` and
-    `hbm_bytes_per_launch: ...`), if it was taken on the current source."""
+def traffic_from_profiles(summary=None, kernel_file="gemm_decode.hip"):
+    """HBM bytes per launch of a kernel (the decode kernel over the sweep by
+    default), from its committed rocprofv3 counter summary (lines
+    `source_hash: ...` and `hbm_bytes_per_launch: ...`), if it was taken on
+    the current source."""
     fields = {}
     try:
-        with open(TRAFFIC_SUMMARY) as fh:
+        with open(summary or TRAFFIC_SUMMARY) as fh:
             for ln in fh:
                 k, sep, v = ln.partition(":")
                 if sep and k.strip() in ("source_hash", "hbm_bytes_per_launch"):
                     fields[k.strip()] = v.strip().strip("`")
     except OSError:
         return None
-    if fields.get("source_hash") != kernel_source_hash():
+    if fields.get("source_hash") != kernel_source_hash(kernel_file):
         return None
     try:
         return float(fields["hbm_bytes_per_launch"])
@@ -254,8 +259,26 @@ def bench_prefill(torch, r9k, inputs, dev, reps):
     ms = tm.run(lambda i: g.replay(), reps) / C
     tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
     log(f"prefill {M}x{K}x{N}: {ms * 1e3:.1f} us, {tflops:.0f} TFLOP/s")
+    # The GEMM kernel on its own: the split entry point on codes quantised once
+    # beforehand is one k_gemm_tiled launch plus the transpose of the 4096 x 32
+    # activation scales (a few microseconds), so this slightly understates the kernel.
+    aq, as_ = r9k.quant_act(a)
+    kcalls = [lambda c=c: r9k.gemm_fp8_block_packed(aq, as_, copies[c][0], copies[c][1], c=c_out, workspace=wsp)
+              for c in range(C)]
+    for f in kcalls:
+        f()
+    gk = capture(torch, kcalls)
+    tk = Timer(torch)
+    tk.run(lambda i: gk.replay(), 1)
+    kms = tk.run(lambda i: gk.replay(), reps) / C
+    ktf = 2.0 * M * N * K / (kms * 1e-3) / 1e12
+    log(f"prefill GEMM kernel (pre-quantised A): {kms * 1e3:.1f} us, {ktf:.0f} TFLOP/s")
+    roof = dict(bound="mfma", achieved=ktf, peak=FP8_PEAK_TFLOPS, unit="TFLOP/s", frac=ktf / FP8_PEAK_TFLOPS,
+                traffic=traffic_from_profiles(PREFILL_COUNTERS, "gemm_tiled.hip"),
+                kernel="k_gemm_tiled (256 x 256 tile, fragment-order weights) with the scale transpose, per call",
+                flops_per_launch=2.0 * M * N * K, us_per_launch=kms * 1e3)
     return dict(workload=f"M={M}, K={K}, N={N}, fused act quant, fragment-order weights", us=ms * 1e3,
-                value=tflops, unit="TFLOP/s", peak=FP8_PEAK_TFLOPS, frac=tflops / FP8_PEAK_TFLOPS)
+                value=tflops, unit="TFLOP/s", peak=FP8_PEAK_TFLOPS, frac=tflops / FP8_PEAK_TFLOPS, roofline=roof)
 
 
 def bench_mid(torch, r9k, inputs, dev, reps):

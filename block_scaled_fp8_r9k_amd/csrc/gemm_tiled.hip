@@ -196,18 +196,33 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_gemm_tiled(TiledArgs p) {
     const uint8_t *abase = p.aq + m0 * K;
     const float *wsbase = p.ws + nb * G;
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
-    auto issue = [&](int64_t g, int st) {
+    // load instructions u0 .. u1 - 1 of this wave's share of group g, into
+    // stage st: the W rows first, then the A rows, then the two scale loads
+    constexpr int LPS = C::LOADS_PER_STAGE;
+    auto issue = [&](int64_t g, int st, int u0, int u1) {
         const uint32_t sb = lds0 + st * STAGE + C::WLOADS * wave * 1024;
         const uint32_t sa = lds0 + st * STAGE + WBYTES + C::ALOADS * wave * 1024;
         const uint32_t ss = lds0 + st * STAGE + WBYTES + ABYTES + wave * 512;
         const uint8_t *wg = wbase + g * (PK ? 2048 : 128), *ag = abase + g * 128;
 #pragma unroll
-        for (int u = 0; u < C::WLOADS; ++u) load_lds16(wg, woff[u], sb + u * 1024);
+        for (int u = 0; u < C::WLOADS; ++u)
+            if (u >= u0 && u < u1) load_lds16(wg, woff[u], sb + u * 1024);
 #pragma unroll
-        for (int u = 0; u < C::ALOADS; ++u) load_lds16(ag, aoff[u], sa + u * 1024);
-        load_lds4(p.as_t + g * M, soff, ss);
-        load_lds4(wsbase + g, 0u, ss + 256);
+        for (int u = 0; u < C::ALOADS; ++u)
+            if (C::WLOADS + u >= u0 && C::WLOADS + u < u1) load_lds16(ag, aoff[u], sa + u * 1024);
+        if (LPS - 2 >= u0 && LPS - 2 < u1) load_lds4(p.as_t + g * M, soff, ss);
+        if (LPS - 1 >= u0 && LPS - 1 < u1) load_lds4(wsbase + g, 0u, ss + 256);
     };
+    // With two stages (the 256 x 256 tile) the next stage's loads are spread
+    // over the first SPREAD column tiles, PER instructions after each: the
+    // compute unit's load unit takes 64 bytes a clock, so a whole stage issued
+    // at once by every wave queues for about a thousand clocks, with each
+    // wave's MFMAs behind its own loads; the last ones still go out early
+    // enough to land before the next group starts (2-3% faster on the MI355X).
+    // The three-stage tiles issue a stage at once, right after the barrier,
+    // which measured as fast or faster for them.
+    constexpr int SPREAD = (TN * 5 + 7) / 8;
+    constexpr int PER = (LPS + SPREAD - 1) / SPREAD;
 
     // fragment addresses inside a stage: column tile i of this wave at
     // wfo + 2048 i (and ^ 64), row tile j at afo + 2048 j (rows 16 apart keep
@@ -233,7 +248,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_gemm_tiled(TiledArgs p) {
 
 #pragma unroll
     for (int k = 0; k < NST - 1; ++k)
-        if (k < GL) issue(gb + k, k);
+        if (k < GL) issue(gb + k, k, 0, LPS);
     for (int64_t gl = 0; gl < GL; ++gl) {
         const int st = (int)(gl % NST);
         // local group gl's stage has landed: this wave's loads issued after it
@@ -243,7 +258,10 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_gemm_tiled(TiledArgs p) {
         if (NST == 3 && gl + 1 < GL) wait_vm<C::LOADS_PER_STAGE>();
         else wait_vm<0>();
         __syncthreads();
-        if (gl + NST - 1 < GL) issue(gb + gl + NST - 1, (int)((gl + NST - 1) % NST));
+        const bool more = gl + NST - 1 < GL;
+        const int64_t gn = gb + gl + NST - 1;
+        const int stn = (int)((gl + NST - 1) % NST);
+        if (NST == 3 && more) issue(gn, stn, 0, LPS);
 
         const uint8_t *wt = lds + st * STAGE;
         const uint8_t *at = wt + WBYTES;
@@ -274,6 +292,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_gemm_tiled(TiledArgs p) {
                 else promote_mfma(pr[j], wq[i % 3], af[j], e127, sc[j], acc[i - 1][j]);
                 if (j == 0 && i + 2 < TN) wq[(i + 2) % 3] = frag2(wt + wfo + 2048 * (i + 2), wt + wfo2 + 2048 * (i + 2));
             }
+            if (NST == 2 && i < SPREAD && more) issue(gn, stn, PER * i, PER * (i + 1));
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) scp[j] = sc[j];
