@@ -47,13 +47,25 @@ hipError_t launch_quant_act(const uint16_t *a, int64_t M, int64_t K, uint8_t *aq
     return hipGetLastError();
 }
 
-// as [M][G] -> as_t [G][M]; one thread per scale.
+// as [M][G] -> as_t [G][M], through LDS in tiles of 64 rows x 32 groups, so
+// that both the reads (128-byte row pieces) and the writes (256-byte column
+// pieces) are coalesced.  Grid: (ceil(M / 64), ceil(G / 32)).
 __global__ __launch_bounds__(256) void k_transpose_scales(const float *__restrict__ as, float *__restrict__ as_t,
                                                           int64_t M, int64_t G) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // index into as_t
-    if (i >= M * G) return;
-    const int64_t g = i / M, m = i % M;
-    as_t[i] = as[m * G + g];
+    __shared__ float tile[64][33];
+    const int64_t m0 = (int64_t)blockIdx.x * 64, g0 = (int64_t)blockIdx.y * 32;
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int r = (e * 256 + t) >> 5, c = t & 31;
+        if (m0 + r < M && g0 + c < G) tile[r][c] = as[(m0 + r) * G + g0 + c];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int c = (e * 256 + t) >> 6, r = t & 63;
+        if (m0 + r < M && g0 + c < G) as_t[(g0 + c) * M + m0 + r] = tile[r][c];
+    }
 }
 
 // One thread per 16-byte chunk of the packed output (consecutive threads write
@@ -79,8 +91,8 @@ hipError_t launch_pack_weight(const uint8_t *wq, int64_t N, int64_t K, uint8_t *
 }
 
 hipError_t launch_transpose_scales(const float *as, int64_t M, int64_t G, float *as_t, hipStream_t s) {
-    const int64_t n = M * G;
-    hipLaunchKernelGGL(k_transpose_scales, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, as, as_t, M, G);
+    hipLaunchKernelGGL(k_transpose_scales, dim3((unsigned)((M + 63) / 64), (unsigned)((G + 31) / 32)), dim3(256), 0,
+                       s, as, as_t, M, G);
     return hipGetLastError();
 }
 
