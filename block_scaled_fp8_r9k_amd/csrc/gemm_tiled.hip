@@ -267,12 +267,11 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_gemm_tiled(TiledArgs p) {
         const float *sl = (const float *)(at + ABYTES + wave * 512);
         // the weight fragments of column tiles 0 and 1; tile i + 2's is read
         // during tile i, into the registers tile i - 1 used
-        v8i wq[3];
+        v8i wq[3], af[4];
         wq[0] = frag2(wt + wfo, wt + wfo2);
-        if (TN > 1) wq[1] = frag2(wt + wfo + 2048, wt + wfo2 + 2048);
-        v8i af[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) af[j] = frag2(wt + afo + 2048 * j, wt + afo2 + 2048 * j);
+        if (TN > 1) wq[1] = frag2(wt + wfo + 2048, wt + wfo2 + 2048);
         const float wsg = sl[64 + lane];
         float sc[4];
 #pragma unroll

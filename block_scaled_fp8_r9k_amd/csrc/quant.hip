@@ -47,23 +47,22 @@ hipError_t launch_quant_act(const uint16_t *a, int64_t M, int64_t K, uint8_t *aq
     return hipGetLastError();
 }
 
-// as [M][G] -> as_t [G][M], through LDS in tiles of 64 rows x 32 groups, so
-// that both the reads (128-byte row pieces) and the writes (256-byte column
-// pieces) are coalesced.  Grid: (ceil(M / 64), ceil(G / 32)).
-__global__ __launch_bounds__(256) void k_transpose_scales(const float *__restrict__ as, float *__restrict__ as_t,
+// as [M][G] -> as_t [G][M], through LDS in tiles of 16 rows x 32 groups (one
+// value per thread, 512 threads), so that the reads take 128-byte row pieces
+// and the writes 64-byte column pieces, with enough CTAs to keep the memory
+// system busy (256 for M = 4096, G = 32).  Grid: (ceil(M / 16), ceil(G / 32)).
+__global__ __launch_bounds__(512) void k_transpose_scales(const float *__restrict__ as, float *__restrict__ as_t,
                                                           int64_t M, int64_t G) {
-    __shared__ float tile[64][33];
-    const int64_t m0 = (int64_t)blockIdx.x * 64, g0 = (int64_t)blockIdx.y * 32;
+    __shared__ float tile[16][33];
+    const int64_t m0 = (int64_t)blockIdx.x * 16, g0 = (int64_t)blockIdx.y * 32;
     const int t = threadIdx.x;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int r = (e * 256 + t) >> 5, c = t & 31;
+    {
+        const int r = t >> 5, c = t & 31;
         if (m0 + r < M && g0 + c < G) tile[r][c] = as[(m0 + r) * G + g0 + c];
     }
     __syncthreads();
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int c = (e * 256 + t) >> 6, r = t & 63;
+    {
+        const int c = t >> 4, r = t & 15;
         if (m0 + r < M && g0 + c < G) as_t[(g0 + c) * M + m0 + r] = tile[r][c];
     }
 }
@@ -91,7 +90,7 @@ hipError_t launch_pack_weight(const uint8_t *wq, int64_t N, int64_t K, uint8_t *
 }
 
 hipError_t launch_transpose_scales(const float *as, int64_t M, int64_t G, float *as_t, hipStream_t s) {
-    hipLaunchKernelGGL(k_transpose_scales, dim3((unsigned)((M + 63) / 64), (unsigned)((G + 31) / 32)), dim3(256), 0,
+    hipLaunchKernelGGL(k_transpose_scales, dim3((unsigned)((M + 15) / 16), (unsigned)((G + 31) / 32)), dim3(512), 0,
                        s, as, as_t, M, G);
     return hipGetLastError();
 }
