@@ -158,8 +158,12 @@ int r9k_gemm_fp8_block_qa(const uint16_t *a, int64_t M, int64_t K, const uint8_t
 int r9k_pack_weight(const uint8_t *wq, int64_t N, int64_t K, uint8_t *wp, void *stream);
 
 /* r9k_gemm_fp8_block and r9k_gemm_fp8_block_qa on fragment-order weights wp
- * (r9k_pack_weight); same arguments otherwise, same workspace query, and the
- * same result bit for bit as the row-major calls on the unpacked weights.
+ * (r9k_pack_weight); same arguments otherwise and the same workspace query.
+ * The result is the row-major calls' on the unpacked weights bit for bit when
+ * both run the same launch; at decode widths the planner may slice K
+ * differently for each layout (its fastest launch), and then the fp32 partial
+ * sums are added in another order, so that a few outputs differ by one bf16
+ * ulp.  r9k_gemm_fp8_block_plan reports the kernel and K split of each.
  * Errors: as the row-major calls. */
 int r9k_gemm_fp8_block_packed(const uint8_t *aq, const float *as, int64_t M, int64_t K, const uint8_t *wp,
                               const float *ws, int64_t N, uint16_t *c, void *workspace, size_t ws_bytes,

@@ -53,3 +53,20 @@ def assert_close(ora, gpu_bits: np.ndarray, oracle_f64: np.ndarray, what: str, r
         raise AssertionError(f"{what}: worst |gpu-oracle|/bound = {ratio:.3g} at {idx}: gpu {g[idx]!r} "
                              f"oracle {oracle_f64[idx]!r} bound {bound[idx]!r}")
     return ratio
+
+
+def assert_layouts_agree(ora, a_bits: np.ndarray, b_bits: np.ndarray, what: str):
+    """Two bf16 results of the same GEMM on the two weight layouts.  The decode planner may slice K
+    differently for fragment-order and row-major weights (each layout's fastest launch), and a different
+    slicing sums the fp32 partials in a different order; so the results agree to within one bf16 ulp,
+    and only on a small share of the outputs do they differ at all.  Where the plans coincide they are
+    equal."""
+    a = ora.bf16_value(a_bits).astype(np.float64)
+    b = ora.bf16_value(b_bits).astype(np.float64)
+    assert a.shape == b.shape, (what, a.shape, b.shape)
+    diff = np.abs(a - b)
+    bound = ora.bf16_ulp(b)
+    bad = np.argwhere(diff > bound)
+    assert bad.size == 0, f"{what}: {len(bad)} outputs differ by more than one bf16 ulp, first at {tuple(bad[0])}"
+    n_diff = int(np.count_nonzero(a_bits != b_bits))
+    assert n_diff <= max(2, a.size // 1000), f"{what}: {n_diff} of {a.size} outputs differ"

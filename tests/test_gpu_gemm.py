@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 from block_scaled_fp8_r9k_amd import inputs
-from tests.gpu_util import assert_bits_equal, assert_close, dev, host, say
+from tests.gpu_util import assert_bits_equal, assert_close, assert_layouts_agree, dev, host, say
 
 pytestmark = pytest.mark.gpu
 
@@ -180,15 +180,15 @@ def test_gemm_in_hip_graph(r9k, ora):
 @pytest.mark.parametrize("M,K,N", [(17, 4096, 2048), (24, 4096, 1024), (32, 4096, 2048), (32, 2048, 14336),
                                    (8, 14336, 1024)])
 def test_gemm_decode_two_row_tiles(r9k, ora, M, K, N):
-    """The decode kernel's widths past 16 rows (two row tiles) and K=14336 at 8 rows, full output,
-    both weight layouts."""
+    """The decode kernel's widths past 16 rows (two row tiles) and K=14336 at 8 rows, full output, both
+    weight layouts (which may slice K differently: equal up to the fp32 summation order)."""
     say("decode widths", M, K, N)
     p = Problem(r9k, ora, M, K, N, seed=M + 3)
     c64 = p.oracle_full(ora)
     got = p.run(r9k, 0, fused=True)
     assert_close(ora, got, c64, f"decode {M}x{K}x{N}")
     wp = r9k.pack_weight(p.wq_d)
-    assert_bits_equal(host(r9k.gemm_fp8_block_qa_packed(p.a_d, wp, p.ws_d)), got, "packed == row-major")
+    assert_layouts_agree(ora, host(r9k.gemm_fp8_block_qa_packed(p.a_d, wp, p.ws_d)), got, "packed vs row-major")
     assert_bits_equal(p.run(r9k, 0, fused=False), got, "split == fused")
 
 
@@ -196,7 +196,7 @@ def test_gemm_decode_two_row_tiles(r9k, ora, M, K, N):
                                    (32, 14336, 4096), (8, 14336, 4096)])
 def test_gemm_decode_k_split(r9k, ora, M, K, N):
     """Decode-kernel shapes that split K across CTAs (fp32 partials + ordered reduce), full output,
-    both weight layouts, fused == split form."""
+    both weight layouts (equal up to the fp32 summation order), fused == split form."""
     for packed in (False, True):
         kern, ks = r9k.gemm_fp8_block_plan(M, K, N, packed)
         assert kern == r9k.KERNEL_DECODE and ks > 1, (packed, kern, ks)
@@ -206,6 +206,6 @@ def test_gemm_decode_k_split(r9k, ora, M, K, N):
     got = p.run(r9k, 0, fused=True)
     assert_close(ora, got, c64, f"decode k-split {M}x{K}x{N}")
     wp = r9k.pack_weight(p.wq_d)
-    assert_bits_equal(host(r9k.gemm_fp8_block_qa_packed(p.a_d, wp, p.ws_d)), got, "packed == row-major")
+    assert_layouts_agree(ora, host(r9k.gemm_fp8_block_qa_packed(p.a_d, wp, p.ws_d)), got, "packed vs row-major")
     assert_bits_equal(p.run(r9k, 0, fused=False), got, "split == fused")
     assert_bits_equal(p.run(r9k, 0, fused=True), got, "repeat")

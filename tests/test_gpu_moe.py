@@ -81,11 +81,13 @@ def _dump(name, **arrays):
 
 # Shapes: the workload's, and small and wide ones that give K batches of 1, 2,
 # 3, 4, 6 and 8 groups (K/128 from 1 to 56), single- and multi-batch K loops,
-# and experts with more than 16 pairs (several row tiles).
+# experts with more than 16 pairs (several row tiles), and the largest token
+# count the decode path takes (255 tokens, 2040 pairs over 32 experts).
 @pytest.mark.parametrize("shape", [(16, 2048, 128, 768, 8), (2, 256, 4, 128, 2), (40, 256, 4, 256, 2),
                                    (40, 256, 4, 128, 2), (20, 256, 2, 128, 1), (1, 128, 3, 128, 3),
                                    (40, 1024, 4, 384, 2), (24, 512, 3, 512, 3), (40, 2048, 4, 256, 2),
-                                   (8, 512, 2, 2048, 2), (4, 4096, 2, 256, 2), (2, 7168, 2, 256, 2)])
+                                   (8, 512, 2, 2048, 2), (4, 4096, 2, 256, 2), (2, 7168, 2, 256, 2),
+                                   (255, 1024, 32, 256, 8)])
 def test_moe_decode(r9k, ora, shape):
     """Stage by stage on the three-launch path, then the fused path against it."""
     import torch

@@ -2,15 +2,18 @@
 
 The packed layout is checked byte for byte against its definition, restated
 here with numpy.  The GEMMs on packed weights must equal the row-major GEMMs
-on the same codes bit for bit (the kernels receive the same register
-contents), on every engine and in both the fused and the split form; the
-row-major GEMMs are the ones pinned to the oracle (test_gpu_gemm.py).
+on the same codes bit for bit whenever the two run the same launch (the kernels
+receive the same register contents), in both the fused and the split form; the
+decode kernel's planner may slice K differently for the two layouts (each
+layout's fastest launch), and then they agree up to the fp32 summation order
+(within one bf16 ulp, on a small share of the outputs).  The row-major GEMMs
+are the ones pinned to the oracle (test_gpu_gemm.py).
 """
 import numpy as np
 import pytest
 
 from block_scaled_fp8_r9k_amd import inputs
-from tests.gpu_util import assert_bits_equal, assert_close, dev, host, say
+from tests.gpu_util import assert_bits_equal, assert_close, assert_layouts_agree, dev, host, say
 
 pytestmark = pytest.mark.gpu
 
@@ -60,11 +63,14 @@ def test_packed_equals_row_major(r9k, ora, M, K, N, engine):
     wq, ws = r9k.quant_weight(dev(inputs.weights(M, N, K)))
     wp = r9k.pack_weight(wq)
     r9k.set_dispatch(255, engine)
+    # the decode kernel may take another K slicing on each layout; every other launch is the same
+    decode = r9k.gemm_fp8_block_plan(M, K, N, False)[0] == r9k.KERNEL_DECODE
+    same = assert_layouts_agree if decode else (lambda ora_, x, y, what: assert_bits_equal(x, y, what))
     ref = host(r9k.gemm_fp8_block_qa(a, wq, ws))
-    assert_bits_equal(host(r9k.gemm_fp8_block_qa_packed(a, wp, ws)), ref, f"fused {M}x{K}x{N} e{engine}")
+    same(ora, host(r9k.gemm_fp8_block_qa_packed(a, wp, ws)), ref, f"fused {M}x{K}x{N} e{engine}")
     aq, as_ = r9k.quant_act(a)
     ref_s = host(r9k.gemm_fp8_block(aq, as_, wq, ws))
-    assert_bits_equal(host(r9k.gemm_fp8_block_packed(aq, as_, wp, ws)), ref_s, f"split {M}x{K}x{N} e{engine}")
+    same(ora, host(r9k.gemm_fp8_block_packed(aq, as_, wp, ws)), ref_s, f"split {M}x{K}x{N} e{engine}")
 
 
 def test_packed_decode_sweep_against_oracle(r9k, ora):
