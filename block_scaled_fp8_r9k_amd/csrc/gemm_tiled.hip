@@ -123,6 +123,22 @@ __device__ __forceinline__ void promote_mfma(v4f &pr, const v8i &a, const v8i &b
     acc = v4f{a0, a1, a2, a3};
 }
 
+// The order of a group's 4 TN MFMAs: MFMA k computes column tile mfma_i, row
+// tile mfma_j.  With two or more column tiles, the first eight interleave
+// tiles 0 and 1 on rows 0 and 1, then on rows 2 and 3; then tile by tile.
+template <int TN>
+__device__ constexpr int mfma_i(int k) {
+    return TN == 1 ? 0 : k < 4 ? k >> 1 : k < 8 ? (k - 4) >> 1 : k >> 2;
+}
+template <int TN>
+__device__ constexpr int mfma_j(int k) {
+    return TN == 1 ? k : k < 4 ? k & 1 : k < 8 ? 2 + (k & 1) : k & 3;
+}
+// the MFMA after which weight tile t >= 2 is read into slot t % 3: tile 2
+// into the free slot at once, tile 3 after tile 0's last MFMA (k = 5), then
+// tile t during tile t - 2
+__device__ constexpr int wread_k(int t) { return t == 2 ? 0 : t == 3 ? 6 : 4 * (t - 2); }
+
 // wait until at most VM of this wave's vector-memory instructions are in flight
 template <int VM>
 __device__ __forceinline__ void wait_vm() {
@@ -267,30 +283,40 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_gemm_tiled(TiledArgs p) {
         const float *sl = (const float *)(at + ABYTES + wave * 512);
         // the weight fragments of column tiles 0 and 1; tile i + 2's is read
         // during tile i, into the registers tile i - 1 used
+        // Fragments at the group's start in the order of first use: weight
+        // tile 0, A rows 0 and 1, weight tile 1, A rows 2 and 3.
         v8i wq[3], af[4];
         wq[0] = frag2(wt + wfo, wt + wfo2);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) af[j] = frag2(wt + afo + 2048 * j, wt + afo2 + 2048 * j);
+        af[0] = frag2(wt + afo, wt + afo2);
+        af[1] = frag2(wt + afo + 2048, wt + afo2 + 2048);
         if (TN > 1) wq[1] = frag2(wt + wfo + 2048, wt + wfo2 + 2048);
+        af[2] = frag2(wt + afo + 4096, wt + afo2 + 4096);
+        af[3] = frag2(wt + afo + 6144, wt + afo2 + 6144);
         const float wsg = sl[64 + lane];
         float sc[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) sc[j] = sl[16 * j + l16] * wsg;
 
-        // Column tile i's MFMAs run together with the promotion of tile
-        // i - 1 (tile 0's with the previous group's last tile), so an FMA
-        // reads a product four MFMAs old.  The fragment offsets are constants
-        // from one stage base, so every read takes its offset in the
-        // instruction and costs no VALU work.
+        // MFMA k of the group (order: mfma_i / mfma_j) runs together with
+        // the promotion of the product of MFMA k - 4 (for k < 4, of the
+        // previous group's last four), held in product slot k % 4, so an FMA
+        // reads a product four MFMAs old.  The first eight MFMAs take column
+        // tiles 0 and 1 with A rows 0 and 1 before rows 2 and 3, so that the
+        // group starts on four LDS reads.  Weight tile t is read into slot
+        // t % 3 once the tile that used the slot before is done (wread_k).
+        // The fragment offsets are constants from one stage base, so every
+        // read takes its offset in the instruction and costs no VALU work.
 #pragma unroll
-        for (int i = 0; i < TN; ++i) {
+        for (int k = 0; k < 4 * TN; ++k) {
+            const int i = mfma_i<TN>(k), j = mfma_j<TN>(k);
+            const int kp = (k + 4 * TN - 4) % (4 * TN);  // the MFMA whose product this one's FMAs promote
+            const int ip = mfma_i<TN>(kp), jp = mfma_j<TN>(kp);
+            promote_mfma(pr[k & 3], wq[i % 3], af[j], k < 4 ? scp[jp] : sc[jp], acc[ip][jp]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (i == 0) promote_mfma(pr[j], wq[0], af[j], scp[j], acc[TN - 1][j]);
-                else promote_mfma(pr[j], wq[i % 3], af[j], sc[j], acc[i - 1][j]);
-                if (j == 0 && i + 2 < TN) wq[(i + 2) % 3] = frag2(wt + wfo + 2048 * (i + 2), wt + wfo2 + 2048 * (i + 2));
-            }
-            if (NST == 2 && i < SPREAD && more) issue(gn, stn, PER * i, PER * (i + 1));
+            for (int t = 2; t < TN; ++t)
+                if (k == wread_k(t)) wq[t % 3] = frag2(wt + wfo + 2048 * t, wt + wfo2 + 2048 * t);
+            if (NST == 2 && (k & 3) == 3 && (k >> 2) < SPREAD && more)
+                issue(gn, stn, PER * (k >> 2), PER * ((k >> 2) + 1));
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) scp[j] = sc[j];
@@ -298,9 +324,11 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_gemm_tiled(TiledArgs p) {
     // the last group's last tile: wait out the MFMA latency, then promote
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int k = 4 * TN - 4; k < 4 * TN; ++k) {
+        const int i = mfma_i<TN>(k), j = mfma_j<TN>(k);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[TN - 1][j][e] = __builtin_fmaf(pr[j][e], scp[j], acc[TN - 1][j][e]);
+        for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(pr[k & 3][e], scp[j], acc[i][j][e]);
+    }
 
     // lane holds, per tile (i, j), row m = m0 + 64 wm + 16 j + l16 and the four
     // columns n = n0 + TN 16 wn + 16 i + 4 q .. +3
