@@ -6,8 +6,8 @@
 // activations.  Here, with the block scales applied per 128-K group:
 //   C[m][n] = bf16( sum_g ws[n/128][g] * sum_{k in g} a[m][k] * dec(wq[n][k]) ).
 // An e4m3 value has at most four significant bits, so it converts to bf16
-// exactly (v_cvt_pk_f32_fp8, then the upper half of the fp32), and a
-// bf16 x bf16 product is exact in the MFMA's fp32.
+// exactly (v_cvt_scalef32_pk_bf16_fp8 with scale 1), and a bf16 x bf16
+// product is exact in the MFMA's fp32.
 //
 // Shape, like the fp8 decode kernel: a CTA's wn x wk waves own (16-column
 // tile, K slice) pairs; each wave requests its whole weight slice into
@@ -35,14 +35,12 @@ namespace {
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
-// four e4m3 codes (one 32-bit word) -> four bf16, two to a word
+// four e4m3 codes (one 32-bit word) -> four bf16, two to a word: one
+// converting instruction per pair, scale 1 (exact: an e4m3 value has at most
+// four significant bits and its exponent range lies inside bf16's)
 __device__ __forceinline__ void fp8x4_to_bf16(uint32_t x, uint32_t &lo, uint32_t &hi) {
-    typedef float v2f __attribute__((ext_vector_type(2)));
-    const v2f a = __builtin_amdgcn_cvt_pk_f32_fp8((int)x, false);  // bytes 0, 1
-    const v2f b = __builtin_amdgcn_cvt_pk_f32_fp8((int)x, true);   // bytes 2, 3
-    // the upper halves of the fp32 values (exact: at most four significant bits)
-    lo = __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
-    hi = __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u);
+    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x, 1.0f, false));  // bytes 0, 1
+    hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x, 1.0f, true));   // bytes 2, 3
 }
 
 // eight codes (two words) -> one MFMA fragment of eight bf16
