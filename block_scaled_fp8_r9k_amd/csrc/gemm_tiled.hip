@@ -281,10 +281,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_gemm_tiled(TiledArgs p) {
         const uint8_t *wt = lds + st * STAGE;
         const uint8_t *at = wt + WBYTES;
         const float *sl = (const float *)(at + ABYTES + wave * 512);
-        // the weight fragments of column tiles 0 and 1; tile i + 2's is read
-        // during tile i, into the registers tile i - 1 used
         // Fragments at the group's start in the order of first use: weight
-        // tile 0, A rows 0 and 1, weight tile 1, A rows 2 and 3.
+        // tile 0, A rows 0 and 1, weight tile 1, A rows 2 and 3; later weight
+        // tiles are read during the group (wread_k).
         v8i wq[3], af[4];
         wq[0] = frag2(wt + wfo, wt + wfo2);
         af[0] = frag2(wt + afo, wt + afo2);
