@@ -332,30 +332,39 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_gemm_tiled(TiledArgs p) {
     // lane holds, per tile (i, j), row m = m0 + 64 wm + 16 j + l16 and the four
     // columns n = n0 + TN 16 wn + 16 i + 4 q .. +3
     const int64_t nbase = n0 + TN * 16 * wn;
-    if (nbase >= N) return;
-    if (p.ksplit == 1 && TN % 2 == 0) {
-        // bf16 output in 16-byte pieces: lanes q and q ^ 1 (16 lanes apart)
-        // trade halves so that, of column tiles i and i + 1, an even-q lane
-        // holds eight consecutive columns of tile i and an odd-q lane of tile
-        // i + 1; every store then writes 64 contiguous bytes of a row per
-        // 16 lanes instead of 32
-        const bool odd = q & 1;
+    if (p.ksplit == 1) {
+        // bf16 output through LDS: each wave writes its tiles into a row-major
+        // copy of the CTA's output tile (rows padded by 16 bytes against bank
+        // conflicts), then the CTA stores it in 16-byte pieces, consecutive
+        // lanes along a row, so that every store instruction writes whole
+        // rows.  Stored straight from the MFMA layout, a store wrote 32
+        // contiguous bytes of a row per 16 lanes, and the output write took
+        // far longer than its bytes.
+        constexpr int PITCH = BN * 2 + 16;
+        static_assert(BM * PITCH <= C::SMEM, "the output tile fits in the stages' LDS");
+        __syncthreads();  // every wave is done reading the last stage
+        if (nbase < N) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t m = m0 + 64 * wm + 16 * j + l16;
+            for (int j = 0; j < 4; ++j) {
+                const int r = 64 * wm + 16 * j + l16;
 #pragma unroll
-            for (int i = 0; i < TN; i += 2) {
-                const uint2 a = bf16x4_rne(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-                const uint2 b = bf16x4_rne(acc[i + 1][j][0], acc[i + 1][j][1], acc[i + 1][j][2], acc[i + 1][j][3]);
-                const uint2 give = odd ? a : b;  // what the partner stores
-                const uint2 got = make_uint2((uint32_t)__shfl_xor((int)give.x, 16), (uint32_t)__shfl_xor((int)give.y, 16));
-                const uint4 v = odd ? make_uint4(got.x, got.y, b.x, b.y) : make_uint4(a.x, a.y, got.x, got.y);
-                const int col = odd ? 16 * (i + 1) + 4 * (q - 1) : 16 * i + 4 * q;
-                if (m < M) *(uint4 *)(p.c + m * N + nbase + col) = v;
+                for (int i = 0; i < TN; ++i)
+                    *(uint2 *)(lds + r * PITCH + 2 * (TN * 16 * wn + 16 * i + 4 * q)) =
+                        bf16x4_rne(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
             }
+        }
+        __syncthreads();
+        constexpr int CPR = BN / 8;  // 16-byte pieces per row
+        static_assert((BM * CPR) % C::THREADS == 0, "whole passes");
+#pragma unroll
+        for (int k = 0; k < BM * CPR / C::THREADS; ++k) {
+            const int id = k * C::THREADS + tid, r = id / CPR, cc = id % CPR;
+            const uint4 v = *(const uint4 *)(lds + r * PITCH + 16 * cc);
+            if (m0 + r < M && n0 + 8 * cc < N) *(uint4 *)(p.c + (m0 + r) * N + n0 + 8 * cc) = v;
         }
         return;
     }
+    if (nbase >= N) return;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int64_t m = m0 + 64 * wm + 16 * j + l16;
