@@ -364,6 +364,30 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_gemm_tiled(TiledArgs p) {
         }
         return;
     }
+    if constexpr (BM * (BN * 4 + 16) <= C::SMEM) {
+        // fp32 partials of a K split, through LDS in the same way
+        constexpr int PITCH = BN * 4 + 16;
+        __syncthreads();
+        if (nbase < N) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 64 * wm + 16 * j + l16;
+#pragma unroll
+                for (int i = 0; i < TN; ++i) *(v4f *)(lds + r * PITCH + 4 * (TN * 16 * wn + 16 * i + 4 * q)) = acc[i][j];
+            }
+        }
+        __syncthreads();
+        constexpr int CPR = BN / 4;
+        static_assert((BM * CPR) % C::THREADS == 0, "whole passes");
+        float *pbase = p.part + (int64_t)ks * M * N;
+#pragma unroll
+        for (int k = 0; k < BM * CPR / C::THREADS; ++k) {
+            const int id = k * C::THREADS + tid, r = id / CPR, cc = id % CPR;
+            const v4f v = *(const v4f *)(lds + r * PITCH + 16 * cc);
+            if (m0 + r < M && n0 + 4 * cc < N) *(v4f *)(pbase + (m0 + r) * N + n0 + 4 * cc) = v;
+        }
+        return;
+    }
     if (nbase >= N) return;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
