@@ -61,8 +61,8 @@ constexpr int MAX_GS = 16;  // K-groups per wave: 32 x 16-byte loads per lane
 // the activations into LDS, and writes fp32 partial sums part[ks][m][n] that a
 // second kernel adds in ascending ks.  Used where all of K does not fit in LDS
 // or where every CTA quantising all of K would cost more than the stream.
-template <bool QA, bool PK, int GS, int PASSES, int MT>
-__global__ __launch_bounds__(512) void k_gemm_decode(DecodeArgs p, int wn, int wk) {
+template <bool QA, bool PK, int GS, int PASSES, int MT, int NT>
+__global__ __launch_bounds__(NT) void k_gemm_decode(DecodeArgs p, int wn, int wk) {
     constexpr int SR = 16 * MT;                      // scale row stride
     constexpr int PB = PASSES < 4 ? PASSES : 4;      // passes per activation batch
     constexpr int NB = PASSES / PB;                  // activation batches (1 or 2)
@@ -226,7 +226,10 @@ __global__ __launch_bounds__(512) void k_gemm_decode(DecodeArgs p, int wn, int w
 // Is (wn, wk, gs, ksplit) a valid launch for M rows?  Fills c if so.
 static bool decode_fits(int64_t M, int64_t K, int64_t N, int wn, int wk, int64_t gs, int64_t ksplit, DecodeCfg &c) {
     const int64_t G = K / 128, tiles = N / 16;
-    if (tiles % wn || wn * wk > 8 || gs < 1 || gs > MAX_GS || (gs & (gs - 1))) return false;
+    if (tiles % wn || wn * wk > 16 || gs < 1 || gs > MAX_GS || (gs & (gs - 1))) return false;
+    // sixteen-wave CTAs (1024 threads, at most 128 VGPRs a lane) for one row tile and at most eight
+    // groups a wave: their weight slice must fit the smaller register budget
+    if (wn * wk > 8 && ((M + 15) / 16 > 1 || gs > 8)) return false;
     if ((int64_t)wk * gs * ksplit != G) return false;
     const int mt = (int)((M + 15) / 16);
     const int64_t gc = wk * gs;
@@ -273,7 +276,7 @@ DecodeCfg decode_config(int64_t M, int64_t K, int64_t N, bool packed) {
     int force_wk = 0;
     if (const char *e = getenv("R9K_DECODE_WK")) force_wk = atoi(e);
     DecodeCfg best{0, 0, 0, 0, 0, 0, 0};
-    for (int cand = 1; cand <= 8; ++cand) {
+    for (int cand = 1; cand <= 16; ++cand) {
         if (force_wk && cand != force_wk) continue;
         if (G % cand) continue;
         DecodeCfg t;
@@ -311,19 +314,27 @@ size_t decode_partial_bytes(int64_t M, int64_t K, int64_t N) {
 }
 
 // one instantiation: its 160 KiB dynamic-LDS limit is set once per device
-template <bool QA, bool PK, int GS, int PS, int MT>
-static hipError_t launch_one(const DecodeArgs &a, const DecodeCfg &c, hipStream_t s, dim3 grid, dim3 block) {
+template <bool QA, bool PK, int GS, int PS, int MT, int NT>
+static hipError_t launch_nt(const DecodeArgs &a, const DecodeCfg &c, hipStream_t s, dim3 grid, dim3 block) {
     static std::once_flag once[64];
     static hipError_t attr_err[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     std::call_once(once[dev], [&] {
-        attr_err[dev] = hipFuncSetAttribute((const void *)k_gemm_decode<QA, PK, GS, PS, MT>,
+        attr_err[dev] = hipFuncSetAttribute((const void *)k_gemm_decode<QA, PK, GS, PS, MT, NT>,
                                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     });
     if (attr_err[dev] != hipSuccess) return attr_err[dev];
-    hipLaunchKernelGGL((k_gemm_decode<QA, PK, GS, PS, MT>), grid, block, c.lds, s, a, c.wn, c.wk);
+    hipLaunchKernelGGL((k_gemm_decode<QA, PK, GS, PS, MT, NT>), grid, block, c.lds, s, a, c.wn, c.wk);
     return hipGetLastError();
+}
+
+// eight-wave CTAs, or sixteen (one row tile, at most eight groups a wave)
+template <bool QA, bool PK, int GS, int PS, int MT>
+static hipError_t launch_one(const DecodeArgs &a, const DecodeCfg &c, hipStream_t s, dim3 grid, dim3 block) {
+    if (c.wn * c.wk <= 8) return launch_nt<QA, PK, GS, PS, MT, 512>(a, c, s, grid, block);
+    if constexpr (MT == 1 && GS <= 8) return launch_nt<QA, PK, GS, PS, MT, 1024>(a, c, s, grid, block);
+    return hipErrorInvalidValue;
 }
 
 template <bool QA, bool PK, int GS, int MT>
