@@ -4,8 +4,8 @@
 // Activation quant is the per-token-group-128 quant of the r9700-stack release
 // v0.3.1 ("What changed for someone running it"), here as its own launch (the
 // split form); weight quant is the load-time conversion of release v0.3.2
-// (same section).  All three are HBM-bound streaming kernels: 16 lanes share
-// one group, each lane moving 16 bytes of bf16 in and 8 bytes of codes out.
+// (same section).  All three are HBM-bound streaming kernels; each one's
+// lane-to-data mapping is stated above it.
 #include "r9k_device.h"
 #include "r9k_internal.h"
 
@@ -13,36 +13,41 @@ namespace r9k {
 
 // Group gid covers bf16 [gid*128, gid*128 + 128) of the row-major [M][K]
 // array (row m, group g has gid = m*K/128 + g), which is also where its codes
-// go; its scale goes to as[gid].  4 lanes (a DPP quad) per group, 32 values a
-// lane, 64 groups per 256-thread block.
+// go; its scale goes to as[gid].  8 lanes (half a DPP row) per group, 32
+// groups per 256-thread block: lane j of a group holds the 16-byte pieces j
+// and j + 8, so that each load instruction reads whole 128-byte lines (8 lanes
+// x 16 bytes a group) and each store writes 64 contiguous bytes of codes.
 // With `transposed`, the scale of row m, group g goes to as[g*M + m] instead
-// (the tiled engine reads the scales of 256 consecutive rows per group).
-// Group gid walks the groups in the order of the scale array, so that a
-// block's 64 scale stores are contiguous: row-major [M][G] takes the groups of
-// a row in turn, the transposed [G][M] the rows of a group.
-__global__ __launch_bounds__(256) void k_quant_act(const uint4 *__restrict__ a, uint4 *__restrict__ aq,
+// (the tiled engine reads the scales of 256 consecutive rows per group).  The
+// groups are walked in memory order either way: the bf16 and the codes are
+// the bulk of the traffic, and the scattered 4-byte scale stores of
+// neighbouring rows meet in L2 before they reach HBM.
+__global__ __launch_bounds__(256) void k_quant_act(const uint4 *__restrict__ a, uint2 *__restrict__ aq,
                                                    float *__restrict__ as, int64_t ngroups, int64_t G, int64_t M,
                                                    bool transposed) {
-    const int64_t gid = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
-    const int l = threadIdx.x & 3;
-    if (gid >= ngroups) return;  // uniform across the 4 lanes of a group
-    const int64_t grp = transposed ? (gid % M) * G + gid / M : gid;  // row-major group index m * G + g
-    uint4 v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = a[grp * 16 + l * 4 + i];
-    uint4 codes[2];
-    float s;
-    quant_group4(v, codes, s);
-    aq[grp * 8 + l * 2] = codes[0];
-    aq[grp * 8 + l * 2 + 1] = codes[1];
-    if (l == 0) as[gid] = s;
+    const int64_t gid = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+    const int l = threadIdx.x & 7;
+    if (gid >= ngroups) return;  // uniform across the 8 lanes of a group
+    const uint4 v0 = a[gid * 16 + l], v1 = a[gid * 16 + 8 + l];
+    // maximum over the group's 8 lanes: quad_perm [1,0,3,2], [2,3,0,1], then
+    // row_half_mirror (lane i of each 8-lane half row reads lane 7 - i, which
+    // lies in the other quad)
+    uint32_t m = max(absmax8_bits(v0), absmax8_bits(v1));
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false));
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x141, 0xF, 0xF, false));
+    const float s = group_scale(__uint_as_float(m << 16));
+    const float r = 1.0f / s;
+    aq[gid * 16 + l] = quant8(v0, s, r);
+    aq[gid * 16 + 8 + l] = quant8(v1, s, r);
+    if (l == 0) as[transposed ? (gid % G) * M + gid / G : gid] = s;
 }
 
 hipError_t launch_quant_act(const uint16_t *a, int64_t M, int64_t K, uint8_t *aq, float *as, hipStream_t s,
                             bool scales_transposed) {
     int64_t ngroups = M * (K / 128);
-    int64_t blocks = (ngroups + 63) / 64;
-    hipLaunchKernelGGL(k_quant_act, dim3((unsigned)blocks), dim3(256), 0, s, (const uint4 *)a, (uint4 *)aq, as,
+    int64_t blocks = (ngroups + 31) / 32;
+    hipLaunchKernelGGL(k_quant_act, dim3((unsigned)blocks), dim3(256), 0, s, (const uint4 *)a, (uint2 *)aq, as,
                        ngroups, K / 128, M, scales_transposed);
     return hipGetLastError();
 }
