@@ -136,7 +136,10 @@ __global__ __launch_bounds__(NT) void k_gemm_decode(DecodeArgs p, int wn, int wk
         }
     };
 
-    // the weight slice: 16 rows x GS groups, 2 x 16 B per lane per group
+    // the weight slice: 16 rows x GS groups, 2 x 16 B per lane per group.  Packed
+    // weights are loaded with the non-temporal hint (each 1 KiB instruction reads
+    // whole lines once per call: 5-6% faster); row-major loads, which read half
+    // lines, ran 10% slower with the hint and keep plain loads
     uint4 wr[GS][2];
     const uint8_t *wrow = PK ? p.w + ((n0 / 16) * G + gbeg) * 2048 + 16 * lane
                              : p.w + (n0 + l16) * K + gbeg * 128 + 16 * q;
@@ -145,8 +148,8 @@ __global__ __launch_bounds__(NT) void k_gemm_decode(DecodeArgs p, int wn, int wk
         for (int j = 0; j < CH; ++j) {
             const int g = chunk * CH + j;
             if (PK) {
-                wr[g][0] = *(const uint4 *)(wrow + g * 2048);
-                wr[g][1] = *(const uint4 *)(wrow + g * 2048 + 1024);
+                wr[g][0] = load_nt16(wrow + g * 2048);
+                wr[g][1] = load_nt16(wrow + g * 2048 + 1024);
             } else {
                 wr[g][0] = *(const uint4 *)(wrow + g * 128);
                 wr[g][1] = *(const uint4 *)(wrow + g * 128 + 64);
