@@ -115,9 +115,10 @@ I32 = (torch.int32,)
 
 
 class Workspace:
-    """A zero-initialised device buffer that grows on demand (a fresh zeroed
-    allocation), as the library's workspace contract requires.  Not shared
-    between streams that run concurrently."""
+    """A device workspace that grows on demand (each growth is a fresh
+    allocation, zero-filled, though the library needs no initialisation: every
+    call writes what it reads).  Not shared between streams that run
+    concurrently."""
 
     def __init__(self, device=None):
         self.device = device
