@@ -153,8 +153,10 @@ __global__ __launch_bounds__(256) void k_moe_gemm(MoeArgs p) {
                         wr[g][c][1] = load_nt16(src + 1024);
                     } else {
                         const uint8_t *src = wbase + wrow[c] * K + (g0 + g) * 128 + 16 * q;
-                        wr[g][c][0] = load_nt16(src);
-                        wr[g][c][1] = load_nt16(src + 64);
+                        // row-major: two half lines; plain loads (with the
+                        // non-temporal hint these ran 10% slower)
+                        wr[g][c][0] = *(const uint4 *)src;
+                        wr[g][c][1] = *(const uint4 *)(src + 64);
                     }
                 }
 
