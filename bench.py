@@ -8,8 +8,10 @@ scales, bf16 out.  One step = the five fused GEMM calls on one batch of
 synthetic input; `value` is the algorithmic HBM bytes of the step divided by
 its time (GB/s).  Inputs are resident in HBM before timing; the weights rotate
 through enough distinct copies (>= 512 MB) that the 256 MB Infinity Cache
-cannot hold them between launches.  Timing: HIP graphs replayed on the current
-stream, bracketed by HIP events.
+cannot hold them between launches: every launch, also within a step, reads a
+copy that the previous launches did not.  Timing: HIP graphs replayed on the
+current stream, bracketed by HIP events; one graph holds as many consecutive
+steps as there are copies.
 
 The same line carries:
   roofline      the dominant kernel (k_gemm_decode, the weight-streaming
@@ -168,11 +170,29 @@ def bench_decode(torch, r9k, inputs, dev, steps, warmup, packed=True):
         for M in DECODE_M:
             call(M, c)()
     torch.cuda.synchronize()
-    step_graphs = [capture(torch, [call(M, c) for M in DECODE_M]) for c in range(C)]
+    # Every launch of a step reads its own weight copy (the step's five launches and the
+    # steps in turn walk the copies), so that no launch finds its weights in the Infinity
+    # Cache.  One graph holds C consecutive steps, as a decode step's many GEMMs sit in one
+    # graph; `steps` not a multiple of C ends on single-step graphs.
+    nM = len(DECODE_M)
+    step_calls = [[call(M, (c * nM + j) % C) for j, M in enumerate(DECODE_M)] for c in range(C)]
+    block_graph = capture(torch, [f for c in range(C) for f in step_calls[c]])
+    step_graphs = [capture(torch, step_calls[c]) for c in range(C)]
     step_bytes = sum(gemm_bytes(M, K, N) for M in DECODE_M)
     tm = Timer(torch)
-    tm.run(lambda i: step_graphs[i % C].replay(), max(warmup, 1))
-    ms_step = tm.run(lambda i: step_graphs[i % C].replay(), steps)
+
+    def run_steps(n):  # exactly n steps: n // C block replays, then single steps
+        def one(i):
+            if i < n // C:
+                block_graph.replay()
+            else:
+                step_graphs[i % C].replay()
+        return one, n // C + n % C
+
+    fn, calls = run_steps(max(warmup, 1))
+    tm.run(fn, calls)
+    fn, calls = run_steps(steps)
+    ms_step = tm.run(fn, calls) * calls / steps
 
     # the dominant kernel alone: graphs of back-to-back launches at one M
     per_m = {}
@@ -184,7 +204,7 @@ def bench_decode(torch, r9k, inputs, dev, steps, warmup, packed=True):
         b = gemm_bytes(M, K, N)
         per_m[M] = dict(us=ms * 1e3, GBs=b / (ms * 1e-3) / 1e9)
         log(f"decode M={M}: {ms * 1e3:.2f} us/launch, {per_m[M]['GBs']:.0f} GB/s")
-    del step_graphs, copies
+    del step_graphs, block_graph, copies
     torch.cuda.empty_cache()
     us_avg = float(np.mean([per_m[M]["us"] for M in DECODE_M]))
     bytes_avg = float(np.mean([gemm_bytes(M, K, N) for M in DECODE_M]))
