@@ -25,6 +25,13 @@ __device__ __forceinline__ uint4 load_nt16(const void *p) {
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// 16-byte buffer load at byte offset `off` of the descriptor's range, with the
+// non-temporal hint (cache-policy operand 2); offsets past the range read 0.
+__device__ __forceinline__ uint4 load_buf_nt16(__amdgpu_buffer_rsrc_t d, uint32_t off) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(d, (int)off, 0, 2);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // ---- bf16 ------------------------------------------------------------------
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
