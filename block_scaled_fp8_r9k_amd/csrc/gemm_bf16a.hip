@@ -89,15 +89,20 @@ __global__ __launch_bounds__(512) void k_gemm_bf16a(Bf16aArgs p, int wn, int wk)
     }
 
     // 2. the weight slice, 2 x 16 B per lane per group: the stream (packed weights
-    //    with the non-temporal hint, as in the decode kernel)
+    //    through a per-wave buffer descriptor with the non-temporal hint, as in
+    //    the decode kernel)
     uint4 wr[GS][2];
     const uint8_t *wrow = PK ? p.w + ((n0 / 16) * G + gbeg) * 2048 + 16 * lane
                              : p.w + (n0 + l16) * K + gbeg * 128 + 16 * q;
+    __amdgpu_buffer_rsrc_t wdesc;
+    if constexpr (PK)
+        wdesc = __builtin_amdgcn_make_buffer_rsrc((void *)(p.w + ((n0 / 16) * G + gbeg) * 2048), (short)0,
+                                                  GS * 2048, 0x00020000);
 #pragma unroll
     for (int g = 0; g < GS; ++g) {
         if (PK) {
-            wr[g][0] = load_nt16(wrow + g * 2048);
-            wr[g][1] = load_nt16(wrow + g * 2048 + 1024);
+            wr[g][0] = load_buf_nt16(wdesc, 16 * lane + g * 2048);
+            wr[g][1] = load_buf_nt16(wdesc, 16 * lane + g * 2048 + 1024);
         } else {
             wr[g][0] = *(const uint4 *)(wrow + g * 128);
             wr[g][1] = *(const uint4 *)(wrow + g * 128 + 64);
