@@ -141,6 +141,13 @@ def traffic_from_profiles(summary=None, kernel_file="gemm_decode.hip"):
 
 # --------------------------------------------------------------------------
 
+def step_copy(c, j, n_per_step, n_copies):
+    """The weight copy that launch j of step c reads: the launches of a step and the
+    steps in turn walk the copies, so that a copy comes back only after n_copies
+    launches (n_copies * |W| >= 512 MB, twice the Infinity Cache)."""
+    return (c * n_per_step + j) % n_copies
+
+
 def bench_decode(torch, r9k, inputs, dev, steps, warmup, packed=True):
     """The decode sweep.  packed: the weights in fragment order (r9k_pack_weight,
     done once at load like the quantisation, not timed); else row-major."""
@@ -175,7 +182,7 @@ def bench_decode(torch, r9k, inputs, dev, steps, warmup, packed=True):
     # Cache.  One graph holds C consecutive steps, as a decode step's many GEMMs sit in one
     # graph; `steps` not a multiple of C ends on single-step graphs.
     nM = len(DECODE_M)
-    step_calls = [[call(M, (c * nM + j) % C) for j, M in enumerate(DECODE_M)] for c in range(C)]
+    step_calls = [[call(M, step_copy(c, j, nM, C)) for j, M in enumerate(DECODE_M)] for c in range(C)]
     block_graph = capture(torch, [f for c in range(C) for f in step_calls[c]])
     step_graphs = [capture(torch, step_calls[c]) for c in range(C)]
     step_bytes = sum(gemm_bytes(M, K, N) for M in DECODE_M)

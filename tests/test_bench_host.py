@@ -41,3 +41,16 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one MI355X" in r.stderr
     assert r.stdout == ""
+
+
+def test_step_copies_never_repeat_within_the_cache_window():
+    """Each launch of the decode step reads a weight copy that none of the previous n_copies - 1 launches read
+    (the steps replay in order c = 0, 1, ..., C - 1, then again), so no launch finds its weights in the
+    Infinity Cache."""
+    for n_copies in (2, 9, 10, 16):
+        n_per_step = 5
+        seq = [bench.step_copy(c, j, n_per_step, n_copies) for _ in range(3) for c in range(n_copies)
+               for j in range(n_per_step)]
+        for i in range(len(seq)):
+            window = seq[max(0, i - n_copies + 1):i]
+            assert seq[i] not in window, (n_copies, i)
