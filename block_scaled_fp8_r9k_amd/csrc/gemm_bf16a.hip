@@ -60,8 +60,8 @@ __device__ __forceinline__ v8bf as_bf16(uint4 v) { return __builtin_bit_cast(v8b
 // so that the 16 rows a fragment read touches fall on distinct banks.  Without
 // it (rows too long for LDS) each lane loads its fragments from global memory,
 // two groups ahead of their use.
-template <bool PK, int GS, bool ALDS>
-__global__ __launch_bounds__(512) void k_gemm_bf16a(Bf16aArgs p, int wn, int wk) {
+template <bool PK, int GS, bool ALDS, int NT>
+__global__ __launch_bounds__(NT) void k_gemm_bf16a(Bf16aArgs p, int wn, int wk) {
     (void)wk;
     extern __shared__ __align__(16) uint8_t lds[];
     const int64_t K = p.K, N = p.N, G = K / 128;
@@ -206,6 +206,11 @@ Bf16aCfg bf16a_config(int64_t M, int64_t K, int64_t N) {
     if (const char *e = getenv("R9K_BF16A_GS")) force = atoi(e);  // tuning
     const bool wide = (size_t)M * (size_t)(K * 2 + 16) > 72 * 1024;
     static const int pref[] = {8, 16, 4, 2, 1}, pref_wide[] = {16, 8, 4, 2, 1};
+    // wide rows with eight groups a wave: sixteen-wave CTAs (1024 threads), four
+    // slices of eight groups per column tile, so that one CTA per compute unit
+    // runs the slices side by side (measured at M = 16, K = 4096, N = 14336)
+    if (wide && !force && G % 8 == 0 && G / 8 <= 4 && tiles % 4 == 0)
+        return Bf16aCfg{(int)(16 / (G / 8)), (int)(G / 8), 8};
     for (int gs : wide ? pref_wide : pref) {
         if (force && gs != force) continue;
         if (G % gs || G / gs > 8) continue;
@@ -217,7 +222,7 @@ Bf16aCfg bf16a_config(int64_t M, int64_t K, int64_t N) {
     return c;
 }
 
-template <bool PK, int GS, bool ALDS>
+template <bool PK, int GS, bool ALDS, int NT>
 static hipError_t launch_one(const Bf16aArgs &a, const Bf16aCfg &c, size_t lds, hipStream_t s) {
     // the dynamic-LDS limit is a per-device function attribute: set it once per device
     static std::once_flag once[64];
@@ -225,12 +230,12 @@ static hipError_t launch_one(const Bf16aArgs &a, const Bf16aCfg &c, size_t lds, 
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     std::call_once(once[dev], [&] {
-        attr_err[dev] = hipFuncSetAttribute((const void *)k_gemm_bf16a<PK, GS, ALDS>,
+        attr_err[dev] = hipFuncSetAttribute((const void *)k_gemm_bf16a<PK, GS, ALDS, NT>,
                                             hipFuncAttributeMaxDynamicSharedMemorySize, 150 * 1024);
     });
     if (attr_err[dev] != hipSuccess) return attr_err[dev];
     const dim3 grid((unsigned)(a.N / 16 / c.wn)), block((unsigned)(64 * c.wn * c.wk));
-    hipLaunchKernelGGL((k_gemm_bf16a<PK, GS, ALDS>), grid, block, lds, s, a, c.wn, c.wk);
+    hipLaunchKernelGGL((k_gemm_bf16a<PK, GS, ALDS, NT>), grid, block, lds, s, a, c.wn, c.wk);
     return hipGetLastError();
 }
 
@@ -238,7 +243,12 @@ template <bool PK, int GS>
 static hipError_t launch_b(const Bf16aArgs &a, const Bf16aCfg &c, hipStream_t s) {
     bool alds = false;
     const size_t lds = bf16a_lds(a.M, a.K, c, &alds);
-    return alds ? launch_one<PK, GS, true>(a, c, lds, s) : launch_one<PK, GS, false>(a, c, lds, s);
+    if (c.wn * c.wk <= 8)
+        return alds ? launch_one<PK, GS, true, 512>(a, c, lds, s) : launch_one<PK, GS, false, 512>(a, c, lds, s);
+    if constexpr (GS <= 8)  // sixteen waves: at most 128 VGPRs a lane, so at most eight groups a wave
+        if (c.wn * c.wk <= 16)
+            return alds ? launch_one<PK, GS, true, 1024>(a, c, lds, s) : launch_one<PK, GS, false, 1024>(a, c, lds, s);
+    return hipErrorInvalidValue;
 }
 
 template <bool PK>
