@@ -313,6 +313,9 @@ void ora_gemm_block_at(const uint8_t *aq, const float *as, int64_t M, int64_t K,
  *   hq, hs = activation quant of h over I
  *   y = GEMM row of hq against w2[e] [H][I], binary64, not rounded
  *   out[t] = bf16(sum_j w[t][j] * y(t, j)), j ascending, binary64.
+ * A slot whose id lies outside [0, E) names no expert: it is skipped in the
+ * sum, and its intermediates are written as zeros (the reading that such a
+ * slot contributes nothing).
  * Intermediates are written per pair p = t*topk + j when the pointers are not
  * NULL: gu [P][2I] bf16, h [P][I] bf16, hq [P][I], hs [P][I/128], y [P][H]. */
 /* h[i] = bf16(silu(gate[i]) * up[i]) for one pair, gate = gu[0..I), up =
@@ -350,6 +353,14 @@ static void moe_pair_range(int64_t lo, int64_t hi, void *p) {
     for (int64_t pr = lo; pr < hi; ++pr) {
         int64_t t = pr / c->topk;
         int64_t e = c->ids[pr];
+        if (e < 0 || e >= c->E) {  /* no expert: zero intermediates, nothing read */
+            for (int64_t n = 0; n < H; ++n) c->y[pr * H + n] = 0.0;
+            if (c->gu_out && !c->h_in) memset(c->gu_out + pr * 2 * I, 0, sizeof(uint16_t) * 2 * I);
+            if (c->h_out) memset(c->h_out + pr * I, 0, sizeof(uint16_t) * I);
+            if (c->hq_out) memset(c->hq_out + pr * I, 0, I);
+            if (c->hs_out) memset(c->hs_out + pr * GI, 0, sizeof(float) * GI);
+            continue;
+        }
         const uint8_t *w13 = c->w13q + e * 2 * I * H;
         const float *w13s = c->w13s + e * (2 * I / 128) * GH;
         const uint8_t *w2 = c->w2q + e * H * I;
@@ -385,8 +396,11 @@ static void moe_run(struct moe_ctx *c, uint16_t *out, int nthreads) {
     for (int64_t t = 0; t < T; ++t)
         for (int64_t n = 0; n < H; ++n) {
             double acc = 0.0;
-            for (int64_t j = 0; j < c->topk; ++j)
+            for (int64_t j = 0; j < c->topk; ++j) {
+                const int32_t e = c->ids[t * c->topk + j];
+                if (e < 0 || e >= c->E) continue;
                 acc += (double)c->w[t * c->topk + j] * c->y[(t * c->topk + j) * H + n];
+            }
             out[t * H + n] = ora_bf16_round(acc);
         }
     if (own_y) { free(c->y); c->y = NULL; }

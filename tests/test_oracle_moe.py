@@ -5,8 +5,14 @@ MoE decode, per (token t, slot j) with expert e = ids[t,j]:
   h  = bf16(silu(gate) * up), then quantised per 128 along I,
   y  = block GEMM of quant(h) against w2[e] (binary64, unrounded),
   out[t] = bf16(sum_j w[t,j] * y(t,j)), j ascending.
-silu's exp is the one step these pins cannot reach exactly (binary64 exp): the
-silu value itself is parity unpinned beyond the output tolerance.
+silu uses binary64 exp, which no pin reproduces bit for bit; instead silu is
+pinned through the oracle's own stage entry point (ora_moe_silu_mul) by facts
+that do not restate its formula: its zero and its slope 1/2 at zero, its two
+limits, the identity silu(z) - silu(-z) = z on every bf16 z, the closed form
+silu(ln 3) = (3/4) ln 3 and its minimum -W(1/e) (W the Lambert function).
+The stage entry points themselves (silu*up, and the down stage from given h)
+are pinned bit for bit against the whole chain.  A slot with an id outside
+[0, E) contributes nothing.
 
 Routing: the top-k logits (a larger logit first, ties to the lower id), with
 weights exp(l_j - l_0) / sum_i exp(l_i - l_0) over the chosen slots.  The
@@ -18,7 +24,7 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from block_scaled_fp8_r9k_amd import inputs
+import inputs
 from tests import exact
 from tests.test_oracle_gemm import _E4, _bf16_bits_exact
 
@@ -233,3 +239,145 @@ def test_fold_shared_term_closed_forms(ora):
     # the routed part plus the shared part, rounded once, against an independent fp64 sum
     ref = (np.einsum("tj,tjh->th", w.astype(np.float64), y.reshape(T, k, H)) + g[:, None] * sv)
     assert np.array_equal(ora.moe_fold(y, ids, w, E, shared=s, shared_w=g), ora.bf16_round(ref))
+
+
+# ---- the oracle's stage entry points (the references of the GPU test's stages) ----
+
+def test_silu_mul_stage_equals_the_chain(ora):
+    """ora_moe_silu_mul on the chain's own gu rows gives the chain's h bit for bit, so the GPU test's
+    stage-2 reference is the same function the whole-chain oracle applies."""
+    for seed, (T, H, E, I, topk) in ((81, (3, 256, 4, 256, 2)), (82, (5, 512, 3, 384, 3)),
+                                     (83, (16, 2048, 128, 768, 8))):
+        x, ids, w, w13, w2 = _routed(seed, T, H, E, I, topk)
+        used = np.unique(ids)
+        if E > 8:  # the workload shape: quantise only the experts the routing touches
+            q = {int(e): (ora.quant_weight(w13[e]), ora.quant_weight(w2[e])) for e in used}
+            z13, z2 = np.zeros((2 * I, H), np.uint8), np.zeros((H, I), np.uint8)
+            o13, o2 = np.zeros((2 * I // 128, H // 128), np.float32), np.zeros((H // 128, I // 128), np.float32)
+            q13 = np.stack([q[e][0][0] if e in q else z13 for e in range(E)])
+            s13 = np.stack([q[e][0][1] if e in q else o13 for e in range(E)])
+            q2 = np.stack([q[e][1][0] if e in q else z2 for e in range(E)])
+            s2 = np.stack([q[e][1][1] if e in q else o2 for e in range(E)])
+        else:
+            q13, s13, q2, s2 = _quant_experts(ora, w13, w2)
+        out, inter = ora.moe_decode(x, ids, w, q13, s13, q2, s2, intermediates=True)
+        assert np.array_equal(ora.moe_silu_mul(inter["gu"]), inter["h"])
+        # the down stage from those h rows reproduces every later intermediate and the output
+        out_h, inter_h = ora.moe_down_from_h(inter["h"], ids, w, q2, s2, intermediates=True)
+        assert np.array_equal(inter_h["hq"], inter["hq"])
+        assert np.array_equal(inter_h["hs"].view(np.uint32), inter["hs"].view(np.uint32))
+        assert np.array_equal(inter_h["y"].view(np.uint64), inter["y"].view(np.uint64))
+        assert np.array_equal(out_h, out)
+
+
+def test_down_from_h_on_foreign_rows(ora):
+    """moe_down_from_h on h rows that no gate_up produced (seeded bf16 rows): the quant of each row is the
+    dense activation quant, each y is the dense exact GEMM of that row, and the output is the routed sum;
+    out-of-range ids contribute nothing."""
+    T, H, E, I, topk = 3, 256, 4, 256, 2
+    x, ids, w, w13, w2 = _routed(84, T, H, E, I, topk)
+    _, _, q2, s2 = _quant_experts(ora, w13, w2)
+    h = inputs.activations(85, T * topk, I, outliers=True)
+    ids = ids.copy()
+    ids[1, 1] = E + 3                        # out of range: contributes nothing
+    out, inter = ora.moe_down_from_h(h, ids, w, q2, s2, intermediates=True)
+    hq, hs = ora.quant_act(h)
+    for p in range(T * topk):
+        t, j = divmod(p, topk)
+        if ids[t, j] >= E:
+            continue
+        assert np.array_equal(inter["hq"][p], hq[p])
+        assert np.array_equal(inter["hs"][p].view(np.uint32), hs[p].view(np.uint32))
+        _, y64 = ora.gemm_block(hq[p:p + 1], hs[p:p + 1], q2[ids[t, j]], s2[ids[t, j]], want_f64=True)
+        assert np.array_equal(inter["y"][p], y64[0])
+    for t in range(T):
+        acc = np.zeros(H, np.float64)
+        for j in range(topk):
+            if 0 <= ids[t, j] < E:
+                acc += np.float64(w[t, j]) * inter["y"][t * topk + j]
+        assert np.array_equal(out[t], ora.bf16_round(acc))
+
+
+def _silu_bf16(ora, z_bits, u_bits=None):
+    """h = bf16(silu(g) * u) through ora_moe_silu_mul, gate g = z (bf16 bits), up u (default 1.0)."""
+    z_bits = np.asarray(z_bits, np.uint16).ravel()
+    n = z_bits.size
+    u_bits = np.full(n, 0x3F80, np.uint16) if u_bits is None else np.asarray(u_bits, np.uint16).ravel()
+    # one pair per value: I = 128 columns, value i at gate column i % 128 of pair i // 128
+    P = -(-n // 128)
+    gate = np.zeros(P * 128, np.uint16)
+    up = np.full(P * 128, 0x3F80, np.uint16)
+    gate[:n] = z_bits
+    up[:n] = u_bits
+    gu = np.concatenate([gate.reshape(P, 128), up.reshape(P, 128)], axis=1)
+    return ora.moe_silu_mul(gu).reshape(-1)[:n]
+
+
+def _bits(ora, v):
+    return inputs.to_bf16_bits(np.asarray(v, np.float32))
+
+
+def test_silu_zero_and_slope_at_zero(ora):
+    """silu(+-0) = 0, and silu(z) = z/2 to within z^2/4 near zero (the logistic function is 1/2 at 0):
+    for z = 2^-j, j >= 10, the bf16 result is exactly 2^-(j+1)."""
+    h = _silu_bf16(ora, np.array([0x0000, 0x8000], np.uint16))
+    assert np.all(ora.bf16_value(h) == 0.0)
+    for j in range(10, 40):
+        z = _bits(ora, [2.0 ** -j, -(2.0 ** -j)])
+        got = ora.bf16_value(_silu_bf16(ora, z)).astype(np.float64)
+        assert got[0] == 2.0 ** -(j + 1) and got[1] == -(2.0 ** -(j + 1)), (j, got)
+
+
+def test_silu_limits(ora):
+    """Large |z|: silu(z) -> z (exactly, after bf16 rounding, from z = 16 on), and silu(-z) -> -z e^-z
+    (the asymptote, whose relative error e^-z is far below a bf16 ulp).  A mirrored definition
+    z / (1 + e^z) would swap the two limits."""
+    for z in (16.0, 20.0, 24.0, 32.0, 40.0, 64.0):
+        zb = _bits(ora, [z, -z])
+        got = ora.bf16_value(_silu_bf16(ora, zb)).astype(np.float64)
+        assert got[0] == z
+        asym = -z * math.exp(-z)
+        assert abs(got[1] - asym) <= ora.bf16_ulp(np.array([asym]))[0], (z, got[1], asym)
+
+
+def test_silu_odd_part_identity(ora):
+    """silu(z) - silu(-z) = z for every z (the logistic function satisfies s(z) + s(-z) = 1): checked on
+    every finite bf16 z in [-64, 64], to the two bf16 roundings."""
+    allb = np.arange(0x0000, 0x8000, dtype=np.uint16)
+    v = ora.bf16_value(allb).astype(np.float64)
+    zb = allb[(v > 0) & (v <= 64)]
+    z = ora.bf16_value(zb).astype(np.float64)
+    hp = ora.bf16_value(_silu_bf16(ora, zb)).astype(np.float64)
+    hn = ora.bf16_value(_silu_bf16(ora, zb | np.uint16(0x8000))).astype(np.float64)
+    slack = 0.5 * ora.bf16_ulp(hp) + 0.5 * ora.bf16_ulp(np.abs(hn) + 1e-300)
+    assert np.all(np.abs(hp - hn - z) <= slack * (1 + 1e-12))
+
+
+def test_silu_closed_forms(ora):
+    """silu(ln 3) = (3/4) ln 3 (the logistic function is 3/4 there), up to the bf16 rounding of ln 3 (the
+    slope of silu near ln 3 is below 1.1) and of the result; and silu's minimum, -W(1/e) = -0.27846...
+    at z = -1 - W(1/e) (W the Lambert function), matches the smallest bf16 result over a dense grid."""
+    from scipy.special import lambertw
+    ln3 = math.log(3.0)
+    zb = _bits(ora, [ln3])
+    zv = float(ora.bf16_value(zb)[0])
+    got = float(ora.bf16_value(_silu_bf16(ora, zb))[0])
+    assert abs(got - 0.75 * ln3) <= 1.1 * abs(zv - ln3) + float(ora.bf16_ulp(np.array([0.75 * ln3]))[0])
+    w = float(lambertw(1.0 / math.e).real)
+    grid = np.arange(0xBF80, 0xC000, dtype=np.uint16)           # every bf16 in [-2, -1)
+    h = ora.bf16_value(_silu_bf16(ora, grid)).astype(np.float64)
+    assert abs(h.min() + w) <= float(ora.bf16_ulp(np.array([w]))[0])
+    zmin = ora.bf16_value(grid[[np.argmin(h)]])[0]
+    assert abs(float(zmin) - (-1.0 - w)) <= 0.05
+
+
+def test_silu_mul_scaling(ora):
+    """h = bf16(silu(g) * u) rounds once: u = 2^j scales h by exactly 2^j (no intermediate rounding of
+    silu(g) that the scaling could expose), and u = -1 flips its sign."""
+    zb = inputs.activations(86, 1, 128 * 4, outliers=False).ravel()
+    base = ora.bf16_value(_silu_bf16(ora, zb)).astype(np.float64)
+    for j in (-5, -1, 1, 3, 7):
+        h = ora.bf16_value(_silu_bf16(ora, zb, _bits(ora, np.full(zb.size, 2.0 ** j)))).astype(np.float64)
+        assert np.array_equal(h, base * 2.0 ** j)
+    h = ora.bf16_value(_silu_bf16(ora, zb, _bits(ora, np.full(zb.size, -1.0)))).astype(np.float64)
+    assert np.array_equal(h, -base)
