@@ -426,7 +426,7 @@ def main():
 
     import torch
     import block_scaled_fp8_r9k_amd as r9k
-    from block_scaled_fp8_r9k_amd import inputs
+    import inputs
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     r9k.lib()

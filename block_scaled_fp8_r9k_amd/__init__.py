@@ -194,6 +194,8 @@ def gemm_fp8_block(aq, as_, w, ws, c=None, workspace=None, stream=None) -> torch
     N = w.shape[0]
     if c is None:
         c = torch.empty((M, N), dtype=torch.bfloat16, device=aq.device)
+    if M == 0:  # an empty batch: nothing to compute (an empty tensor has no device address to pass)
+        return c
     nbytes = gemm_fp8_block_workspace(M, K, N)
     wsb = _workspace(workspace, nbytes)
     _check(lib().r9k_gemm_fp8_block(_ptr(aq, FP8, "aq"), _ptr(as_, F32, "as"), M, K, _ptr(w, FP8, "w"),
@@ -208,6 +210,8 @@ def gemm_fp8_block_qa(a, w, ws, c=None, workspace=None, stream=None) -> torch.Te
     N = w.shape[0]
     if c is None:
         c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    if M == 0:  # an empty batch: nothing to compute (an empty tensor has no device address to pass)
+        return c
     nbytes = gemm_fp8_block_workspace(M, K, N)
     wsb = _workspace(workspace, nbytes)
     _check(lib().r9k_gemm_fp8_block_qa(_ptr(a, BF16, "a"), M, K, _ptr(w, FP8, "w"), _ptr(ws, F32, "ws"), N,
@@ -246,6 +250,8 @@ def gemm_fp8_block_packed(aq, as_, wp, ws, c=None, workspace=None, stream=None) 
     N = wp.shape[0]
     if c is None:
         c = torch.empty((M, N), dtype=torch.bfloat16, device=aq.device)
+    if M == 0:  # an empty batch: nothing to compute (an empty tensor has no device address to pass)
+        return c
     nbytes = gemm_fp8_block_workspace(M, K, N)
     wsb = _workspace(workspace, nbytes)
     _check(lib().r9k_gemm_fp8_block_packed(_ptr(aq, FP8, "aq"), _ptr(as_, F32, "as"), M, K, _ptr(wp, FP8, "wp"),
@@ -261,6 +267,8 @@ def gemm_fp8_block_qa_packed(a, wp, ws, c=None, workspace=None, stream=None) -> 
     N = wp.shape[0]
     if c is None:
         c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    if M == 0:  # an empty batch: nothing to compute (an empty tensor has no device address to pass)
+        return c
     nbytes = gemm_fp8_block_workspace(M, K, N)
     wsb = _workspace(workspace, nbytes)
     _check(lib().r9k_gemm_fp8_block_qa_packed(_ptr(a, BF16, "a"), M, K, _ptr(wp, FP8, "wp"), _ptr(ws, F32, "ws"),

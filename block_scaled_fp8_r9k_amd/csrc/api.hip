@@ -43,6 +43,32 @@ void read_env() {
     });
 }
 
+}  // namespace
+
+namespace r9k {
+const Tuning &tuning() {
+    static Tuning t;
+    static std::once_flag once;
+    std::call_once(once, [] {
+        auto num = [](const char *name) -> long long {
+            const char *e = getenv(name);
+            return e ? atoll(e) : 0;
+        };
+        t.decode_wn = (int)num("R9K_DECODE_WN");
+        t.decode_wk = (int)num("R9K_DECODE_WK");
+        const char *cfg = getenv("R9K_TILED_CFG");
+        t.tiled_cfg = cfg ? cfg[0] : 0;
+        t.tiled_ksplit = (int)num("R9K_TILED_KSPLIT");
+        t.skinny_kc = (int)num("R9K_SKINNY_KC");
+        t.skinny_ksplit = num("R9K_SKINNY_KSPLIT");
+        t.bf16a_gs = (int)num("R9K_BF16A_GS");
+    });
+    return t;
+}
+}  // namespace r9k
+
+namespace {
+
 // Device check, cached per device id: 1 = gfx950, 2 = not usable.
 constexpr int MAX_DEV = 64;
 std::atomic<int> g_dev_ok[MAX_DEV];
@@ -89,6 +115,7 @@ struct GemmWs {
 };
 GemmWs gemm_ws(int64_t M, int64_t K, int64_t N) {
     GemmWs w;
+    if (M == 0) return GemmWs{0, 0, 0, 0};  // nothing is launched, nothing is needed
     const SkinnyCfg c = skinny_config(M, K, N);
     w.part = 0;
     w.aq = w.part + std::max({skinny_partial_bytes(c, M, N), tiled_partial_bytes(tiled_plan(M, K, N), M, N),

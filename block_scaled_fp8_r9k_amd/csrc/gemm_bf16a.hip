@@ -203,13 +203,15 @@ Bf16aCfg bf16a_config(int64_t M, int64_t K, int64_t N) {
     const int64_t G = K / 128, tiles = N / 16;
     if (M < 1 || M > 16 || K % 128 || N % 128 || G < 1) return c;
     int force = 0;
-    if (const char *e = getenv("R9K_BF16A_GS")) force = atoi(e);  // tuning
+    force = tuning().bf16a_gs;
     const bool wide = (size_t)M * (size_t)(K * 2 + 16) > 72 * 1024;
     static const int pref[] = {8, 16, 4, 2, 1}, pref_wide[] = {16, 8, 4, 2, 1};
     // wide rows with eight groups a wave: sixteen-wave CTAs (1024 threads), four
     // slices of eight groups per column tile, so that one CTA per compute unit
     // runs the slices side by side (measured at M = 16, K = 4096, N = 14336)
-    if (wide && !force && G % 8 == 0 && G / 8 <= 4 && tiles % 4 == 0)
+    // (taken only where the slice count divides sixteen and the CTA's column
+    // tiles divide N's, so that the grid covers every column)
+    if (wide && !force && G % 8 == 0 && 16 % (G / 8) == 0 && tiles % (16 / (G / 8)) == 0)
         return Bf16aCfg{(int)(16 / (G / 8)), (int)(G / 8), 8};
     for (int gs : wide ? pref_wide : pref) {
         if (force && gs != force) continue;

@@ -278,12 +278,10 @@ DecodeCfg decode_config(int64_t M, int64_t K, int64_t N, bool packed) {
     // 1. all of K per CTA
     int wn = (tiles % 2 == 0 && tiles / 2 >= 256) ? 2 : 1;
     if (M >= 12 && tiles % 4 == 0 && tiles / 4 >= 192) wn = 4;
-    if (const char *e = getenv("R9K_DECODE_WN")) {
-        const int v = atoi(e);
+    if (const int v = tuning().decode_wn) {
         if (v >= 1 && v <= 4 && tiles % v == 0) wn = v;
     }
-    int force_wk = 0;
-    if (const char *e = getenv("R9K_DECODE_WK")) force_wk = atoi(e);
+    const int force_wk = tuning().decode_wk;
     DecodeCfg best{0, 0, 0, 0, 0, 0, 0};
     for (int cand = 1; cand <= 16; ++cand) {
         if (force_wk && cand != force_wk) continue;

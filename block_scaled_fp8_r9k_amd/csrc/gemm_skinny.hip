@@ -265,15 +265,13 @@ SkinnyCfg skinny_config(int64_t M, int64_t K, int64_t N) {
         }
         if (!found) { kc = 1; ksplit = G; }
     }
-    if (const char *e = getenv("R9K_SKINNY_KC")) {
-        int v = atoi(e);
+    if (int v = tuning().skinny_kc) {
         if (v >= 1 && v <= kc_max_for(mt) && (v & (v - 1)) == 0 && G % v == 0) {
             kc = v;
             if ((G / kc) % ksplit) ksplit = G / kc;
         }
     }
-    if (const char *e = getenv("R9K_SKINNY_KSPLIT")) {
-        int64_t v = atoll(e);
+    if (int64_t v = tuning().skinny_ksplit) {
         if (v >= 1 && c.mchunks == 1 && (G / kc) % v == 0) ksplit = v;
     }
     c.kc = kc;

@@ -441,11 +441,11 @@ TiledPlan tiled_plan(int64_t M, int64_t K, int64_t N) {
         if (M > 128 && G >= 64) t.shape = TILE_B;
         else t.shape = M <= 128 ? TILE_M1 : TILE_M2;
     }
-    if (const char *e = getenv("R9K_TILED_CFG")) {  // b|c|1|2 forces the tile shape (tuning)
-        if (e[0] == 'b') t.shape = TILE_B;
-        if (e[0] == 'c') t.shape = TILE_C;
-        if (e[0] == '1') t.shape = TILE_M1;
-        if (e[0] == '2') t.shape = TILE_M2;
+    switch (tuning().tiled_cfg) {  // b|c|1|2 forces the tile shape (tuning)
+        case 'b': t.shape = TILE_B; break;
+        case 'c': t.shape = TILE_C; break;
+        case '1': t.shape = TILE_M1; break;
+        case '2': t.shape = TILE_M2; break;
     }
     int64_t ctas = 0;
     switch (t.shape) {
@@ -455,9 +455,8 @@ TiledPlan tiled_plan(int64_t M, int64_t K, int64_t N) {
         case TILE_M2: ctas = ctas_of<CfgM2>(M, N); break;
     }
     // split K so that about 256 CTAs run, each with at least two groups
-    if (t.shape != TILE_C && ctas < 256) t.ksplit = (int)std::max<int64_t>(std::min<int64_t>(256 / ctas, G / 2), 1);
-    if (const char *e = getenv("R9K_TILED_KSPLIT")) {  // tuning
-        const int v = atoi(e);
+    if (t.shape != TILE_C && ctas > 0 && ctas < 256) t.ksplit = (int)std::max<int64_t>(std::min<int64_t>(256 / ctas, G / 2), 1);
+    if (const int v = tuning().tiled_ksplit) {  // tuning
         if (v >= 1 && v <= G && t.shape != TILE_C) t.ksplit = v;
     }
     return t;

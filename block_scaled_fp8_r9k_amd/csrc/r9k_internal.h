@@ -8,6 +8,25 @@
 
 namespace r9k {
 
+// Tuning overrides of the launch configuration, read from the environment once
+// per process (the first call that needs them) and fixed after that, so that a
+// workspace query and the call it sizes always plan the same launch.  0 (or
+// an empty string) means "not set"; each planner ignores values it cannot use.
+//   R9K_DECODE_WN, R9K_DECODE_WK    decode kernel: column tiles / K slices per CTA
+//   R9K_TILED_CFG                   tiled engine tile shape: b, c, 1 or 2
+//   R9K_TILED_KSPLIT                tiled engine K split
+//   R9K_SKINNY_KC, R9K_SKINNY_KSPLIT skinny kernel K batch and K split
+//   R9K_BF16A_GS                    bf16-activation variant: K-groups per wave
+struct Tuning {
+    int decode_wn, decode_wk;
+    char tiled_cfg;
+    int tiled_ksplit;
+    int skinny_kc;
+    long long skinny_ksplit;
+    int bf16a_gs;
+};
+const Tuning &tuning();
+
 // ---- quantisation (quant.hip) ----
 // scales_transposed: write as [K/128][M] instead of [M][K/128]
 hipError_t launch_quant_act(const uint16_t *a, int64_t M, int64_t K, uint8_t *aq, float *as, hipStream_t s,

@@ -1,5 +1,8 @@
 """Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
 
+A module of its own, outside the GPU library's package and the oracle, so that
+neither side imports the other to get its inputs.
+
 This module holds none of the method's arithmetic: it draws random numbers,
 rounds them to bf16 with torch's own conversion and picks outlier channels.
 Quantisation, GEMMs, MoE routing and everything else the method computes

@@ -21,7 +21,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__)
 sys.path.insert(0, ROOT)
 
 import oracle  # noqa: E402
-from block_scaled_fp8_r9k_amd import inputs  # noqa: E402
+import inputs  # noqa: E402
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SINGLE_TOKEN = os.path.join(HERE, "single_token_k512_n1024.txt")

@@ -86,6 +86,10 @@ def test_gemm_workspace_query(L):
     assert _ws(L, 16, 128, 100)[0] == -2
     assert _ws(L, -1, 128, 128)[0] == -2
     assert L.r9k_gemm_fp8_block_workspace(1, 128, 128, None) == -1
+    # an empty batch launches nothing and needs no workspace, for every shape (the query once divided
+    # by the tiled engine's CTA count, which is zero here)
+    for K, N in ((128, 128), (4096, 4096), (4096, 12288), (14336, 4096), (4096, 14336)):
+        assert _ws(L, 0, K, N) == (0, 0)
 
 
 def test_gemm_checks(L):

@@ -94,3 +94,13 @@ def test_plan_argument_checks(r9k):
     assert L.r9k_gemm_fp8_block_plan(1, 4096, 4000, 0, byref(k), byref(s)) == -2
     assert L.r9k_gemm_fp8_block_plan(-1, 4096, 4096, 0, byref(k), byref(s)) == -2
     assert L.r9k_gemm_fp8_block_plan(1, 4096, 4096, 2, byref(k), byref(s)) == -7
+
+
+@pytest.mark.parametrize("M,K,N", [(16, 4096, 151936), (8, 4096, 151936), (32, 4096, 65536), (48, 4096, 16384)])
+def test_wide_n_goes_to_the_skinny_kernel(r9k, M, K, N):
+    # very wide outputs (an LM head over a large vocabulary) at decode widths: the decode kernel's
+    # every-CTA activation quant would be repeated across too many column tiles, so the skinny kernel,
+    # with its quant in the A-load (M <= 64), takes them
+    for packed in (False, True):
+        kern, ks = r9k.gemm_fp8_block_plan(M, K, N, packed)
+        assert kern == r9k.KERNEL_SKINNY and ks >= 1, (packed, kern, ks)

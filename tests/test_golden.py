@@ -5,7 +5,7 @@ import hashlib
 import numpy as np
 import pytest
 
-from block_scaled_fp8_r9k_amd import inputs
+import inputs
 from tests.golden.make_golden import SINGLE_TOKEN, single_token
 
 

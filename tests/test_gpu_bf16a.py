@@ -3,7 +3,7 @@ against the oracle, through the C ABI, on both weight layouts."""
 import numpy as np
 import pytest
 
-from block_scaled_fp8_r9k_amd import inputs
+import inputs
 from tests.gpu_util import assert_bits_equal, dev, host, say
 
 pytestmark = pytest.mark.gpu
@@ -44,7 +44,9 @@ def _weights(ora, r9k, N, K, seed):
 
 @pytest.mark.parametrize("M,K,N", [(1, 4096, 14336), (2, 4096, 14336), (4, 4096, 14336), (8, 4096, 14336),
                                    (16, 4096, 14336), (5, 14336, 4096), (16, 14336, 4096), (3, 7168, 1024),
-                                   (1, 128, 128), (7, 384, 256), (13, 640, 384), (9, 1280, 512), (16, 2048, 2048)])
+                                   (1, 128, 128), (7, 384, 256), (13, 640, 384), (9, 1280, 512), (16, 2048, 2048),
+                                   # long staged rows whose K/1024 does not divide sixteen (three slices)
+                                   (16, 3072, 4096), (12, 3072, 4096), (16, 6144, 2048)])
 def test_bf16a_against_oracle(r9k, ora, M, K, N):
     say("bf16a", M, K, N)
     a = inputs.activations(M + K // 128, M, K, outliers=True)

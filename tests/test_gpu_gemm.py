@@ -9,7 +9,7 @@ bitwise identical.
 import numpy as np
 import pytest
 
-from block_scaled_fp8_r9k_amd import inputs
+import inputs
 from tests.gpu_util import assert_bits_equal, assert_close, assert_layouts_agree, dev, host, say
 
 pytestmark = pytest.mark.gpu
@@ -209,3 +209,36 @@ def test_gemm_decode_k_split(r9k, ora, M, K, N):
     assert_layouts_agree(ora, host(r9k.gemm_fp8_block_qa_packed(p.a_d, wp, p.ws_d)), got, "packed vs row-major")
     assert_bits_equal(p.run(r9k, 0, fused=False), got, "split == fused")
     assert_bits_equal(p.run(r9k, 0, fused=True), got, "repeat")
+
+
+def test_gemm_wide_n_skinny_inload_quant(r9k, ora):
+    """A wide output at a decode width (32 rows of a 4096 -> 65536 projection) runs the skinny kernel with
+    the activation quant in its A-load: sampled outputs against the oracle, fused == split bit for bit,
+    both weight layouts."""
+    M, K, N = 32, 4096, 65536
+    for packed in (False, True):
+        assert r9k.gemm_fp8_block_plan(M, K, N, packed)[0] == r9k.KERNEL_SKINNY
+    say("wide-N skinny", M, K, N)
+    p = Problem(r9k, ora, M, K, N, seed=21)
+    rows = np.array([0, 1, 15, 16, 31])
+    ms, ns, c64 = _sampled(ora, p, rows, n_random=8000)
+    got = p.run(r9k, 0, fused=True)
+    assert_close(ora, got[ms, ns], c64, "wide-N skinny")
+    assert_bits_equal(got, p.run(r9k, 0, fused=False), "wide-N skinny fused vs split")
+    wp = r9k.pack_weight(p.wq_d)
+    assert_bits_equal(host(r9k.gemm_fp8_block_qa_packed(p.a_d, wp, p.ws_d)), got, "wide-N skinny packed")
+
+
+def test_gemm_empty_batch(r9k):
+    """M = 0 through the binding returns an empty output without a launch, for every GEMM form."""
+    import torch
+    a = torch.empty((0, 4096), dtype=torch.bfloat16, device="cuda")
+    aq = torch.empty((0, 4096), dtype=torch.uint8, device="cuda")
+    as_ = torch.empty((0, 32), dtype=torch.float32, device="cuda")
+    w = torch.zeros((4096, 4096), dtype=torch.uint8, device="cuda")
+    ws = torch.ones((32, 32), dtype=torch.float32, device="cuda")
+    for c in (r9k.gemm_fp8_block_qa(a, w, ws), r9k.gemm_fp8_block(aq, as_, w, ws),
+              r9k.gemm_fp8_block_qa_packed(a, w, ws), r9k.gemm_fp8_block_packed(aq, as_, w, ws)):
+        assert tuple(c.shape) == (0, 4096)
+    assert r9k.gemm_fp8_block_workspace(0, 4096, 4096) == 0
+    torch.cuda.synchronize()

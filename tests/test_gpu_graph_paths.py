@@ -4,7 +4,7 @@ the replays."""
 import numpy as np
 import pytest
 
-from block_scaled_fp8_r9k_amd import inputs
+import inputs
 from tests.gpu_util import assert_bits_equal, dev, host, say
 
 pytestmark = pytest.mark.gpu

@@ -10,7 +10,7 @@ order, where the decode planner slices K differently for them).
 import numpy as np
 import pytest
 
-from block_scaled_fp8_r9k_amd import inputs
+import inputs
 from tests.gpu_util import assert_close, assert_layouts_agree, dev, host, say
 
 pytestmark = pytest.mark.gpu

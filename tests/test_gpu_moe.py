@@ -8,7 +8,7 @@ the GPU's own h, whose codes must match bit for bit.
 import numpy as np
 import pytest
 
-from block_scaled_fp8_r9k_amd import inputs
+import inputs
 from tests.gpu_util import assert_bits_equal, assert_close, dev, host, say
 
 pytestmark = pytest.mark.gpu
@@ -127,13 +127,23 @@ def test_moe_decode(r9k, ora, shape):
         assert np.all(np.abs(y.astype(np.float64) - yo) <= bound), "down GEMM y"
         # 5. the combine from the GPU's h
         assert_close(ora, unfused, ysum_h, f"moe output from the GPU's h {shape}")
-        # 6. the whole chain from x: at the workload's shape (I = 768, top-8) to
-        # the GEMM tolerance; the small shapes (two or one h groups, top-1/2)
-        # average a flipped group scale over few terms, so they get 5x
+        # 6. the whole chain from x.  The GPU's h differs from the oracle's h
+        # only where stage 1's fp32 sums flipped a gu rounding; a flip at a
+        # group's largest element moves that group's scale and so every code
+        # of the group.  The oracle measures exactly how far those h
+        # differences move the result (ysum_h against ysum, both binary64), so
+        # the chain is held to the tolerance plus that measured displacement,
+        # elementwise, with no free factor; and at the workload's shape
+        # (I = 768, top-8), where the displacement averages out, to the
+        # tolerance alone.
         ysum = np.einsum("tj,tjh->th", p.w.astype(np.float64), inter["y"].reshape(T, k, H))
-        ok, ratio, _ = ora.within_tolerance(unfused, ysum)
+        ok, ratio, bound = ora.within_tolerance(unfused, ysum)
         say(f"whole-chain worst error / tolerance = {ratio:.3f}")
-        assert ratio <= (1.0 if (I >= 768 and k >= 8) else 5.0), f"whole chain ratio {ratio}"
+        moved = np.abs(ysum_h - ysum)
+        err = np.abs(ora.bf16_value(unfused).astype(np.float64) - ysum)
+        assert np.all(err <= bound + moved), "whole chain beyond the tolerance plus the h displacement"
+        if I >= 768 and k >= 8:
+            assert ratio <= 1.0, f"whole chain ratio {ratio} at the workload shape"
     except AssertionError:
         _dump("moe_fail_%d_%d_%d_%d_%d.npz" % shape, gu=gu, h=h, hq=hq, hs=hs, y=y, out=unfused,
               ids=p.ids, w=p.w)

@@ -12,7 +12,7 @@ are the ones pinned to the oracle (test_gpu_gemm.py).
 import numpy as np
 import pytest
 
-from block_scaled_fp8_r9k_amd import inputs
+import inputs
 from tests.gpu_util import assert_bits_equal, assert_close, assert_layouts_agree, dev, host, say
 
 pytestmark = pytest.mark.gpu

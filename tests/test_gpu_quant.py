@@ -3,7 +3,7 @@ bit-exact against the oracle (codes and fp32 scale bits)."""
 import numpy as np
 import pytest
 
-from block_scaled_fp8_r9k_amd import inputs
+import inputs
 from tests.gpu_util import assert_bits_equal, dev, host, say
 
 pytestmark = pytest.mark.gpu

@@ -9,7 +9,7 @@ import os
 import numpy as np
 import pytest
 
-from block_scaled_fp8_r9k_amd import inputs
+import inputs
 from tests.gpu_util import assert_bits_equal, assert_close, dev, host, say
 
 pytestmark = pytest.mark.gpu

@@ -6,7 +6,7 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from block_scaled_fp8_r9k_amd import inputs
+import inputs
 from tests import exact
 from tests.test_oracle_gemm import _E4, _bf16_bits_exact, _grid_values
 
