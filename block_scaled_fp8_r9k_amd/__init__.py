@@ -20,7 +20,7 @@ from ctypes import POINTER, c_char_p, c_int, c_int64, c_size_t, c_void_p
 
 import torch
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 ENGINE_AUTO, ENGINE_SKINNY, ENGINE_TILED = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -287,7 +287,7 @@ def get_dispatch() -> tuple[int, int]:
     return m.value, e.value
 
 
-KERNEL_NONE, KERNEL_DECODE, KERNEL_SKINNY, KERNEL_TILED = 0, 1, 2, 3
+KERNEL_NONE, KERNEL_DECODE, KERNEL_SKINNY, KERNEL_TILED, KERNEL_MID = 0, 1, 2, 3, 4
 
 
 def gemm_fp8_block_plan(M: int, K: int, N: int, packed: bool = False) -> tuple[int, int]:

@@ -62,6 +62,7 @@ const Tuning &tuning() {
         t.skinny_kc = (int)num("R9K_SKINNY_KC");
         t.skinny_ksplit = num("R9K_SKINNY_KSPLIT");
         t.bf16a_gs = (int)num("R9K_BF16A_GS");
+        t.mid = getenv("R9K_MID") ? (int)num("R9K_MID") : -1;
     });
     return t;
 }
@@ -133,27 +134,36 @@ struct GemmRoute {
     int kernel;  // R9K_KERNEL_*
     DecodeCfg dc;
     TiledPlan tp;
+    MidCfg mc;
 };
+// The skinny engine (M <= the boundary) is three kernels: the decode kernel
+// (all of K per CTA, the activation quant in its A-load) where it runs without
+// a K split; else, from 17 rows on, the mid-width kernel (all of K per CTA on
+// activations quantised once per call); else the decode kernel with a K split,
+// or the split-K skinny kernel (very wide N).  Above the boundary: the tiled
+// engine.
 GemmRoute route_gemm(int64_t M, int64_t K, int64_t N, bool packed) {
-    GemmRoute r{R9K_KERNEL_SKINNY, DecodeCfg{0, 0, 0, 0, 0, 0, 0}, TiledPlan{TILE_C, 1}};
-    int engine = engine_for(M);
-    if (engine == R9K_ENGINE_SKINNY) {
-        // decode widths: the dedicated weight-streaming kernel when the shape
-        // fits it, with the activation quant in its A-load
-        r.dc = decode_config(M, K, N, packed);
-        if (r.dc.wn) {
-            r.kernel = R9K_KERNEL_DECODE;
-            return r;
-        }
-        // wider skinny shapes under automatic dispatch: the tiled engine with
-        // its K split is faster from 64 rows on, and at any width for long K
-        // (measured on the MI355X at N = 4096, K = 4096 and 14336)
-        if (g_engine.load() == R9K_ENGINE_AUTO && (M >= 64 || K >= 8192)) engine = R9K_ENGINE_TILED;
-    }
+    GemmRoute r{R9K_KERNEL_SKINNY, DecodeCfg{0, 0, 0, 0, 0, 0, 0}, TiledPlan{TILE_C, 1}, MidCfg{0, 0, 0, 0}};
+    const int engine = engine_for(M);
     if (engine == R9K_ENGINE_TILED) {
         r.kernel = R9K_KERNEL_TILED;
         r.tp = tiled_plan(M, K, N);
+        return r;
     }
+    r.dc = decode_config(M, K, N, packed);
+    const int mid = tuning().mid;
+    if (r.dc.wn && r.dc.ksplit == 1 && mid != 1) {
+        r.kernel = R9K_KERNEL_DECODE;
+        return r;
+    }
+    if (mid != 0 && (M >= 17 || mid == 1)) {
+        r.mc = mid_config(M, K, N);
+        if (r.mc.mt) {
+            r.kernel = R9K_KERNEL_MID;
+            return r;
+        }
+    }
+    if (r.dc.wn) r.kernel = R9K_KERNEL_DECODE;
     return r;
 }
 
@@ -170,6 +180,18 @@ int run_gemm(const uint16_t *a, const uint8_t *aq, const float *as, int64_t M, i
     if (route.kernel == R9K_KERNEL_DECODE) {
         DecodeArgs d{a, aq, as, w, ws, c, M, K, N, packed, (float *)(base + L.part)};
         return launch_result(launch_gemm_decode(d, route.dc, s));
+    }
+    if (route.kernel == R9K_KERNEL_MID) {
+        if (a) {  // quantise A once per call into the workspace, then run on codes
+            uint8_t *aq_w = base + L.aq;
+            float *as_w = (float *)(base + L.as);
+            rc = launch_result(launch_quant_act(a, M, K, aq_w, as_w, s));
+            if (rc) return rc;
+            aq = aq_w;
+            as = as_w;
+        }
+        MidArgs m{aq, as, w, ws, c, M, K, N, packed};
+        return launch_result(launch_gemm_mid(m, route.mc, s));
     }
     if (route.kernel == R9K_KERNEL_TILED) {
         // the tiled engine reads codes and transposed scales [K/128][M] from
@@ -338,6 +360,7 @@ int r9k_gemm_fp8_block_plan(int64_t M, int64_t K, int64_t N, int packed, int *ke
     *kernel = r.kernel;
     *ksplit = r.kernel == R9K_KERNEL_DECODE ? r.dc.ksplit
               : r.kernel == R9K_KERNEL_TILED ? r.tp.ksplit
+              : r.kernel == R9K_KERNEL_MID   ? 1
                                               : skinny_config(M, K, N).ksplit;
     return R9K_OK;
 }

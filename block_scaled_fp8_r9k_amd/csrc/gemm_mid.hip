@@ -1,0 +1,285 @@
+// Engine (a) at mid widths (17 to 256 rows): the block-scaled fp8 GEMM as one
+// launch over all of K, with no partial sums leaving a CTA.
+//
+// The r9700-stack release v0.3.2 notes ("What changed for someone running it")
+// run the fp8 decode kernels up to 255 rows.  At these widths the weight is
+// still most of the bytes, but the activation codes (M x K) are read by every
+// column block, and the product of the two is large enough that splitting K
+// across CTAs means writing and re-reading fp32 partials of M x N.  Here a CTA
+// covers a BM x BN output block over all of K:
+//   - BM = 16 MT rows (MT row tiles of 16, up to 64 rows), BN = 16 WN columns;
+//     WN x WK waves, wave (ct, slice) owns column tile ct and the K-groups
+//     g = s WK + slice of steps s = 0 .. G/WK - 1; the WK slices of a column
+//     tile are summed through LDS at the end, in ascending slice order;
+//   - the CTA count is about 256 (one per compute unit) and BM x BN is as square
+//     as the shape allows, which minimises the bytes a compute unit reads
+//     (BN + BM) x K;
+//   - weight fragments stream straight into registers (16-byte loads, fragment
+//     order or row-major), D steps ahead of their use;
+//   - activation codes come quantised (the fused entry point quantises once per
+//     call, like the tiled engine): with WN > 1 the CTA stages each step's
+//     WK groups of its BM rows in LDS (loaded into registers D steps ahead,
+//     written to one of two LDS buffers, one barrier per step), shared by the WN
+//     column tiles; with WN = 1 nothing is shared and each wave loads its own
+//     activation fragments into registers;
+//   - per group one e4m3 16x16x128 MFMA per row tile, promoted with the group's
+//     scales, acc += P * as[m,g] * ws[n/128,g].
+// MFMA roles as in the decode kernel: weight rows are the A operand (16 n),
+// activation rows the B operand (16 m); a lane's four outputs are four
+// consecutive n of row l % 16, and lane quarter q feeds bytes [16q, +16) and
+// [64 + 16q, +16) of a group.  Rows past M read row M - 1 and are never stored.
+#include <algorithm>
+#include <mutex>
+
+#include "r9k_device.h"
+#include "r9k_internal.h"
+
+namespace r9k {
+
+namespace {
+constexpr int MID_PITCH = 144;  // bytes per staged row of one group (+16: distinct banks for a fragment read)
+}
+
+template <int MT, int WN, int WK, int D, bool PK>
+__global__ __launch_bounds__(64 * WN * WK) void k_gemm_mid(MidArgs p) {
+    constexpr int NW = WN * WK, NT = 64 * NW, BM = 16 * MT;
+    constexpr bool ALDS = WN > 1;
+    constexpr int STAGE = WK * BM * MID_PITCH;        // one step's groups of the CTA's rows
+    constexpr int CHUNKS = WK * BM * 8;               // 16-byte pieces of a step's activation codes
+    constexpr int ACH = ALDS ? (CHUNKS + NT - 1) / NT : 2 * MT;  // per thread (staged) or per lane (direct)
+    extern __shared__ __align__(16) uint8_t lds[];
+
+    const int64_t K = p.K, N = p.N, M = p.M, G = K / 128;
+    const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, q = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ct = wave % WN, slice = wave / WN;
+
+    // block -> (column block, row block).  Blocks are dealt round-robin to the
+    // 8 XCDs; each XCD takes a contiguous range of local ids, and the row blocks
+    // of one column block are consecutive ids, so they run together on one XCD
+    // and share its weight bytes in L2.
+    const int64_t nrb = (M + BM - 1) / BM, nblk = (N / (16 * WN)) * nrb;
+    int64_t lid = blockIdx.x;
+    if (nblk % 8 == 0) lid = (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8;
+    const int64_t cb = lid / nrb, rb = lid % nrb;
+    const int64_t m0 = rb * BM, n0 = (cb * WN + ct) * 16;
+    const int64_t steps = G / WK;
+    const int64_t nbk = __builtin_amdgcn_readfirstlane((int)(n0 / 128));
+    const float *wsrow = p.ws + nbk * G;
+
+    // this lane's activation rows (one per row tile), clamped to M - 1
+    int64_t arow[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) arow[mt] = min<int64_t>(m0 + 16 * mt + l16, M - 1);
+
+    uint4 wr[D][2];        // weight fragments of a step
+    // activation codes of a step (staged pieces, or this lane's fragments), held
+    // as plain vectors: as uint4 aggregates the staged copies stay in scratch memory
+    u32x4 ar[D][ACH];
+    float sr[D][MT];       // the activation scales of this lane's rows for its group of a step
+
+    const uint8_t *wtile = PK ? p.w + (n0 / 16) * G * 2048 + 16 * lane : p.w + (n0 + l16) * K + 16 * q;
+    auto issue = [&](int64_t s, int slot) {
+        const int64_t g = s * WK + slice;
+        if (PK) {
+            wr[slot][0] = load_nt16(wtile + g * 2048);
+            wr[slot][1] = load_nt16(wtile + g * 2048 + 1024);
+        } else {
+            wr[slot][0] = *(const uint4 *)(wtile + g * 128);
+            wr[slot][1] = *(const uint4 *)(wtile + g * 128 + 64);
+        }
+        if constexpr (ALDS) {
+#pragma unroll
+            for (int c = 0; c < ACH; ++c) {
+                int id = tid + c * NT;
+                id = id < CHUNKS ? id : CHUNKS - 1;
+                const int kk = id / (BM * 8), r = (id / 8) % BM, c16 = id % 8;
+                const int64_t row = min<int64_t>(m0 + r, M - 1);
+                ar[slot][c] = *(const u32x4 *)(p.aq + row * K + (s * WK + kk) * 128 + c16 * 16);
+            }
+        } else {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const uint8_t *src = p.aq + arow[mt] * K + g * 128 + 16 * q;
+                ar[slot][2 * mt] = *(const u32x4 *)src;
+                ar[slot][2 * mt + 1] = *(const u32x4 *)(src + 64);
+            }
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) sr[slot][mt] = p.as[arow[mt] * G + g];
+    };
+
+    v4f acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+
+    // step s from ring slot j: stage the activations (ALDS), then one MFMA per row tile
+    auto consume = [&](int64_t s, int j) {
+        const uint8_t *st = lds + (j & 1) * STAGE;  // D is even or 1 step per chunk: slot parity = step parity
+        if constexpr (ALDS) {
+#pragma unroll
+            for (int c = 0; c < ACH; ++c) {
+                const int id = tid + c * NT;
+                if (CHUNKS % NT == 0 || id < CHUNKS) {
+                    const int kk = id / (BM * 8), r = (id / 8) % BM, c16 = id % 8;
+                    *(u32x4 *)(lds + (j & 1) * STAGE + (kk * BM + r) * MID_PITCH + c16 * 16) = ar[j][c];
+                }
+            }
+            __syncthreads();
+        }
+        const float wsg = wsrow[s * WK + slice];
+        const v8i wf = make_frag(wr[j][0], wr[j][1]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            v8i af;
+            if constexpr (ALDS) {
+                const uint8_t *ap = st + (slice * BM + 16 * mt + l16) * MID_PITCH + 16 * q;
+                af = make_frag(*(const uint4 *)ap, *(const uint4 *)(ap + 64));
+            } else {
+                const u32x4 lo = ar[j][2 * mt], hi = ar[j][2 * mt + 1];
+                af = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            }
+            const v4f pr = mfma_e4m3_16x16x128(wf, af, zero);
+            const float sc = sr[j][mt] * wsg;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[mt][i] = __builtin_fmaf(pr[i], sc, acc[mt][i]);
+        }
+    };
+
+    // the planner guarantees steps % D == 0 and steps >= D
+#pragma unroll
+    for (int j = 0; j < D; ++j) issue(j, j);
+    int64_t s0 = 0;
+    for (; s0 + D < steps; s0 += D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            consume(s0 + j, j);
+            issue(s0 + j + D, j);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < D; ++j) consume(s0 + j, j);
+
+    // ---- sum the K slices in ascending order, round, store
+    if constexpr (WK > 1) {
+        __syncthreads();  // every wave is done with the staged activations
+        v4f *red = (v4f *)lds;  // [wave][MT][64 lanes]
+        if (slice > 0) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) red[(wave * MT + mt) * 64 + lane] = acc[mt];
+        }
+        __syncthreads();
+        if (slice > 0) return;
+#pragma unroll
+        for (int sl = 1; sl < WK; ++sl)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt] += red[((sl * WN + ct) * MT + mt) * 64 + lane];
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int64_t m = m0 + 16 * mt + l16;
+        if (m < M)
+            *(uint2 *)(p.c + m * N + n0 + 4 * q) = bf16x4_rne(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
+    }
+}
+
+// LDS of a launch: two activation stages (WN > 1) and the slice reduction
+static size_t mid_lds(const MidCfg &c) {
+    const size_t stages = c.wn > 1 ? 2 * (size_t)c.wk * 16 * c.mt * MID_PITCH : 0;
+    const size_t red = c.wk > 1 ? (size_t)c.wn * c.wk * c.mt * 64 * 16 : 0;
+    return std::max<size_t>(std::max(stages, red), 16);
+}
+
+// (mt, wn, wk, depth) for a shape.  Row tiles: enough for min(M, 64) rows; then
+// the widest column block (wn = 4, 2, 1) that still gives at least 256 CTAs,
+// eight waves a CTA (wk = 8 / wn, fewer where K/128 is not a multiple), and the
+// deepest load ring (4 steps; 2 where a wave loads its own four row tiles of
+// activations, for the register budget) that divides the step count.
+MidCfg mid_config(int64_t M, int64_t K, int64_t N) {
+    MidCfg c{0, 0, 0, 0};
+    const int64_t G = K / 128;
+    if (M < 1 || M > 256 || N % 16) return c;
+    const int mt = (int)std::min<int64_t>((M + 15) / 16, 4);
+    const int64_t nrb = (M + 16 * mt - 1) / (16 * mt);
+    for (int wn : {4, 2, 1}) {
+        if (N % (16 * wn)) continue;
+        if (wn > 1 && (N / (16 * wn)) * nrb < 256) continue;
+        for (int wk = 8 / wn; wk >= 1; wk /= 2) {
+            if (G % wk) continue;
+            const int64_t steps = G / wk;
+            for (int d : {4, 2, 1}) {
+                if (wn == 1 && mt > 2 && d > 2) continue;  // direct fragments: 8 mt registers a step
+                if (wn > 1 && d == 1) continue;             // two LDS buffers alternate by step parity
+                if (steps < d || steps % d) continue;
+                return MidCfg{mt, wn, wk, d};
+            }
+        }
+    }
+    return c;
+}
+
+template <int MT, int WN, int WK, int D, bool PK>
+static hipError_t launch_mid_one(const MidArgs &a, const MidCfg &c, hipStream_t s) {
+    static std::once_flag once[64];
+    static hipError_t attr_err[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::call_once(once[dev], [&] {
+        attr_err[dev] = hipFuncSetAttribute((const void *)k_gemm_mid<MT, WN, WK, D, PK>,
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    });
+    if (attr_err[dev] != hipSuccess) return attr_err[dev];
+    const int64_t nblk = (a.N / (16 * WN)) * ((a.M + 16 * MT - 1) / (16 * MT));
+    hipLaunchKernelGGL((k_gemm_mid<MT, WN, WK, D, PK>), dim3((unsigned)nblk), dim3(64 * WN * WK), mid_lds(c), s,
+                       a);
+    return hipGetLastError();
+}
+
+template <int MT, int WN, int WK, bool PK>
+static hipError_t launch_mid_d(const MidArgs &a, const MidCfg &c, hipStream_t s) {
+    switch (c.depth) {
+        case 4: if constexpr (WN > 1 || MT <= 2) return launch_mid_one<MT, WN, WK, 4, PK>(a, c, s); break;
+        case 2: return launch_mid_one<MT, WN, WK, 2, PK>(a, c, s);
+        case 1: if constexpr (WN == 1) return launch_mid_one<MT, WN, WK, 1, PK>(a, c, s); break;
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int MT, int WN, bool PK>
+static hipError_t launch_mid_wk(const MidArgs &a, const MidCfg &c, hipStream_t s) {
+    switch (c.wk) {
+        case 8: if constexpr (WN == 1) return launch_mid_d<MT, WN, 8, PK>(a, c, s); break;
+        case 4: if constexpr (WN <= 2) return launch_mid_d<MT, WN, 4, PK>(a, c, s); break;
+        case 2: return launch_mid_d<MT, WN, 2, PK>(a, c, s);
+        case 1: return launch_mid_d<MT, WN, 1, PK>(a, c, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int MT, bool PK>
+static hipError_t launch_mid_wn(const MidArgs &a, const MidCfg &c, hipStream_t s) {
+    switch (c.wn) {
+        case 4: return launch_mid_wk<MT, 4, PK>(a, c, s);
+        case 2: return launch_mid_wk<MT, 2, PK>(a, c, s);
+        case 1: return launch_mid_wk<MT, 1, PK>(a, c, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <bool PK>
+static hipError_t launch_mid_mt(const MidArgs &a, const MidCfg &c, hipStream_t s) {
+    switch (c.mt) {
+        case 1: return launch_mid_wn<1, PK>(a, c, s);
+        case 2: return launch_mid_wn<2, PK>(a, c, s);
+        case 3: return launch_mid_wn<3, PK>(a, c, s);
+        case 4: return launch_mid_wn<4, PK>(a, c, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_mid(const MidArgs &a, const MidCfg &c, hipStream_t s) {
+    return a.packed ? launch_mid_mt<true>(a, c, s) : launch_mid_mt<false>(a, c, s);
+}
+
+}  // namespace r9k

@@ -17,6 +17,7 @@ namespace r9k {
 //   R9K_TILED_KSPLIT                tiled engine K split
 //   R9K_SKINNY_KC, R9K_SKINNY_KSPLIT skinny kernel K batch and K split
 //   R9K_BF16A_GS                    bf16-activation variant: K-groups per wave
+//   R9K_MID                         mid-width kernel: 0 never, 1 wherever it fits (else the planner's choice)
 struct Tuning {
     int decode_wn, decode_wk;
     char tiled_cfg;
@@ -24,6 +25,7 @@ struct Tuning {
     int skinny_kc;
     long long skinny_ksplit;
     int bf16a_gs;
+    int mid;  // -1: not set
 };
 const Tuning &tuning();
 
@@ -94,6 +96,26 @@ struct SkinnyArgs {
     bool packed;
 };
 hipError_t launch_gemm_skinny(const SkinnyArgs &args, const SkinnyCfg &cfg, hipStream_t s);
+
+// ---- mid widths, one launch over all of K (gemm_mid.hip) ----
+// Activations come quantised: codes [M][K] and scales [M][K/128] (row-major).
+struct MidArgs {
+    const uint8_t *aq;
+    const float *as;
+    const uint8_t *w;   // weight codes, row-major or fragment-order (packed)
+    const float *ws;
+    uint16_t *c;
+    int64_t M, K, N;
+    bool packed;
+};
+struct MidCfg {
+    int mt;     // row tiles of 16 per CTA (0: the shape does not fit)
+    int wn;     // column tiles of 16 per CTA
+    int wk;     // K slices per column tile (waves per CTA = wn * wk)
+    int depth;  // steps of loads in flight per wave
+};
+MidCfg mid_config(int64_t M, int64_t K, int64_t N);
+hipError_t launch_gemm_mid(const MidArgs &args, const MidCfg &cfg, hipStream_t s);
 
 // ---- LDS-tiled MFMA engine (gemm_tiled.hip) ----
 // Activations come pre-quantised, with their scales transposed: as_t [K/128][M].

@@ -60,9 +60,11 @@ extern "C" {
 #pragma GCC visibility push(default)
 #endif
 
-#define R9K_ABI_VERSION 5
+#define R9K_ABI_VERSION 6
 
-/* Return codes. */
+/* Return codes: 0 or negative, as the pages' kernels return them (release
+ * v0.3.0, its validation record: a test failing "with the kernel's -7").
+ * The values below are this library's own. */
 #define R9K_OK 0
 #define R9K_ERR_NULLPTR (-1)   /* a required pointer is NULL */
 #define R9K_ERR_SHAPE (-2)     /* a size is out of range (see each call) */
@@ -73,12 +75,15 @@ extern "C" {
 #define R9K_ERR_ARG (-7)       /* an enumerated argument has an unknown value */
 
 /* The ABI version this library implements (R9K_ABI_VERSION; 4 added the MoE
- * routing and the shared-expert fold, 5 the bf16-activation variant).  Callers refuse
- * a library whose version differs from the header they were built against,
- * the convention of the pages' plugin, which refuses an older library. */
+ * routing and the shared-expert fold, 5 the bf16-activation variant, 6 the
+ * mid-width kernel in the plan query).  Callers refuse
+ * a library whose version differs from the header they were built against:
+ * the convention of the pages' plugin, which refuses an older libr9k.so
+ * (release v0.2.2, "Upgrading").  Host only; cannot fail. */
 int r9k_abi_version(void);
 
-/* Static text for a return code; never NULL. */
+/* Static text for a return code (the codes above; release v0.3.0's validation
+ * record for the convention); never NULL, also for unknown codes.  Host only. */
 const char *r9k_strerror(int code);
 
 /* ------------------------------------------------------------------------ */
@@ -110,7 +115,11 @@ int r9k_encode_e4m3(const float *x, int64_t n, uint8_t *codes, void *stream);
 /* ------------------------------------------------------------------------ */
 
 /* Workspace bytes that r9k_gemm_fp8_block and r9k_gemm_fp8_block_qa need for
- * this shape, under any dispatch setting.  Host only; touches no device.
+ * this shape, under any dispatch setting (release v0.3.1, "What changed for
+ * someone running it": the split form's separate quant launch writes the
+ * activation codes somewhere; release v0.3.2, same section: the tiled GEMMs
+ * above the decode widths quantise their activations).  0 for M = 0.
+ * Host only; touches no device.
  * The workspace holds the activation codes and scales of a call that
  * quantises once before the GEMM, and the fp32 split-K partial sums of the
  * skinny engine; every call writes what it reads, so the contents need no
@@ -171,8 +180,11 @@ int r9k_gemm_fp8_block_packed(const uint8_t *aq, const float *as, int64_t M, int
 int r9k_gemm_fp8_block_qa_packed(const uint16_t *a, int64_t M, int64_t K, const uint8_t *wp, const float *ws,
                                  int64_t N, uint16_t *c, void *workspace, size_t ws_bytes, void *stream);
 
-/* Dispatch control.  skinny_max_m: the largest M the skinny engine takes
- * (default 255, the pages' boundary; env R9K_FP8_SKINNY_MAXM).  engine:
+/* Dispatch control (release v0.3.2, "What changed for someone running it":
+ * the fp8 decode kernels are used to 255 rows, a setting that restores the
+ * earlier boundary, and the tiled fp8 GEMMs above it).  skinny_max_m: the
+ * largest M the skinny engine takes (default 255, the pages' boundary; env
+ * R9K_FP8_SKINNY_MAXM).  engine:
  * R9K_ENGINE_AUTO (by M), R9K_ENGINE_SKINNY or R9K_ENGINE_TILED (forced, for
  * tests; env R9K_FP8_ENGINE=auto|skinny|tiled).  The setting is process-wide;
  * change it only while no GEMM call is being issued.
@@ -219,14 +231,17 @@ int r9k_gemm_fp8_block_bf16a_packed(const uint16_t *a, int64_t M, int64_t K, con
 #define R9K_KERNEL_DECODE 1
 #define R9K_KERNEL_SKINNY 2
 #define R9K_KERNEL_TILED 3
+#define R9K_KERNEL_MID 4
 int r9k_gemm_fp8_block_plan(int64_t M, int64_t K, int64_t N, int packed, int *kernel, int *ksplit);
 
 /* ------------------------------------------------------------------------ */
 /* MoE decode                                                                */
 /* ------------------------------------------------------------------------ */
 
-/* Workspace bytes for r9k_moe_fp8_decode (host only).  Needs no
- * initialisation; calls sharing one must not overlap in time.
+/* Workspace bytes for r9k_moe_fp8_decode (host only): the intermediates of
+ * release v0.3.3's three-launch path (gu, h and its codes and scales, y), which
+ * the fused path partly keeps in registers.  Needs no initialisation; calls
+ * sharing one must not overlap in time.
  * Errors: NULLPTR (bytes); SHAPE as for the call. */
 int r9k_moe_fp8_decode_workspace(int64_t T, int64_t H, int64_t E, int64_t I, int64_t topk, size_t *bytes);
 
@@ -303,7 +318,8 @@ int r9k_moe_fp8_decode_ex(const uint16_t *x, int64_t T, int64_t H, const int32_t
 int r9k_moe_route(const float *logits, int64_t T, int64_t E, int64_t topk, int32_t *topk_ids, float *topk_w,
                   void *stream);
 
-/* Byte offset inside the MoE workspace of an intermediate (for tests):
+/* Byte offset inside the MoE workspace of an intermediate of the three-launch
+ * path (release v0.3.3, "What changed for someone running it"; for tests):
  * which = 0 gu [P][2I] bf16, 1 h [P][I] bf16, 2 y [P][H] fp32, 3 hq [P][I] fp8,
  * 4 hs [P][I/128] fp32 (P = T*topk; gu, hq and hs are written by the
  * three-launch path only).  Host only.  Errors: NULLPTR; SHAPE; ARG. */

@@ -23,7 +23,8 @@ def test_kernel_codes_match_header(r9k):
     text = open(os.path.join(ROOT, "include", "r9k.h")).read()
     d = {k: int(v) for k, v in re.findall(r"#define\s+(R9K_KERNEL_\w+)\s+(\d+)", text)}
     assert d == {"R9K_KERNEL_NONE": r9k.KERNEL_NONE, "R9K_KERNEL_DECODE": r9k.KERNEL_DECODE,
-                 "R9K_KERNEL_SKINNY": r9k.KERNEL_SKINNY, "R9K_KERNEL_TILED": r9k.KERNEL_TILED}
+                 "R9K_KERNEL_SKINNY": r9k.KERNEL_SKINNY, "R9K_KERNEL_TILED": r9k.KERNEL_TILED,
+                 "R9K_KERNEL_MID": r9k.KERNEL_MID}
 
 
 @pytest.mark.parametrize("packed", [False, True])
@@ -34,8 +35,7 @@ def test_decode_sweep_streams_whole_rows(r9k, M, packed):
     assert r9k.gemm_fp8_block_plan(M, 4096, 14336, packed) == (r9k.KERNEL_DECODE, 1)
 
 
-@pytest.mark.parametrize("M,K,N", [(32, 4096, 4096), (17, 4096, 4096), (64, 4096, 4096), (32, 14336, 4096),
-                                   (16, 14336, 4096), (8, 14336, 4096)])
+@pytest.mark.parametrize("M,K,N", [(16, 14336, 4096), (8, 14336, 4096), (16, 14336, 2048), (1, 28672, 1024)])
 def test_decode_k_split(r9k, M, K, N):
     for packed in (False, True):
         kern, ks = r9k.gemm_fp8_block_plan(M, K, N, packed)
@@ -43,11 +43,20 @@ def test_decode_k_split(r9k, M, K, N):
         assert (K // 128) % ks == 0
 
 
-@pytest.mark.parametrize("M,K,N", [(64, 14336, 4096), (128, 4096, 4096), (255, 14336, 4096), (256, 4096, 4096),
-                                   (4096, 4096, 12288)])
+@pytest.mark.parametrize("M,K,N", [(256, 4096, 4096), (300, 4096, 4096), (4096, 4096, 12288)])
 def test_wide_shapes_go_tiled(r9k, M, K, N):
     kern, ks = r9k.gemm_fp8_block_plan(M, K, N)
     assert kern == r9k.KERNEL_TILED and ks >= 1
+
+
+@pytest.mark.parametrize("M,K,N", [(17, 4096, 4096), (32, 4096, 4096), (64, 4096, 4096), (128, 4096, 4096),
+                                   (255, 4096, 4096), (32, 14336, 4096), (64, 14336, 4096), (128, 14336, 4096),
+                                   (255, 14336, 4096), (48, 4096, 16384), (32, 4096, 65536)])
+def test_mid_widths_run_in_one_launch(r9k, M, K, N):
+    # 17 to 255 rows where the decode kernel would need a K split: the mid-width kernel, all of K per
+    # CTA, no partial sums and no reduction launch
+    for packed in (False, True):
+        assert r9k.gemm_fp8_block_plan(M, K, N, packed) == (r9k.KERNEL_MID, 1)
 
 
 def test_prefill_has_no_k_split(r9k):
@@ -66,8 +75,10 @@ def test_forced_engines(r9k):
         r9k.set_dispatch(0, r9k.ENGINE_AUTO)           # the skinny engine takes no width
         assert r9k.gemm_fp8_block_plan(1, 4096, 14336)[0] == r9k.KERNEL_TILED
         r9k.set_dispatch(255, r9k.ENGINE_SKINNY)
-        # a shape the decode kernel does not take stays on the skinny kernel
-        assert r9k.gemm_fp8_block_plan(200, 4096, 4096)[0] == r9k.KERNEL_SKINNY
+        # shapes the decode kernel does not take without a K split: the mid-width kernel up to 256 rows,
+        # the split-K skinny kernel above
+        assert r9k.gemm_fp8_block_plan(200, 4096, 4096)[0] == r9k.KERNEL_MID
+        assert r9k.gemm_fp8_block_plan(300, 4096, 4096)[0] == r9k.KERNEL_SKINNY
         assert r9k.gemm_fp8_block_plan(4, 4096, 4096)[0] == r9k.KERNEL_DECODE
     finally:
         r9k.set_dispatch(255, r9k.ENGINE_AUTO)
@@ -79,10 +90,12 @@ def test_workspace_covers_partials(r9k, M, K, N):
     ws = r9k.gemm_fp8_block_workspace(M, K, N)
     for packed in (False, True):
         kern, ks = r9k.gemm_fp8_block_plan(M, K, N, packed)
-        assert kern in (r9k.KERNEL_DECODE, r9k.KERNEL_SKINNY, r9k.KERNEL_TILED)
+        assert kern in (r9k.KERNEL_DECODE, r9k.KERNEL_SKINNY, r9k.KERNEL_TILED, r9k.KERNEL_MID)
         assert 1 <= ks <= K // 128
         if ks > 1:
             assert ws >= 4 * ks * M * N, (M, K, N, packed, ks, ws)
+        if kern in (r9k.KERNEL_MID, r9k.KERNEL_TILED):   # activation codes and scales, quantised once a call
+            assert ws >= M * K + 4 * M * (K // 128), (M, K, N, packed, ws)
 
 
 def test_plan_argument_checks(r9k):
@@ -96,11 +109,11 @@ def test_plan_argument_checks(r9k):
     assert L.r9k_gemm_fp8_block_plan(1, 4096, 4096, 2, byref(k), byref(s)) == -7
 
 
-@pytest.mark.parametrize("M,K,N", [(16, 4096, 151936), (8, 4096, 151936), (32, 4096, 65536), (48, 4096, 16384)])
+@pytest.mark.parametrize("M,K,N", [(16, 4096, 151936), (8, 4096, 151936), (16, 8192, 32768), (4, 16384, 65536)])
 def test_wide_n_goes_to_the_skinny_kernel(r9k, M, K, N):
-    # very wide outputs (an LM head over a large vocabulary) at decode widths: the decode kernel's
-    # every-CTA activation quant would be repeated across too many column tiles, so the skinny kernel,
-    # with its quant in the A-load (M <= 64), takes them
+    # very wide outputs (an LM head over a large vocabulary) at decode widths (up to 16 rows): the decode
+    # kernel's every-CTA activation quant would be repeated across too many column tiles, so the skinny
+    # kernel, with its quant in the A-load, takes them
     for packed in (False, True):
         kern, ks = r9k.gemm_fp8_block_plan(M, K, N, packed)
         assert kern == r9k.KERNEL_SKINNY and ks >= 1, (packed, kern, ks)
