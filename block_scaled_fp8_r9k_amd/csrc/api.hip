@@ -181,21 +181,10 @@ int run_gemm(const uint16_t *a, const uint8_t *aq, const float *as, int64_t M, i
         DecodeArgs d{a, aq, as, w, ws, c, M, K, N, packed, (float *)(base + L.part)};
         return launch_result(launch_gemm_decode(d, route.dc, s));
     }
-    if (route.kernel == R9K_KERNEL_MID) {
-        if (a) {  // quantise A once per call into the workspace, then run on codes
-            uint8_t *aq_w = base + L.aq;
-            float *as_w = (float *)(base + L.as);
-            rc = launch_result(launch_quant_act(a, M, K, aq_w, as_w, s));
-            if (rc) return rc;
-            aq = aq_w;
-            as = as_w;
-        }
-        MidArgs m{aq, as, w, ws, c, M, K, N, packed};
-        return launch_result(launch_gemm_mid(m, route.mc, s));
-    }
-    if (route.kernel == R9K_KERNEL_TILED) {
-        // the tiled engine reads codes and transposed scales [K/128][M] from
-        // the workspace: quantise A once per call, or transpose the caller's scales
+    if (route.kernel == R9K_KERNEL_TILED || route.kernel == R9K_KERNEL_MID) {
+        // the tiled and mid-width kernels read codes and transposed scales
+        // [K/128][M]: quantise A once per call into the workspace, or transpose
+        // the caller's scales there
         float *as_t = (float *)(base + L.as);
         if (a) {
             uint8_t *aq_w = base + L.aq;
@@ -205,6 +194,10 @@ int run_gemm(const uint16_t *a, const uint8_t *aq, const float *as, int64_t M, i
             rc = launch_result(launch_transpose_scales(as, M, K / 128, as_t, s));
         }
         if (rc) return rc;
+        if (route.kernel == R9K_KERNEL_MID) {
+            MidArgs m{aq, as_t, w, ws, c, M, K, N, packed};
+            return launch_result(launch_gemm_mid(m, route.mc, s));
+        }
         TiledArgs t{aq, as_t, w, ws, c, M, K, N, packed, (float *)(base + L.part), 1};
         return launch_result(launch_gemm_tiled(t, route.tp, s));
     }

@@ -17,7 +17,8 @@
 //   - weight fragments stream straight into registers (16-byte loads, fragment
 //     order or row-major), D steps ahead of their use;
 //   - activation codes come quantised (the fused entry point quantises once per
-//     call, like the tiled engine): with WN > 1 the CTA stages each step's
+//     call, like the tiled engine), with the scales transposed to [K/128][M] so
+//     that the 16 rows of a row tile read one line of scales: with WN > 1 the CTA stages each step's
 //     WK groups of its BM rows in LDS (loaded into registers D steps ahead,
 //     written to one of two LDS buffers, one barrier per step), shared by the WN
 //     column tiles; with WN = 1 nothing is shared and each wave loads its own
@@ -80,6 +81,7 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm_mid(MidArgs p) {
 
     const uint8_t *wtile = PK ? p.w + (n0 / 16) * G * 2048 + 16 * lane : p.w + (n0 + l16) * K + 16 * q;
     auto issue = [&](int64_t s, int slot) {
+        __builtin_amdgcn_sched_barrier(0);
         const int64_t g = s * WK + slice;
         if (PK) {
             wr[slot][0] = load_nt16(wtile + g * 2048);
@@ -106,7 +108,11 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm_mid(MidArgs p) {
             }
         }
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) sr[slot][mt] = p.as[arow[mt] * G + g];
+        for (int mt = 0; mt < MT; ++mt) sr[slot][mt] = p.as_t[g * M + arow[mt]];
+        // keep every step's loads in this order, in the prologue as in the loop, so
+        // that the waits the compiler derives for the loop hold from its first trip
+        // (reordered in the prologue, they forced a drain of the ring every D steps)
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     v4f acc[MT];

@@ -98,10 +98,10 @@ struct SkinnyArgs {
 hipError_t launch_gemm_skinny(const SkinnyArgs &args, const SkinnyCfg &cfg, hipStream_t s);
 
 // ---- mid widths, one launch over all of K (gemm_mid.hip) ----
-// Activations come quantised: codes [M][K] and scales [M][K/128] (row-major).
+// Activations come quantised: codes [M][K] and scales transposed, as_t [K/128][M].
 struct MidArgs {
     const uint8_t *aq;
-    const float *as;
+    const float *as_t;
     const uint8_t *w;   // weight codes, row-major or fragment-order (packed)
     const float *ws;
     uint16_t *c;
