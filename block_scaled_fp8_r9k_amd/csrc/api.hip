@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstdlib>
+#include <cstdio>
 #include <cstring>
 #include <mutex>
 
@@ -63,6 +64,9 @@ const Tuning &tuning() {
         t.skinny_ksplit = num("R9K_SKINNY_KSPLIT");
         t.bf16a_gs = (int)num("R9K_BF16A_GS");
         t.mid = getenv("R9K_MID") ? (int)num("R9K_MID") : -1;
+        if (const char *e = getenv("R9K_MID_CFG"))
+            if (sscanf(e, "%d,%d,%d,%d", &t.mid_cfg[0], &t.mid_cfg[1], &t.mid_cfg[2], &t.mid_cfg[3]) != 4)
+                t.mid_cfg[0] = 0;
     });
     return t;
 }
@@ -110,7 +114,7 @@ int engine_for(int64_t M) {
     return M <= g_skinny_max_m.load() ? R9K_ENGINE_SKINNY : R9K_ENGINE_TILED;
 }
 
-// GEMM workspace: [skinny split-K partials][A codes][A scales]
+// GEMM workspace: [split-K partials][A codes][A scales]
 struct GemmWs {
     size_t part, aq, as, total;
 };

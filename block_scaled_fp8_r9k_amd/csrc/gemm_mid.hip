@@ -7,7 +7,7 @@
 // column block, and the product of the two is large enough that splitting K
 // across CTAs means writing and re-reading fp32 partials of M x N.  Here a CTA
 // covers a BM x BN output block over all of K:
-//   - BM = 16 MT rows (MT row tiles of 16, up to 64 rows), BN = 16 WN columns;
+//   - BM = 16 MT rows (MT = 1, 2 or 4 row tiles of 16), BN = 16 WN columns;
 //     WN x WK waves, wave (ct, slice) owns column tile ct and the K-groups
 //     g = s WK + slice of steps s = 0 .. G/WK - 1; the WK slices of a column
 //     tile are summed through LDS at the end, in ascending slice order;
@@ -78,6 +78,7 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm_mid(MidArgs p) {
     // as plain vectors: as uint4 aggregates the staged copies stay in scratch memory
     u32x4 ar[D][ACH];
     float sr[D][MT];       // the activation scales of this lane's rows for its group of a step
+    float wsr[D];          // the weight block scale of a step's group (the same in every lane)
 
     const uint8_t *wtile = PK ? p.w + (n0 / 16) * G * 2048 + 16 * lane : p.w + (n0 + l16) * K + 16 * q;
     auto issue = [&](int64_t s, int slot) {
@@ -109,6 +110,7 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm_mid(MidArgs p) {
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) sr[slot][mt] = p.as_t[g * M + arow[mt]];
+        wsr[slot] = wsrow[g];  // a vector load of one address: it joins the ring instead of a scalar wait a step
         // keep every step's loads in this order, in the prologue as in the loop, so
         // that the waits the compiler derives for the loop hold from its first trip
         // (reordered in the prologue, they forced a drain of the ring every D steps)
@@ -134,22 +136,31 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm_mid(MidArgs p) {
             }
             __syncthreads();
         }
-        const float wsg = wsrow[s * WK + slice];
+        // all of the step's fragments first, then its MFMAs back to back, then the
+        // promotions: each MFMA then waits for no LDS read of its own, and each
+        // product is promoted MT - 1 MFMAs after it was issued
         const v8i wf = make_frag(wr[j][0], wr[j][1]);
+        v8i af[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            v8i af;
             if constexpr (ALDS) {
                 const uint8_t *ap = st + (slice * BM + 16 * mt + l16) * MID_PITCH + 16 * q;
-                af = make_frag(*(const uint4 *)ap, *(const uint4 *)(ap + 64));
+                af[mt] = make_frag(*(const uint4 *)ap, *(const uint4 *)(ap + 64));
             } else {
                 const u32x4 lo = ar[j][2 * mt], hi = ar[j][2 * mt + 1];
-                af = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                af[mt] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
             }
-            const v4f pr = mfma_e4m3_16x16x128(wf, af, zero);
-            const float sc = sr[j][mt] * wsg;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        v4f pr[MT];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[mt][i] = __builtin_fmaf(pr[i], sc, acc[mt][i]);
+        for (int mt = 0; mt < MT; ++mt) pr[mt] = mfma_e4m3_16x16x128(wf, af[mt], zero);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const float sc = sr[j][mt] * wsr[j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[mt][i] = __builtin_fmaf(pr[mt][i], sc, acc[mt][i]);
         }
     };
 
@@ -197,32 +208,61 @@ static size_t mid_lds(const MidCfg &c) {
     return std::max<size_t>(std::max(stages, red), 16);
 }
 
-// (mt, wn, wk, depth) for a shape.  Row tiles: enough for min(M, 64) rows; then
-// the widest column block (wn = 4, 2, 1) that still gives at least 256 CTAs,
-// eight waves a CTA (wk = 8 / wn, fewer where K/128 is not a multiple), and the
-// deepest load ring (4 steps; 2 where a wave loads its own four row tiles of
-// activations, for the register budget) that divides the step count.
+// Does (mt, wn, wk, depth) give a valid launch of this shape?
+static bool mid_fits(int64_t M, int64_t K, int64_t N, const MidCfg &c) {
+    const int64_t G = K / 128;
+    if (M < 1 || (c.mt != 1 && c.mt != 2 && c.mt != 4) || (c.wn != 1 && c.wn != 2 && c.wn != 4) || c.wk < 1 || c.wn * c.wk > 8)
+        return false;
+    if ((c.wk & (c.wk - 1)) || (c.depth != 1 && c.depth != 2 && c.depth != 4)) return false;
+    if (c.wn == 1 && c.mt > 2 && c.depth > 2) return false;  // direct fragments: 8 mt registers a step
+    if (c.wn > 1 && c.depth == 1) return false;              // two LDS buffers alternate by step parity
+    return N % (16 * c.wn) == 0 && G % c.wk == 0 && G / c.wk >= c.depth && (G / c.wk) % c.depth == 0;
+}
+
+// (mt, wn, wk, depth) for a shape.  The launch shapes that share activations
+// through LDS (two or four column tiles a CTA) ran fastest on the MI355X
+// (N = 4096, K = 4096 and 14336, M = 32 to 255): among row tiles mt = 4, 2, 1
+// and column tiles wn = 4, 2, the fewest CTAs that still give 256 (one per
+// compute unit), then the smallest BM + BN (the bytes a CTA reads per K), then
+// the wider column block; eight waves a CTA (wk = 8 / wn), and the deepest
+// load ring (4 steps, else 2) that divides the step count.  Where no such shape
+// gives 256 CTAs (narrow N), the shape with the most CTAs, also among the
+// one-column-tile shapes that load their activations per wave.
 MidCfg mid_config(int64_t M, int64_t K, int64_t N) {
     MidCfg c{0, 0, 0, 0};
     const int64_t G = K / 128;
     if (M < 1 || M > 256 || N % 16) return c;
-    const int mt = (int)std::min<int64_t>((M + 15) / 16, 4);
-    const int64_t nrb = (M + 16 * mt - 1) / (16 * mt);
-    for (int wn : {4, 2, 1}) {
-        if (N % (16 * wn)) continue;
-        if (wn > 1 && (N / (16 * wn)) * nrb < 256) continue;
-        for (int wk = 8 / wn; wk >= 1; wk /= 2) {
-            if (G % wk) continue;
-            const int64_t steps = G / wk;
-            for (int d : {4, 2, 1}) {
-                if (wn == 1 && mt > 2 && d > 2) continue;  // direct fragments: 8 mt registers a step
-                if (wn > 1 && d == 1) continue;             // two LDS buffers alternate by step parity
-                if (steps < d || steps % d) continue;
-                return MidCfg{mt, wn, wk, d};
+    const int *f = tuning().mid_cfg;  // tuning override
+    if (f[0] && mid_fits(M, K, N, MidCfg{f[0], f[1], f[2], f[3]})) return MidCfg{f[0], f[1], f[2], f[3]};
+    const int mtmax = (int)std::min<int64_t>((M + 15) / 16, 4);
+    MidCfg best{0, 0, 0, 0};
+    int64_t best_ctas = 0, best_edge = 0;
+    for (int mt : {4, 2, 1}) {
+        if (mt > mtmax && mt != 1) continue;
+        for (int wn : {4, 2, 1}) {
+            MidCfg t{0, 0, 0, 0};
+            for (int wk = 8 / wn; wk >= 1 && !t.mt; wk /= 2)
+                for (int d : {4, 2, 1})
+                    if (!t.mt && mid_fits(M, K, N, MidCfg{mt, wn, wk, d})) t = MidCfg{mt, wn, wk, d};
+            if (!t.mt) continue;
+            const int64_t ctas = ((M + 16 * mt - 1) / (16 * mt)) * (N / (16 * wn));
+            const int64_t edge = 16 * mt + 16 * wn;
+            bool better;
+            if (!best.mt) better = true;
+            else if ((best_ctas >= 256) != (ctas >= 256)) better = ctas >= 256;
+            else if (ctas >= 256 && ctas != best_ctas) better = ctas < best_ctas;
+            else if (ctas < 256 && ctas != best_ctas) better = ctas > best_ctas;
+            else if ((best.wn > 1) != (wn > 1)) better = wn > 1;
+            else if (edge != best_edge) better = edge < best_edge;
+            else better = wn > best.wn;
+            if (better) {
+                best = t;
+                best_ctas = ctas;
+                best_edge = edge;
             }
         }
     }
-    return c;
+    return best;
 }
 
 template <int MT, int WN, int WK, int D, bool PK>
@@ -278,7 +318,6 @@ static hipError_t launch_mid_mt(const MidArgs &a, const MidCfg &c, hipStream_t s
     switch (c.mt) {
         case 1: return launch_mid_wn<1, PK>(a, c, s);
         case 2: return launch_mid_wn<2, PK>(a, c, s);
-        case 3: return launch_mid_wn<3, PK>(a, c, s);
         case 4: return launch_mid_wn<4, PK>(a, c, s);
     }
     return hipErrorInvalidValue;

@@ -18,6 +18,7 @@ namespace r9k {
 //   R9K_SKINNY_KC, R9K_SKINNY_KSPLIT skinny kernel K batch and K split
 //   R9K_BF16A_GS                    bf16-activation variant: K-groups per wave
 //   R9K_MID                         mid-width kernel: 0 never, 1 wherever it fits (else the planner's choice)
+//   R9K_MID_CFG=mt,wn,wk,d          mid-width kernel launch shape (ignored where it does not fit)
 struct Tuning {
     int decode_wn, decode_wk;
     char tiled_cfg;
@@ -26,6 +27,7 @@ struct Tuning {
     long long skinny_ksplit;
     int bf16a_gs;
     int mid;  // -1: not set
+    int mid_cfg[4];
 };
 const Tuning &tuning();
 
