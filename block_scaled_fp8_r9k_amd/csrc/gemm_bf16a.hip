@@ -172,6 +172,8 @@ __global__ __launch_bounds__(NT) void k_gemm_bf16a(Bf16aArgs p, int wn, int wk) 
         for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(pr[i], wsg, acc[i]);
     }
 
+    pin_acc(acc);  // the MFMAs run with every lane enabled
+
     // 4. sum the K slices in ascending order, round, store: lane holds row
     // l16, columns n0 + 4q .. +3 (the reduction reuses the LDS)
     if (ALDS) __syncthreads();  // every wave is done reading the staged rows

@@ -206,6 +206,9 @@ __global__ __launch_bounds__(NT) void k_gemm_decode(DecodeArgs p, int wn, int wk
         }
     }
 
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) pin_acc(acc[mt]);  // the MFMAs run with every lane enabled
+
     // ---- sum the K slices in ascending order, round, store
     __syncthreads();                                   // every wave is done reading the codes
     v4f *red = (v4f *)lds;                             // [wave][MT][64 lanes]

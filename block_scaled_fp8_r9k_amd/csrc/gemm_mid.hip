@@ -177,6 +177,8 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm_mid(MidArgs p) {
     }
 #pragma unroll
     for (int j = 0; j < D; ++j) consume(s0 + j, j);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) pin_acc(acc[mt]);  // the last step's MFMAs run with every lane enabled
 
     // ---- sum the K slices in ascending order, round, store
     if constexpr (WK > 1) {

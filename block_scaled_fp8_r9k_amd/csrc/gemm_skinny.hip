@@ -164,6 +164,11 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(SkinnyArgs p, int ksplit, i
         }
     }
 
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) pin_acc(acc[mt][c]);  // the MFMAs run with every lane enabled
+
     // ---- epilogue
     // lane's outputs: rows m = m_base + 16 mt + l16, columns n = n_wave + 16 c + 4 q + i
     if (ksplit == 1) {

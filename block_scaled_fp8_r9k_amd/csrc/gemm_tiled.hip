@@ -329,6 +329,11 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_gemm_tiled(TiledArgs p) {
         for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(pr[k & 3][e], scp[j], acc[i][j][e]);
     }
 
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pin_acc(acc[i][j]);  // the MFMAs run with every lane enabled
+
     // lane holds, per tile (i, j), row m = m0 + 64 wm + 16 j + l16 and the four
     // columns n = n0 + TN 16 wn + 16 i + 4 q .. +3
     const int64_t nbase = n0 + TN * 16 * wn;

@@ -209,6 +209,8 @@ __global__ __launch_bounds__(256) void k_moe_gemm(MoeArgs p) {
             }
         }
 
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) pin_acc(acc[c]);  // the MFMAs run with every lane enabled
         // epilogue: lane holds rows (pairs) list[r0 + l16], columns 4q + i of each tile c
         if (l16 < rows) {
             const int64_t pr = list[r0 + l16];

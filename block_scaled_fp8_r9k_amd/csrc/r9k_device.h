@@ -152,6 +152,14 @@ __device__ __forceinline__ v4f mfma_e4m3_16x16x128(v8i a, v8i b, v4f c) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// Pin a value computed from MFMA results where it stands.  An MFMA mixes its
+// operands across the wave's lanes, so it must run with every lane enabled; a
+// value used only under a lane-dependent branch (a store of rows below M) lets
+// the compiler sink the MFMAs that feed it into that branch, where lanes are
+// disabled and their operands drop out of the other lanes' results.  An empty
+// asm that reads and writes the value makes it be computed first.
+__device__ __forceinline__ void pin_acc(v4f &x) { asm volatile("" : "+v"(x)); }
+
 __device__ __forceinline__ v8i make_frag(uint4 lo, uint4 hi) {
     v8i f;
     f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
