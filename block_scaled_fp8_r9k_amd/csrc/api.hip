@@ -160,14 +160,23 @@ GemmRoute route_gemm(int64_t M, int64_t K, int64_t N, bool packed) {
         r.kernel = R9K_KERNEL_DECODE;
         return r;
     }
-    if (mid != 0 && (M >= 17 || mid == 1)) {
+    // above 128 rows with long K the tiled engine's K split moves fewer bytes than
+    // the mid-width kernel's all-K CTAs (measured at N = 4096, K = 14336: 255 rows
+    // 40 against 44 us; 128 rows within 3%)
+    const bool long_k_wide = M > 128 && K >= 8192;
+    if (mid != 0 && ((M >= 17 && !long_k_wide) || mid == 1)) {
         r.mc = mid_config(M, K, N);
         if (r.mc.mt) {
             r.kernel = R9K_KERNEL_MID;
             return r;
         }
     }
-    if (r.dc.wn) r.kernel = R9K_KERNEL_DECODE;
+    if (r.dc.wn) {
+        r.kernel = R9K_KERNEL_DECODE;
+    } else if (long_k_wide && g_engine.load() == R9K_ENGINE_AUTO) {
+        r.kernel = R9K_KERNEL_TILED;
+        r.tp = tiled_plan(M, K, N);
+    }
     return r;
 }
 

@@ -43,7 +43,8 @@ def test_decode_k_split(r9k, M, K, N):
         assert (K // 128) % ks == 0
 
 
-@pytest.mark.parametrize("M,K,N", [(256, 4096, 4096), (300, 4096, 4096), (4096, 4096, 12288)])
+@pytest.mark.parametrize("M,K,N", [(256, 4096, 4096), (300, 4096, 4096), (4096, 4096, 12288), (255, 14336, 4096),
+                                   (129, 8192, 4096)])
 def test_wide_shapes_go_tiled(r9k, M, K, N):
     kern, ks = r9k.gemm_fp8_block_plan(M, K, N)
     assert kern == r9k.KERNEL_TILED and ks >= 1
@@ -51,7 +52,7 @@ def test_wide_shapes_go_tiled(r9k, M, K, N):
 
 @pytest.mark.parametrize("M,K,N", [(17, 4096, 4096), (32, 4096, 4096), (64, 4096, 4096), (128, 4096, 4096),
                                    (255, 4096, 4096), (32, 14336, 4096), (64, 14336, 4096), (128, 14336, 4096),
-                                   (255, 14336, 4096), (48, 4096, 16384), (32, 4096, 65536)])
+                                   (48, 4096, 16384), (32, 4096, 65536)])
 def test_mid_widths_run_in_one_launch(r9k, M, K, N):
     # 17 to 255 rows where the decode kernel would need a K split: the mid-width kernel, all of K per
     # CTA, no partial sums and no reduction launch
