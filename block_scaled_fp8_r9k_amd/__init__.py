@@ -20,7 +20,7 @@ from ctypes import POINTER, c_char_p, c_int, c_int64, c_size_t, c_void_p
 
 import torch
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 ENGINE_AUTO, ENGINE_SKINNY, ENGINE_TILED = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.r9k_gemm_fp8_block_bf16a.argtypes = [c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_int64, c_void_p,
                                                c_void_p]
         L.r9k_gemm_fp8_block_bf16a_packed.argtypes = L.r9k_gemm_fp8_block_bf16a.argtypes
+        L.r9k_gemm_fp8_block_qa_noalloc.argtypes = [c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_int64,
+                                                    c_void_p, c_int, c_void_p]
         v = L.r9k_abi_version()
         if v != ABI_VERSION:
             raise ImportError(f"libr9k.so has ABI version {v}, this binding needs {ABI_VERSION}")
@@ -217,6 +219,25 @@ def gemm_fp8_block_qa(a, w, ws, c=None, workspace=None, stream=None) -> torch.Te
     _check(lib().r9k_gemm_fp8_block_qa(_ptr(a, BF16, "a"), M, K, _ptr(w, FP8, "w"), _ptr(ws, F32, "ws"), N,
                                        _ptr(c, BF16, "c"), _ptr(wsb, FP8, "workspace"), wsb.numel(),
                                        _stream(stream)), "r9k_gemm_fp8_block_qa")
+    return c
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def gemm_fp8_block_qa_noalloc(a, w, ws, c=None, packed: bool = False, stream=None) -> torch.Tensor:
+    """The fused GEMM without a workspace (r9k_gemm_fp8_block_qa_noalloc): the library's own scratch on
+    this GPU, no device allocation in the call (pass c to avoid torch's output allocation too).  Calls on
+    one GPU must not overlap in time."""
+    M, K = a.shape
+    N = w.shape[0]
+    if c is None:
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    if M == 0:  # an empty batch: nothing to compute (an empty tensor has no device address to pass)
+        return c
+    _check(lib().r9k_gemm_fp8_block_qa_noalloc(_ptr(a, BF16, "a"), M, K, _ptr(w, FP8, "w"), _ptr(ws, F32, "ws"), N,
+                                               _ptr(c, BF16, "c"), 1 if packed else 0, _stream(stream)),
+           "r9k_gemm_fp8_block_qa_noalloc")
     return c
 
 

@@ -229,6 +229,37 @@ int run_gemm(const uint16_t *a, const uint8_t *aq, const float *as, int64_t M, i
     return launch_result(launch_gemm_skinny(sa, cfg, s));
 }
 
+// ---- the allocation-free entry point's scratch -------------------------------
+// A file-scope device array that stands in for the workspace of
+// r9k_gemm_fp8_block_qa_noalloc.  In host code its name is a host-side
+// stand-in, not a device address: the address is taken once per device with
+// hipGetSymbolAddress (that device current) and only that pointer is used.
+constexpr size_t SCRATCH_BYTES = R9K_NOALLOC_SCRATCH_BYTES;
+static_assert(SCRATCH_BYTES % 256 == 0, "scratch size");
+__device__ __align__(256) uint8_t scratch[SCRATCH_BYTES];
+std::once_flag g_scratch_once[MAX_DEV];
+void *g_scratch_ptr[MAX_DEV];
+hipError_t g_scratch_err[MAX_DEV];
+
+int scratch_for_current_device(void **ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEV) {
+        (void)hipGetLastError();
+        return R9K_ERR_DEVICE;
+    }
+    std::call_once(g_scratch_once[dev], [dev] {
+        void *p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+    });
+    if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev]) {
+        (void)hipGetLastError();
+        return R9K_ERR_DEVICE;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return R9K_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -318,6 +349,21 @@ int r9k_gemm_fp8_block_qa_packed(const uint16_t *a, int64_t M, int64_t K, const 
     if (!aligned16(a) || !aligned16(wp) || !aligned16(ws) || !aligned16(c) || !aligned16(workspace))
         return R9K_ERR_ALIGN;
     return run_gemm(a, nullptr, nullptr, M, K, wp, ws, N, c, workspace, ws_bytes, (hipStream_t)stream, true);
+}
+
+int r9k_gemm_fp8_block_qa_noalloc(const uint16_t *a, int64_t M, int64_t K, const uint8_t *w, const float *ws,
+                                  int64_t N, uint16_t *c, int packed, void *stream) {
+    if (!a || !w || !ws || !c) return R9K_ERR_NULLPTR;
+    if (int rc = check_gemm_shape(M, K, N)) return rc;
+    if (packed != 0 && packed != 1) return R9K_ERR_ARG;
+    if (!aligned16(a) || !aligned16(w) || !aligned16(ws) || !aligned16(c)) return R9K_ERR_ALIGN;
+    if (M == 0) return R9K_OK;
+    const size_t need = gemm_ws(M, K, N).total;
+    if (need > SCRATCH_BYTES) return R9K_ERR_WORKSPACE;  // beyond the fixed scratch: use r9k_gemm_fp8_block_qa
+    if (int rc = check_device()) return rc;
+    void *ptr = nullptr;
+    if (int rc = scratch_for_current_device(&ptr)) return rc;
+    return run_gemm(a, nullptr, nullptr, M, K, w, ws, N, c, ptr, SCRATCH_BYTES, (hipStream_t)stream, packed == 1);
 }
 
 static int run_bf16a(const uint16_t *a, int64_t M, int64_t K, const uint8_t *w, const float *ws, int64_t N,

@@ -232,7 +232,6 @@ static bool mid_fits(int64_t M, int64_t K, int64_t N, const MidCfg &c) {
 // one-column-tile shapes that load their activations per wave.
 MidCfg mid_config(int64_t M, int64_t K, int64_t N) {
     MidCfg c{0, 0, 0, 0};
-    const int64_t G = K / 128;
     if (M < 1 || M > 256 || N % 16) return c;
     const int *f = tuning().mid_cfg;  // tuning override
     if (f[0] && mid_fits(M, K, N, MidCfg{f[0], f[1], f[2], f[3]})) return MidCfg{f[0], f[1], f[2], f[3]};

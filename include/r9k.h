@@ -60,7 +60,7 @@ extern "C" {
 #pragma GCC visibility push(default)
 #endif
 
-#define R9K_ABI_VERSION 6
+#define R9K_ABI_VERSION 7
 
 /* Return codes: 0 or negative, as the pages' kernels return them (release
  * v0.3.0, its validation record: a test failing "with the kernel's -7").
@@ -76,7 +76,7 @@ extern "C" {
 
 /* The ABI version this library implements (R9K_ABI_VERSION; 4 added the MoE
  * routing and the shared-expert fold, 5 the bf16-activation variant, 6 the
- * mid-width kernel in the plan query).  Callers refuse
+ * mid-width kernel in the plan query, 7 the allocation-free GEMM entry point).  Callers refuse
  * a library whose version differs from the header they were built against:
  * the convention of the pages' plugin, which refuses an older libr9k.so
  * (release v0.2.2, "Upgrading").  Host only; cannot fail. */
@@ -150,6 +150,25 @@ int r9k_gemm_fp8_block(const uint8_t *aq, const float *as, int64_t M, int64_t K,
  * Errors: as r9k_gemm_fp8_block. */
 int r9k_gemm_fp8_block_qa(const uint16_t *a, int64_t M, int64_t K, const uint8_t *w, const float *ws,
                           int64_t N, uint16_t *c, void *workspace, size_t ws_bytes, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the fused
+ * GEMM r9k_gemm_fp8_block_qa (packed = 0) or r9k_gemm_fp8_block_qa_packed
+ * (packed = 1) with the same arguments and result bits, but no workspace
+ * argument.  Its scratch is a device array inside the library, of
+ * R9K_NOALLOC_SCRATCH_BYTES on each GPU the call runs on, held until the
+ * process ends; the call allocates nothing (no hipMalloc, no library
+ * allocation).  Shapes whose workspace (r9k_gemm_fp8_block_workspace) exceeds
+ * that size are rejected.  Every call on one GPU shares the one array and
+ * leaves its contents behind (nothing in it needs to start at zero): calls on
+ * one GPU that overlap in time, on different streams or threads, race and give
+ * wrong results; order them (one stream, or events).
+ * Errors: NULLPTR; SHAPE as r9k_gemm_fp8_block_qa; ARG if packed is not 0 or 1;
+ * ALIGN; WORKSPACE if the shape needs more than R9K_NOALLOC_SCRATCH_BYTES;
+ * DEVICE (also if the scratch's address cannot be taken); LAUNCH. */
+#define R9K_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int r9k_gemm_fp8_block_qa_noalloc(const uint16_t *a, int64_t M, int64_t K, const uint8_t *w, const float *ws,
+                                  int64_t N, uint16_t *c, int packed, void *stream);
 
 /* Fragment-order weights.  The r9700-stack release v0.3.1 notes ("What
  * changed for someone running it") keep fragment-order copies of the fp8

@@ -203,3 +203,18 @@ def test_binding_refuses_host_tensors():
     import block_scaled_fp8_r9k_amd as r9k
     with pytest.raises(ValueError):
         r9k.quant_act(torch.zeros((1, 128), dtype=torch.bfloat16))
+
+
+def test_noalloc_checks(L):
+    # the allocation-free entry point's host checks, before any device is touched
+    f = L.r9k_gemm_fp8_block_qa_noalloc
+    assert f(NUL, 1, 128, B16, C16, 128, A16, 0, S) == -1
+    assert f(A16, 1, 130, B16, C16, 128, A16, 0, S) == -2
+    assert f(A16, 1, 128, B16, C16, 128, A16, 2, S) == -7
+    assert f(ODD, 1, 128, B16, C16, 128, A16, 0, S) == -3
+    assert f(A16, 0, 128, B16, C16, 128, A16, 0, S) == 0           # M == 0: nothing to do
+    d = _defines()
+    assert "R9K_NOALLOC_SCRATCH_BYTES" not in d or d["R9K_NOALLOC_SCRATCH_BYTES"] > 0
+    rc, need = _ws(L, 8192, 8192, 1024)
+    assert rc == 0 and need > 64 << 20                             # beyond the scratch: refused
+    assert f(A16, 8192, 8192, B16, C16, 1024, A16, 0, S) == -6
