@@ -27,9 +27,15 @@ The same line carries:
   moe           16 tokens, hidden 2048, 128 experts of 768, top-8: GB/s over
                 the bytes of the experts the routing touches, plus the
                 routing kernel and the fused path with a shared expert;
+  single_token  M=1, K=512, N=1024 (seed 0, no outliers): microseconds a call;
   bf16a         the decode sweep on the bf16-activation variant (no quant).
+Every leg's GPU time is the median of TRIALS (3) timed trials, each over many
+launches, with the trials listed; prefill, mid, moe and single_token each carry
+a `cpu_baseline` of their own (the oracle on the leg's workload, or a stated
+sample of it, median of up to 3 runs).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only decode,prefill,mid,moe,bf16a]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+                       [--only decode,prefill,mid,moe,single_token,bf16a]
                        [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -51,6 +57,7 @@ FP8_PEAK_TFLOPS = 5033.2        # 256 CU x 2.4 GHz x 8192 flop/CU/clk, dense fp8
 DECODE_M = (1, 2, 4, 8, 16)
 DECODE_K, DECODE_N = 4096, 14336
 ROTATE_BYTES = 512 << 20
+TRIALS = 3
 
 
 def log(*a):
@@ -78,6 +85,22 @@ class Timer:
         e.record()
         e.synchronize()
         return s.elapsed_time(e) / reps  # ms
+
+
+def median_of_trials(run_once, n=TRIALS):
+    """Median of n timed trials (run_once() -> ms) and the trials themselves."""
+    t = [run_once() for _ in range(n)]
+    return float(np.median(t)), t
+
+
+def cpu_seconds(fn, budget_s=10.0, max_runs=3):
+    """Median wall time of up to max_runs calls of fn, stopping once budget_s is spent."""
+    times = []
+    while len(times) < max_runs and sum(times) < budget_s:
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+    return float(np.median(times)), len(times)
 
 
 def capture(torch, calls):
@@ -207,9 +230,9 @@ def bench_decode(torch, r9k, inputs, dev, steps, warmup, packed=True):
         reps_per_graph = 2 * C
         g = capture(torch, [call(M, i % C) for i in range(reps_per_graph)])
         tm.run(lambda i: g.replay(), 2)
-        ms = tm.run(lambda i: g.replay(), max(3, steps // 4)) / reps_per_graph
+        ms, tr = median_of_trials(lambda: tm.run(lambda i: g.replay(), max(3, steps // 4)) / reps_per_graph)
         b = gemm_bytes(M, K, N)
-        per_m[M] = dict(us=ms * 1e3, GBs=b / (ms * 1e-3) / 1e9)
+        per_m[M] = dict(us=ms * 1e3, GBs=b / (ms * 1e-3) / 1e9, trials_us=[t * 1e3 for t in tr])
         log(f"decode M={M}: {ms * 1e3:.2f} us/launch, {per_m[M]['GBs']:.0f} GB/s")
     del step_graphs, block_graph, copies
     torch.cuda.empty_cache()
@@ -238,8 +261,8 @@ def bench_bf16a(torch, r9k, inputs, dev, reps):
         g = capture(torch, calls)
         tm = Timer(torch)
         tm.run(lambda i: g.replay(), 2)
-        ms = tm.run(lambda i: g.replay(), reps) / len(calls)
-        res[str(M)] = dict(us=ms * 1e3, GBs=gemm_bytes(M, K, N) / (ms * 1e-3) / 1e9)
+        ms, tr = median_of_trials(lambda: tm.run(lambda i: g.replay(), reps) / len(calls))
+        res[str(M)] = dict(us=ms * 1e3, GBs=gemm_bytes(M, K, N) / (ms * 1e-3) / 1e9, trials_us=[t * 1e3 for t in tr])
         log(f"bf16a M={M}: {ms * 1e3:.2f} us/launch, {res[str(M)]['GBs']:.0f} GB/s")
     del copies
     torch.cuda.empty_cache()
@@ -290,14 +313,15 @@ def bench_prefill(torch, r9k, inputs, dev, reps):
     gk = capture(torch, kcalls)
     # The kernel's time rises by up to a fifth over its first few dozen launches
     # as the GPU heats, so both graphs first run back to back until the GPU is
-    # warm; then each is timed over `reps` back-to-back replays, twice, in
-    # alternation, and the two timings of each are averaged.
+    # warm; then each is timed over `reps` back-to-back replays, TRIALS times,
+    # in alternation, and the median of each is taken.
     tm = Timer(torch)
     tm.run(lambda i: (g if i % 2 else gk).replay(), 8)
-    ms = kms = 0.0
-    for _ in range(2):
-        ms += tm.run(lambda i: g.replay(), reps) / C / 2
-        kms += tm.run(lambda i: gk.replay(), reps) / C / 2
+    tr, ktr = [], []
+    for _ in range(TRIALS):
+        tr.append(tm.run(lambda i: g.replay(), reps) / C)
+        ktr.append(tm.run(lambda i: gk.replay(), reps) / C)
+    ms, kms = float(np.median(tr)), float(np.median(ktr))
     tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
     ktf = 2.0 * M * N * K / (kms * 1e-3) / 1e12
     log(f"prefill {M}x{K}x{N}: {ms * 1e3:.1f} us, {tflops:.0f} TFLOP/s")
@@ -307,7 +331,12 @@ def bench_prefill(torch, r9k, inputs, dev, reps):
                 kernel="k_gemm_tiled (256 x 256 tile, fragment-order weights) with the scale transpose, per call",
                 flops_per_launch=2.0 * M * N * K, us_per_launch=kms * 1e3)
     return dict(workload=f"M={M}, K={K}, N={N}, fused act quant, fragment-order weights", us=ms * 1e3,
-                value=tflops, unit="TFLOP/s", peak=FP8_PEAK_TFLOPS, frac=tflops / FP8_PEAK_TFLOPS, roofline=roof)
+                value=tflops, unit="TFLOP/s", peak=FP8_PEAK_TFLOPS, frac=tflops / FP8_PEAK_TFLOPS, roofline=roof,
+                trials_us=[t * 1e3 for t in tr], codes_trials_us=[t * 1e3 for t in ktr],
+                fused_over_codes=ms / kms)
+
+
+KERNEL_NAMES = {1: "decode", 2: "skinny", 3: "tiled", 4: "mid"}
 
 
 def bench_mid(torch, r9k, inputs, dev, reps):
@@ -329,11 +358,13 @@ def bench_mid(torch, r9k, inputs, dev, reps):
             g = capture(torch, calls)
             tm = Timer(torch)
             tm.run(lambda i: g.replay(), 1)
-            ms = tm.run(lambda i: g.replay(), reps) / C
+            ms, tr = median_of_trials(lambda: tm.run(lambda i: g.replay(), reps) / C)
             gbs = gemm_bytes(M, K, N) / (ms * 1e-3) / 1e9
             tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
             log(f"mid M={M} K={K} N={N}: {ms * 1e3:.2f} us, {gbs:.0f} GB/s, {tf:.0f} TFLOP/s")
-            res.append(dict(M=M, K=K, N=N, us=ms * 1e3, GBs=gbs, hbm_frac=gbs / HBM_PEAK_GBS, TFLOPs=tf))
+            res.append(dict(M=M, K=K, N=N, us=ms * 1e3, GBs=gbs, hbm_frac=gbs / HBM_PEAK_GBS, TFLOPs=tf,
+                            kernel=KERNEL_NAMES.get(r9k.gemm_fp8_block_plan(M, K, N, True)[0]),
+                            trials_us=[t * 1e3 for t in tr]))
         del copies
         torch.cuda.empty_cache()
     return res
@@ -342,12 +373,12 @@ def bench_mid(torch, r9k, inputs, dev, reps):
 def bench_moe(torch, r9k, inputs, dev, reps):
     T, H, E, I, k = 16, 2048, 128, 768, 8
     x, logits, w13, w2 = inputs.moe_inputs(0, T, H, E, I)
+    host = dict(x=x, logits=logits, k=k, H=H, I=I, E=E, w13=w13, w2=w2)
     logits_d = torch.from_numpy(logits).cuda()
     ids_d, tw_d = r9k.moe_route(logits_d, k)  # the library's one-launch routing
     ids = ids_d.cpu().numpy()
     q13, s13 = r9k.quant_weight(dev(w13.reshape(E * 2 * I, H)))
     q2, s2 = r9k.quant_weight(dev(w2.reshape(E * H, I)))
-    del w13, w2
     # fragment-order expert weights (packed once at load, not timed)
     q13 = r9k.pack_weight(q13)
     q2 = r9k.pack_weight(q2)
@@ -365,7 +396,8 @@ def bench_moe(torch, r9k, inputs, dev, reps):
     g = capture(torch, rcalls)
     tm = Timer(torch)
     tm.run(lambda i: g.replay(), 1)
-    res["route"] = dict(us=tm.run(lambda i: g.replay(), reps) / len(rcalls) * 1e3, T=T, E=E, topk=k)
+    ms, tr = median_of_trials(lambda: tm.run(lambda i: g.replay(), reps) / len(rcalls))
+    res["route"] = dict(us=ms * 1e3, T=T, E=E, topk=k, trials_us=[t * 1e3 for t in tr])
     log(f"moe route T={T} E={E} top-{k}: {res['route']['us']:.2f} us")
     for fused in (True, False):
         calls = [lambda s=s: r9k.moe_fp8_decode(x_d, ids_d, tw_d, s[0].view(E, 2 * I, H),
@@ -377,10 +409,11 @@ def bench_moe(torch, r9k, inputs, dev, reps):
         g = capture(torch, calls)
         tm = Timer(torch)
         tm.run(lambda i: g.replay(), 1)
-        ms = tm.run(lambda i: g.replay(), reps) / len(sets)
+        ms, tr = median_of_trials(lambda: tm.run(lambda i: g.replay(), reps) / len(sets))
         gbs = nbytes / (ms * 1e-3) / 1e9
         log(f"moe fused={fused}: {ms * 1e3:.1f} us, {gbs:.0f} GB/s over {touched} touched experts")
-        res["fused" if fused else "three_launch"] = dict(us=ms * 1e3, GBs=gbs, hbm_frac=gbs / HBM_PEAK_GBS)
+        res["fused" if fused else "three_launch"] = dict(us=ms * 1e3, GBs=gbs, hbm_frac=gbs / HBM_PEAK_GBS,
+                                                         trials_us=[t * 1e3 for t in tr])
     # the fused path with the shared expert's term folded into the combine
     calls = [lambda s=s: r9k.moe_fp8_decode(x_d, ids_d, tw_d, s[0].view(E, 2 * I, H),
                                             s[1].view(E, 2 * I // 128, H // 128), s[2].view(E, H, I),
@@ -391,11 +424,99 @@ def bench_moe(torch, r9k, inputs, dev, reps):
     g = capture(torch, calls)
     tm = Timer(torch)
     tm.run(lambda i: g.replay(), 1)
-    ms = tm.run(lambda i: g.replay(), reps) / len(sets)
-    res["fused_shared"] = dict(us=ms * 1e3, GBs=nbytes / (ms * 1e-3) / 1e9)
+    ms, tr = median_of_trials(lambda: tm.run(lambda i: g.replay(), reps) / len(sets))
+    res["fused_shared"] = dict(us=ms * 1e3, GBs=nbytes / (ms * 1e-3) / 1e9, trials_us=[t * 1e3 for t in tr])
     log(f"moe fused with the shared expert's term: {ms * 1e3:.1f} us")
     res.update(workload=f"T={T}, H={H}, E={E}, I={I}, top-{k}", touched_experts=touched, bytes=nbytes)
-    return res
+    host["nbytes"] = nbytes
+    return res, host
+
+
+def bench_single_token(torch, r9k, inputs, dev, reps):
+    """The single decode token: A 1x512 (N(0,1), no outliers), W 1024x512, seed 0,
+    row-major weights, fused act quant.  Everything sits in cache; this is the
+    call's latency, in a graph of back-to-back calls and as eager calls."""
+    M, K, N = 1, 512, 1024
+    a = dev(inputs.activations(0, M, K, outliers=False))
+    wq, ws = r9k.quant_weight(dev(inputs.weights(0, N, K)))
+    wsp = torch.zeros(max(r9k.gemm_fp8_block_workspace(M, K, N), 256), dtype=torch.uint8, device="cuda")
+    c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    one = lambda: r9k.gemm_fp8_block_qa(a, wq, ws, c=c, workspace=wsp)
+    one()
+    calls = [one] * 50
+    g = capture(torch, calls)
+    tm = Timer(torch)
+    tm.run(lambda i: g.replay(), 2)
+    ms, tr = median_of_trials(lambda: tm.run(lambda i: g.replay(), reps) / len(calls))
+    ems, etr = median_of_trials(lambda: tm.run(lambda i: one(), 200))
+    log(f"single token {M}x{K}x{N}: {ms * 1e3:.2f} us a call in a graph, {ems * 1e3:.2f} us eager")
+    return dict(workload=f"M={M}, K={K}, N={N}, seed 0, fused act quant, row-major weights", us=ms * 1e3,
+                eager_us=ems * 1e3, trials_us=[t * 1e3 for t in tr], eager_trials_us=[t * 1e3 for t in etr],
+                kernel=KERNEL_NAMES.get(r9k.gemm_fp8_block_plan(M, K, N)[0]))
+
+
+# ---- the oracle beside each leg (CPU, the box's host cores) ----
+
+def cpu_prefill(ora, inputs, rows=128):
+    M, K, N = 4096, 4096, 12288
+    a = inputs.activations(1, M, K, outliers=True)[:rows]
+    wq, ws = ora.quant_weight(inputs.weights(1, N, K))
+    t, n = cpu_seconds(lambda: ora.gemm_block_qa(a, wq, ws))
+    return dict(value=2.0 * rows * K * N / t / 1e12, unit="TFLOP/s", cores=ora.threads(), kind="oracle",
+                seconds=t, repeats=n,
+                sample=f"the first {rows} of the {M} rows (K={K}, N={N}): oracle act quant + exact block GEMM, "
+                       f"weight quant not timed; TFLOP/s of the sample")
+
+
+def cpu_mid(ora, inputs):
+    M, K, N = 255, 4096, 4096
+    a = inputs.activations(2, 255, K, outliers=True)
+    wq, ws = ora.quant_weight(inputs.weights(2, N, K))
+    t, n = cpu_seconds(lambda: ora.gemm_block_qa(a, wq, ws))
+    return dict(value=gemm_bytes(M, K, N) / t / 1e9, unit="GB/s", tflops=2.0 * M * K * N / t / 1e12,
+                cores=ora.threads(), kind="oracle", seconds=t, repeats=n,
+                sample=f"the M={M}, K={K}, N={N} point in full: oracle act quant + exact block GEMM, weight "
+                       f"quant not timed; GB/s of the same algorithmic bytes as the GPU figure")
+
+
+def moe_oracle_args(ora, host):
+    """The oracle's MoE decode arguments for the workload: routed by the oracle, with
+    only the experts the routing touches quantised (by the oracle) and the ids
+    renumbered into that compact set; the other experts are never read."""
+    x, logits, k = host["x"], host["logits"], host["k"]
+    H = x.shape[1]
+    E, I = host["E"], host["I"]
+    ids, w = ora.moe_route(logits, k)
+    touched = np.unique(ids)
+    remap = np.full(E, -1, np.int64)
+    remap[touched] = np.arange(len(touched))
+    w13, w2 = host["w13"][touched], host["w2"][touched]
+    q13, s13 = ora.quant_weight(w13.reshape(-1, H))
+    q2, s2 = ora.quant_weight(w2.reshape(-1, I))
+    Et = len(touched)
+    return (x, remap[ids].astype(ids.dtype), w, q13.reshape(Et, 2 * I, H), s13.reshape(Et, 2 * I // 128, H // 128),
+            q2.reshape(Et, H, I), s2.reshape(Et, H // 128, I // 128))
+
+
+def cpu_moe(ora, host):
+    x, k = host["x"], host["k"]
+    T = x.shape[0]
+    args = moe_oracle_args(ora, host)  # setup, not timed
+    Et = args[3].shape[0]
+    t, n = cpu_seconds(lambda: ora.moe_decode(*args))
+    return dict(value=host["nbytes"] / t / 1e9, unit="GB/s", cores=ora.threads(), kind="oracle", seconds=t,
+                repeats=n, sample=f"the workload in full (T={T}, top-{k}, the {Et} touched experts): oracle "
+                                  f"gate_up + silu*up + row quant + down + weighted sum, routing and weight quant "
+                                  f"not timed; GB/s over the same bytes as the GPU figure")
+
+
+def cpu_single_token(ora, inputs):
+    M, K, N = 1, 512, 1024
+    a = inputs.activations(0, M, K, outliers=False)
+    wq, ws = ora.quant_weight(inputs.weights(0, N, K))
+    t, n = cpu_seconds(lambda: ora.gemm_block_qa(a, wq, ws), max_runs=20)
+    return dict(value=t * 1e6, unit="us", cores=ora.threads(), kind="oracle", repeats=n,
+                sample=f"the M={M}, K={K}, N={N} call in full (weight quant not timed)")
 
 
 def copy_bandwidth(torch):
@@ -415,7 +536,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--only", default="decode,prefill,mid,moe,bf16a")
+    ap.add_argument("--only", default="decode,prefill,mid,moe,single_token,bf16a")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -462,14 +583,29 @@ def main():
             log("cpu baseline (oracle) ...")
             line["cpu_baseline"] = cpu_baseline(oracle, d["a_bits"], d["w_bits"], d["step_bytes"])
     reps = max(5, args.steps // 20)
+    moe_host = None
     if "prefill" in which:
         line["prefill"] = bench_prefill(torch, r9k, inputs, dev, reps)
     if "mid" in which:
-        line["mid"] = bench_mid(torch, r9k, inputs, dev, reps)
+        line["mid"] = dict(points=bench_mid(torch, r9k, inputs, dev, reps))
     if "moe" in which:
-        line["moe"] = bench_moe(torch, r9k, inputs, dev, reps)
+        line["moe"], moe_host = bench_moe(torch, r9k, inputs, dev, reps)
+    if "single_token" in which:
+        line["single_token"] = bench_single_token(torch, r9k, inputs, dev, reps)
     if "bf16a" in which:
         line["bf16a"] = bench_bf16a(torch, r9k, inputs, dev, reps)
+    if not args.no_cpu_baseline:
+        import oracle
+        log("cpu baselines of the other legs (oracle) ...")
+        if "prefill" in which:
+            line["prefill"]["cpu_baseline"] = cpu_prefill(oracle, inputs)
+        if "mid" in which:
+            line["mid"]["cpu_baseline"] = cpu_mid(oracle, inputs)
+        if "moe" in which:
+            line["moe"]["cpu_baseline"] = cpu_moe(oracle, moe_host)
+        if "single_token" in which:
+            line["single_token"]["cpu_baseline"] = cpu_single_token(oracle, inputs)
+    moe_host = None
     line["copy_GBs_context"] = copy_bandwidth(torch)
     line["kernel_source_hash"] = kernel_source_hash()
     print(json.dumps(line), flush=True)

@@ -121,9 +121,10 @@ int r9k_encode_e4m3(const float *x, int64_t n, uint8_t *codes, void *stream);
  * above the decode widths quantise their activations).  0 for M = 0.
  * Host only; touches no device.
  * The workspace holds the activation codes and scales of a call that
- * quantises once before the GEMM, and the fp32 split-K partial sums of the
- * skinny engine; every call writes what it reads, so the contents need no
- * initialisation.  Calls that share a workspace must not overlap in time
+ * quantises once before the GEMM (or the transposed scales the tiled and
+ * mid-width kernels read), and the fp32 partial sums of a K split (decode,
+ * skinny and tiled kernels); every call writes what it reads, so the contents
+ * need no initialisation.  Calls that share a workspace must not overlap in time
  * (same stream, or ordered by events).
  * Errors: NULLPTR (bytes); SHAPE as for the GEMM. */
 int r9k_gemm_fp8_block_workspace(int64_t M, int64_t K, int64_t N, size_t *bytes);
@@ -144,8 +145,18 @@ int r9k_gemm_fp8_block(const uint8_t *aq, const float *as, int64_t M, int64_t K,
  * bit-identical to r9k_quant_act; the result is bit-identical to
  * r9k_quant_act followed by r9k_gemm_fp8_block under the same dispatch.
  * The dispatcher picks the engine by M (release v0.3.2: the decode kernels to
- * 255 rows, the tiled GEMMs above): M <= skinny_max_m -> the weight-streaming
- * skinny engine, else the LDS-tiled MFMA engine.
+ * 255 rows, the tiled GEMMs above).  Under R9K_ENGINE_AUTO:
+ *   M > skinny_max_m (default 255)       -> the LDS-tiled MFMA engine;
+ *   else, where the decode kernel covers all of K in each CTA (up to 64 rows,
+ *   enough column tiles to fill the chip) -> the decode kernel, with the
+ *   activation quant in its A-load, one launch;
+ *   else from 17 rows on, unless M > 128 and K >= 8192 -> the mid-width
+ *   kernel (all of K per CTA, on activations quantised once per call: a quant
+ *   launch, then the GEMM launch, no partial sums);
+ *   else the decode kernel with a K split (partials summed by a second launch),
+ *   or where that does not fit, the tiled engine for M > 128 and K >= 8192,
+ *   and the split-K skinny kernel otherwise (very wide N).
+ * r9k_gemm_fp8_block_plan names the kernel a shape runs.
  *   a [M][K] bf16, w [N][K] fp8, ws [N/128][K/128] fp32 -> c [M][N] bf16.
  * Errors: as r9k_gemm_fp8_block. */
 int r9k_gemm_fp8_block_qa(const uint16_t *a, int64_t M, int64_t K, const uint8_t *w, const float *ws,
@@ -239,7 +250,8 @@ int r9k_gemm_fp8_block_bf16a_packed(const uint16_t *a, int64_t M, int64_t K, con
  * setting (host only, launches nothing, needs no device): kernel receives
  * R9K_KERNEL_DECODE (the whole-row weight-streaming kernel of the decode
  * widths), R9K_KERNEL_SKINNY (the split-K skinny kernel), R9K_KERNEL_TILED
- * (the LDS-tiled MFMA GEMM) or R9K_KERNEL_NONE (M = 0: nothing is launched);
+ * (the LDS-tiled MFMA GEMM), R9K_KERNEL_MID (the mid-width kernel, 17 to 255
+ * rows, all of K per CTA) or R9K_KERNEL_NONE (M = 0: nothing is launched);
  * ksplit receives the number of CTAs that share one output tile along K
  * (1: no K split, and no reduction launch follows).  packed (0 or 1) says
  * whether the weight is in the fragment order of r9k_pack_weight; the same

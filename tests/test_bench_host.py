@@ -1,8 +1,10 @@
 """bench.py's host-side logic (CPU only): the algorithmic byte count, the counter-summary lookup that fills
-roofline.traffic, and the single-GPU guard."""
+roofline.traffic, the single-GPU guard, the trial helpers and the MoE baseline's arguments."""
 import os
 import subprocess
 import sys
+
+import numpy as np
 
 import bench
 
@@ -54,3 +56,28 @@ def test_step_copies_never_repeat_within_the_cache_window():
         for i in range(len(seq)):
             window = seq[max(0, i - n_copies + 1):i]
             assert seq[i] not in window, (n_copies, i)
+
+
+def test_median_of_trials_and_cpu_seconds():
+    vals = iter([3.0, 1.0, 2.0])
+    m, t = bench.median_of_trials(lambda: next(vals))
+    assert m == 2.0 and t == [3.0, 1.0, 2.0]
+    calls = []
+    s, n = bench.cpu_seconds(lambda: calls.append(1), budget_s=10.0, max_runs=3)
+    assert n == 3 and len(calls) == 3 and s >= 0.0
+
+
+def test_moe_cpu_baseline_computes_the_workload(ora):
+    """The MoE CPU baseline's compact-expert arguments (only the touched experts quantised, ids
+    renumbered) give the oracle's output on the full expert set bit for bit."""
+    import inputs
+    T, H, E, I, k = 3, 256, 6, 128, 2
+    x, logits, w13, w2 = inputs.moe_inputs(5, T, H, E, I)
+    host = dict(x=x, logits=logits, k=k, H=H, I=I, E=E, w13=w13, w2=w2)
+    compact = ora.moe_decode(*bench.moe_oracle_args(ora, host))
+    ids, w = ora.moe_route(logits, k)
+    q13, s13 = ora.quant_weight(w13.reshape(-1, H))
+    q2, s2 = ora.quant_weight(w2.reshape(-1, I))
+    full = ora.moe_decode(x, ids, w, q13.reshape(E, 2 * I, H), s13.reshape(E, 2 * I // 128, H // 128),
+                          q2.reshape(E, H, I), s2.reshape(E, H // 128, I // 128))
+    assert np.array_equal(compact, full)
