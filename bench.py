@@ -35,7 +35,7 @@ a `cpu_baseline` of their own (the oracle on the leg's workload, or a stated
 sample of it, median of up to 3 runs).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-                       [--only decode,prefill,mid,moe,single_token,bf16a]
+                       [--only decode,prefill,mid,moe,single_token,bf16a] [--mid-points 255x4096,...]
                        [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -128,13 +128,15 @@ def weight_copies(torch, r9k, dev, w_bits, min_bytes=ROTATE_BYTES, cap=16):
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_gemm_decode_packed_sweep_k4096_n14336_traffic.md")
 PREFILL_COUNTERS = os.path.join(ROOT, "profiles", "k_gemm_tiled_prefill_m4096_k4096_n12288_counters.md")
+MID_COUNTERS = os.path.join(ROOT, "profiles", "k_gemm_mid_m255_k4096_n4096_counters.md")
 
 
 def kernel_source_hash(kernel_file="gemm_decode.hip"):
     """Hash of the sources that make up one kernel (the decode kernel by
-    default) and its launch."""
+    default; a tuple names several kernel files) and its launch."""
     h = hashlib.sha256()
-    for f in (kernel_file, "r9k_device.h", "r9k_internal.h", "api.hip"):
+    files = (kernel_file,) if isinstance(kernel_file, str) else tuple(kernel_file)
+    for f in files + ("r9k_device.h", "r9k_internal.h", "api.hip"):
         with open(os.path.join(ROOT, "block_scaled_fp8_r9k_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -339,14 +341,22 @@ def bench_prefill(torch, r9k, inputs, dev, reps):
 KERNEL_NAMES = {1: "decode", 2: "skinny", 3: "tiled", 4: "mid"}
 
 
-def bench_mid(torch, r9k, inputs, dev, reps):
+MID_POINTS = tuple((M, K) for K in (4096, 14336) for M in (32, 64, 128, 255))
+MID_N = 4096
+MID_ROOF = (255, 4096)  # the point whose kernel the mid leg's roofline names
+
+
+def bench_mid(torch, r9k, inputs, dev, reps, points=MID_POINTS):
     res = []
-    for K, N in ((4096, 4096), (14336, 4096)):
+    for K, N in ((4096, MID_N), (14336, MID_N)):
+        Ms = [M for M, k in points if k == K]
+        if not Ms:
+            continue
         a = dev(inputs.activations(2, 255, K, outliers=True))
         copies = weight_copies(torch, r9k, dev, inputs.weights(2, N, K))
         copies = [(r9k.pack_weight(wq), ws) for wq, ws in copies]  # fragment order, packed at load
         C = len(copies)
-        for M in (32, 64, 128, 255):
+        for M in Ms:
             wsp = torch.zeros(r9k.gemm_fp8_block_workspace(M, K, N), dtype=torch.uint8, device="cuda")
             am = a[:M].contiguous()
             c_out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
@@ -457,7 +467,7 @@ def bench_single_token(torch, r9k, inputs, dev, reps):
 
 # ---- the oracle beside each leg (CPU, the machine's host cores) ----
 
-def cpu_prefill(ora, inputs, rows=128):
+def cpu_prefill(ora, inputs, rows=512):
     M, K, N = 4096, 4096, 12288
     a = inputs.activations(1, M, K, outliers=True)[:rows]
     wq, ws = ora.quant_weight(inputs.weights(1, N, K))
@@ -538,6 +548,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", default="decode,prefill,mid,moe,single_token,bf16a")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mid-points", default=None,
+                    help="mid leg points as MxK,... (N=4096; default: M in 32,64,128,255 at K=4096 and 14336)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one MI355X: the path is single-GPU (no collectives); run with --gpus 1",
@@ -587,7 +599,18 @@ def main():
     if "prefill" in which:
         line["prefill"] = bench_prefill(torch, r9k, inputs, dev, reps)
     if "mid" in which:
-        line["mid"] = dict(points=bench_mid(torch, r9k, inputs, dev, reps))
+        points = MID_POINTS
+        if args.mid_points:
+            points = tuple(tuple(int(v) for v in p.split("x")) for p in args.mid_points.split(","))
+        line["mid"] = dict(points=bench_mid(torch, r9k, inputs, dev, reps, points))
+        roof = [p for p in line["mid"]["points"] if (p["M"], p["K"]) == MID_ROOF]
+        if roof:
+            p = roof[0]
+            line["mid"]["roofline"] = dict(
+                bound="hbm", achieved=p["GBs"], peak=HBM_PEAK_GBS, unit="GB/s", frac=p["GBs"] / HBM_PEAK_GBS,
+                traffic=traffic_from_profiles(MID_COUNTERS, ("gemm_mid.hip", "quant.hip")),
+                kernel=f"k_quant_act + k_gemm_mid per fused call at M={p['M']}, K={p['K']}, N={p['N']}",
+                bytes_per_launch=gemm_bytes(p["M"], p["K"], p["N"]), us_per_launch=p["us"])
     if "moe" in which:
         line["moe"], moe_host = bench_moe(torch, r9k, inputs, dev, reps)
     if "single_token" in which:
