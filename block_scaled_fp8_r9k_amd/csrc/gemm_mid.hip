@@ -20,7 +20,8 @@
 //     call, like the tiled engine), with the scales transposed to [K/128][M] so
 //     that the 16 rows of a row tile read one line of scales: with WN > 1 the CTA stages each step's
 //     WK groups of its BM rows in LDS (loaded into registers D steps ahead,
-//     written to one of two LDS buffers, one barrier per step), shared by the WN
+//     written to one of two LDS buffers in a bank-swizzled layout, one barrier
+//     per step), shared by the WN
 //     column tiles; with WN = 1 nothing is shared and each wave loads its own
 //     activation fragments into registers;
 //   - per group one e4m3 16x16x128 MFMA per row tile, promoted with the group's
@@ -38,7 +39,13 @@
 namespace r9k {
 
 namespace {
-constexpr int MID_PITCH = 144;  // bytes per staged row of one group (+16: distinct banks for a fragment read)
+// Staged activations: rows of one group, 128 bytes each, with the 16-byte chunk
+// c of row R at chunk c ^ ((R >> 1) & 7).  A fragment read (16 rows, one chunk
+// each) then falls on 16 distinct bank groups, and a staging write (8 lanes per
+// row, two rows) too: the LDS bank-conflict counter reads 0 (with rows padded
+// to 144 bytes instead it counted 4 extra cycles per fragment read).
+constexpr int MID_PITCH = 128;
+__device__ __forceinline__ int mid_chunk(int row, int c) { return c ^ ((row >> 1) & 7); }
 }
 
 template <int MT, int WN, int WK, int D, bool PK>
@@ -131,7 +138,8 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm_mid(MidArgs p) {
                 const int id = tid + c * NT;
                 if (CHUNKS % NT == 0 || id < CHUNKS) {
                     const int kk = id / (BM * 8), r = (id / 8) % BM, c16 = id % 8;
-                    *(u32x4 *)(lds + (j & 1) * STAGE + (kk * BM + r) * MID_PITCH + c16 * 16) = ar[j][c];
+                    const int R = kk * BM + r;
+                    *(u32x4 *)(lds + (j & 1) * STAGE + R * MID_PITCH + mid_chunk(R, c16) * 16) = ar[j][c];
                 }
             }
             __syncthreads();
@@ -144,8 +152,10 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm_mid(MidArgs p) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             if constexpr (ALDS) {
-                const uint8_t *ap = st + (slice * BM + 16 * mt + l16) * MID_PITCH + 16 * q;
-                af[mt] = make_frag(*(const uint4 *)ap, *(const uint4 *)(ap + 64));
+                // chunks q and q + 4 of row R: the second at the first's chunk ^ 4
+                const int R = slice * BM + 16 * mt + l16, c0 = mid_chunk(R, q);
+                const uint8_t *row = st + R * MID_PITCH;
+                af[mt] = make_frag(*(const uint4 *)(row + 16 * c0), *(const uint4 *)(row + 16 * (c0 ^ 4)));
             } else {
                 const u32x4 lo = ar[j][2 * mt], hi = ar[j][2 * mt + 1];
                 af[mt] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
