@@ -19,6 +19,9 @@ The same line carries:
                 its average launch time vs 8 TB/s, averaged over the sweep;
                 `traffic` is the HBM bytes per launch that the committed
                 rocprofv3 counter summary measured on the same kernel source;
+                `frac_of_read_ceiling` the same against hbm_read_ceiling;
+  hbm_read_ceiling  a plain read (no compute) of the weight's byte count,
+                timed like the decode launches: what this GPU streams at best;
   cpu_baseline  the CPU oracle timed on one full step of the same inputs;
   prefill       M=4096, K=4096, N=12288: fp8 TFLOP/s vs 5.03 PFLOP/s dense, for
                 the fused call and (its `roofline`) for the GEMM kernel on
@@ -529,6 +532,43 @@ def cpu_single_token(ora, inputs):
                 sample=f"the M={M}, K={K}, N={N} call in full (weight quant not timed)")
 
 
+BENCH_LIB = os.path.join(ROOT, "block_scaled_fp8_r9k_amd", "libr9k_bench.so")
+
+
+def hbm_read_ceiling(torch, reps, nbytes=DECODE_K * DECODE_N):
+    """The bandwidth ceiling beside the decode roofline: a plain read (no compute) of
+    the decode weight's byte count, rotated over the same number of copies and timed
+    the same way (graphs of back-to-back launches), in two access patterns
+    (libr9k_bench.so: a grid-stride read, and 16 KiB slabs per wave with staggered
+    starts); median of 3 trials each."""
+    import ctypes
+    lib = ctypes.CDLL(BENCH_LIB)
+    lib.r9kb_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    n = max(2, min(16, -(-ROTATE_BYTES // nbytes)))
+    bufs = [torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda") for _ in range(n)]
+    out = torch.zeros(512, dtype=torch.int32, device="cuda")
+    res = {}
+    for mode, name in ((0, "grid_stride"), (1, "slabs_16k_staggered")):
+        def one(i, mode=mode):
+            rc = lib.r9kb_hbm_read(bufs[i % n].data_ptr(), nbytes, mode, out.data_ptr(),
+                                   torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"r9kb_hbm_read mode {mode}: {rc}")
+        calls = [lambda i=i: one(i) for i in range(2 * n)]
+        for f in calls:
+            f()
+        g = capture(torch, calls)
+        tm = Timer(torch)
+        tm.run(lambda i: g.replay(), 2)
+        ms, tr = median_of_trials(lambda: tm.run(lambda i: g.replay(), reps) / len(calls))
+        res[name] = dict(us=ms * 1e3, GBs=nbytes / (ms * 1e-3) / 1e9, trials_us=[t * 1e3 for t in tr])
+        log(f"plain read of {nbytes / 1e6:.1f} MB ({name}): {ms * 1e3:.2f} us, {res[name]['GBs']:.0f} GB/s")
+    best = max(v["GBs"] for v in res.values())
+    del bufs
+    torch.cuda.empty_cache()
+    return dict(bytes=nbytes, copies=n, best_GBs=best, frac_of_peak=best / HBM_PEAK_GBS, **res)
+
+
 def copy_bandwidth(torch):
     """Context only: a plain device copy of 1 GiB (read + write bytes / time)."""
     n = 1 << 30
@@ -590,6 +630,10 @@ def main():
                                        "weights), average over the sweep's five launches",
                                 bytes_per_launch=d["bytes_avg"], us_per_launch=d["us_avg"])
         line["per_m"] = {str(M): v for M, v in d["per_m"].items()}
+        if os.path.exists(BENCH_LIB):
+            ceil = hbm_read_ceiling(torch, max(5, args.steps // 20))
+            line["hbm_read_ceiling"] = ceil
+            line["roofline"]["frac_of_read_ceiling"] = d["achieved"] / ceil["best_GBs"]
         if not args.no_cpu_baseline:
             import oracle
             log("cpu baseline (oracle) ...")

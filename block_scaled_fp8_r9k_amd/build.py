@@ -3,7 +3,9 @@
     python -m block_scaled_fp8_r9k_amd.build
 
 Every .hip file under csrc/ is compiled by hipcc in parallel and linked into
-block_scaled_fp8_r9k_amd/libr9k.so.  Flags: the numerics need IEEE fp32
+block_scaled_fp8_r9k_amd/libr9k.so; the benchmark's own kernels (bench_kernels/,
+a plain read that gives the bandwidth ceiling) go into libr9k_bench.so, which
+the library never loads.  Flags: the numerics need IEEE fp32
 division and denormals and no contraction of a*b+c into fma behind the code's
 back (the kernels write their fmas explicitly); packed-fp32 instructions are
 turned off.  MFMA results go to ordinary VGPRs: every kernel promotes them with
@@ -22,6 +24,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libr9k.so")
+BENCH_SRC = os.path.join(HERE, "bench_kernels")
+BENCH_LIB = os.path.join(HERE, "libr9k_bench.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 CFLAGS = [
@@ -59,6 +63,15 @@ def build(verbose: bool = True) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    bsrcs = sorted(glob.glob(os.path.join(BENCH_SRC, "*.hip")))
+    if bsrcs:
+        tmp = BENCH_LIB + ".tmp%d" % os.getpid()
+        r = subprocess.run([HIPCC, *CFLAGS, "-shared", "-o", tmp, *bsrcs], capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("benchmark kernels failed to build:\n" + r.stderr)
+        os.replace(tmp, BENCH_LIB)
+        if verbose:
+            print(f"built {BENCH_LIB}")
     return LIB
 
 

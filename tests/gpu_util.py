@@ -58,14 +58,16 @@ def assert_close(ora, gpu_bits: np.ndarray, oracle_f64: np.ndarray, what: str, r
 def assert_layouts_agree(ora, a_bits: np.ndarray, b_bits: np.ndarray, what: str):
     """Two bf16 results of the same GEMM on the two weight layouts.  The decode planner may slice K
     differently for fragment-order and row-major weights (each layout's fastest launch), and a different
-    slicing sums the fp32 partials in a different order; so the results agree to within one bf16 ulp,
-    and only on a small share of the outputs do they differ at all.  Where the plans coincide they are
-    equal."""
+    slicing sums the fp32 partials in a different order.  Two fp32 sums of the same terms in different
+    orders differ by a few fp32 roundings of the terms' size, which is far below a bf16 ulp of a typical
+    output but not of one that nearly cancels; so the results agree to within one bf16 ulp plus 2^-16 of
+    the output's RMS (about 2^7 fp32 roundings of a typical term), and only on a small share of the
+    outputs do they differ at all.  Where the plans coincide they are equal."""
     a = ora.bf16_value(a_bits).astype(np.float64)
     b = ora.bf16_value(b_bits).astype(np.float64)
     assert a.shape == b.shape, (what, a.shape, b.shape)
     diff = np.abs(a - b)
-    bound = ora.bf16_ulp(b)
+    bound = ora.bf16_ulp(b) + 2.0 ** -16 * np.sqrt(np.mean(b * b))
     bad = np.argwhere(diff > bound)
     assert bad.size == 0, f"{what}: {len(bad)} outputs differ by more than one bf16 ulp, first at {tuple(bad[0])}"
     n_diff = int(np.count_nonzero(a_bits != b_bits))
