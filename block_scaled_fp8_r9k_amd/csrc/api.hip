@@ -65,7 +65,8 @@ const Tuning &tuning() {
         t.bf16a_gs = (int)num("R9K_BF16A_GS");
         t.mid = getenv("R9K_MID") ? (int)num("R9K_MID") : -1;
         if (const char *e = getenv("R9K_MID_CFG"))
-            if (sscanf(e, "%d,%d,%d,%d", &t.mid_cfg[0], &t.mid_cfg[1], &t.mid_cfg[2], &t.mid_cfg[3]) != 4)
+            if (sscanf(e, "%d,%d,%d,%d,%d", &t.mid_cfg[0], &t.mid_cfg[1], &t.mid_cfg[2], &t.mid_cfg[3],
+                       &t.mid_cfg[4]) < 4)
                 t.mid_cfg[0] = 0;
     });
     return t;
@@ -124,7 +125,7 @@ GemmWs gemm_ws(int64_t M, int64_t K, int64_t N) {
     const SkinnyCfg c = skinny_config(M, K, N);
     w.part = 0;
     w.aq = w.part + std::max({skinny_partial_bytes(c, M, N), tiled_partial_bytes(tiled_plan(M, K, N), M, N),
-                              decode_partial_bytes(M, K, N)});
+                              decode_partial_bytes(M, K, N), mid_partial_bytes(M, K, N)});
     w.as = w.aq + align_up((size_t)(M * K), 256);
     w.total = w.as + align_up((size_t)(M * (K / 128)) * sizeof(float), 256);
     return w;
@@ -147,7 +148,7 @@ struct GemmRoute {
 // or the split-K skinny kernel (very wide N).  Above the boundary: the tiled
 // engine.
 GemmRoute route_gemm(int64_t M, int64_t K, int64_t N, bool packed) {
-    GemmRoute r{R9K_KERNEL_SKINNY, DecodeCfg{0, 0, 0, 0, 0, 0, 0}, TiledPlan{TILE_C, 1}, MidCfg{0, 0, 0, 0}};
+    GemmRoute r{R9K_KERNEL_SKINNY, DecodeCfg{0, 0, 0, 0, 0, 0, 0}, TiledPlan{TILE_C, 1}, MidCfg{0, 0, 0, 0, 1}};
     const int engine = engine_for(M);
     if (engine == R9K_ENGINE_TILED) {
         r.kernel = R9K_KERNEL_TILED;
@@ -208,7 +209,7 @@ int run_gemm(const uint16_t *a, const uint8_t *aq, const float *as, int64_t M, i
         }
         if (rc) return rc;
         if (route.kernel == R9K_KERNEL_MID) {
-            MidArgs m{aq, as_t, w, ws, c, M, K, N, packed};
+            MidArgs m{aq, as_t, w, ws, c, M, K, N, packed, (float *)(base + L.part)};
             return launch_result(launch_gemm_mid(m, route.mc, s));
         }
         TiledArgs t{aq, as_t, w, ws, c, M, K, N, packed, (float *)(base + L.part), 1};
@@ -412,7 +413,7 @@ int r9k_gemm_fp8_block_plan(int64_t M, int64_t K, int64_t N, int packed, int *ke
     *kernel = r.kernel;
     *ksplit = r.kernel == R9K_KERNEL_DECODE ? r.dc.ksplit
               : r.kernel == R9K_KERNEL_TILED ? r.tp.ksplit
-              : r.kernel == R9K_KERNEL_MID   ? 1
+              : r.kernel == R9K_KERNEL_MID   ? r.mc.ksplit
                                               : skinny_config(M, K, N).ksplit;
     return R9K_OK;
 }

@@ -1,5 +1,6 @@
 // Engine (a) at mid widths (17 to 256 rows): the block-scaled fp8 GEMM as one
-// launch over all of K, with no partial sums leaving a CTA.
+// launch over all of K, with no partial sums leaving a CTA; at long K and up to
+// 64 rows, a K split whose fp32 partials a second launch sums in order.
 //
 // The r9700-stack release v0.3.2 notes ("What changed for someone running it")
 // run the fp8 decode kernels up to 255 rows.  At these widths the weight is
@@ -71,7 +72,9 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm_mid(MidArgs p) {
     if (nblk % 8 == 0) lid = (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8;
     const int64_t cb = lid / nrb, rb = lid % nrb;
     const int64_t m0 = rb * BM, n0 = (cb * WN + ct) * 16;
-    const int64_t steps = G / WK;
+    // K split (gridDim.y = S > 1): this CTA covers K-groups [ks G / S, (ks + 1) G / S)
+    const int64_t S = gridDim.y, ks = blockIdx.y;
+    const int64_t steps = G / (S * WK), gbase = ks * (G / S);
     const int64_t nbk = __builtin_amdgcn_readfirstlane((int)(n0 / 128));
     const float *wsrow = p.ws + nbk * G;
 
@@ -90,7 +93,7 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm_mid(MidArgs p) {
     const uint8_t *wtile = PK ? p.w + (n0 / 16) * G * 2048 + 16 * lane : p.w + (n0 + l16) * K + 16 * q;
     auto issue = [&](int64_t s, int slot) {
         __builtin_amdgcn_sched_barrier(0);
-        const int64_t g = s * WK + slice;
+        const int64_t g = gbase + s * WK + slice;
         if (PK) {
             wr[slot][0] = load_nt16(wtile + g * 2048);
             wr[slot][1] = load_nt16(wtile + g * 2048 + 1024);
@@ -105,7 +108,7 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm_mid(MidArgs p) {
                 id = id < CHUNKS ? id : CHUNKS - 1;
                 const int kk = id / (BM * 8), r = (id / 8) % BM, c16 = id % 8;
                 const int64_t row = min<int64_t>(m0 + r, M - 1);
-                ar[slot][c] = *(const u32x4 *)(p.aq + row * K + (s * WK + kk) * 128 + c16 * 16);
+                ar[slot][c] = *(const u32x4 *)(p.aq + row * K + (gbase + s * WK + kk) * 128 + c16 * 16);
             }
         } else {
 #pragma unroll
@@ -208,7 +211,10 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm_mid(MidArgs p) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const int64_t m = m0 + 16 * mt + l16;
-        if (m < M)
+        if (m >= M) continue;
+        if (S > 1)  // fp32 partial [ks][M][N]; a second kernel adds the splits in ascending ks
+            *(v4f *)(p.part + (ks * M + m) * N + n0 + 4 * q) = acc[mt];
+        else
             *(uint2 *)(p.c + m * N + n0 + 4 * q) = bf16x4_rne(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
     }
 }
@@ -220,15 +226,17 @@ static size_t mid_lds(const MidCfg &c) {
     return std::max<size_t>(std::max(stages, red), 16);
 }
 
-// Does (mt, wn, wk, depth) give a valid launch of this shape?
+// Does (mt, wn, wk, depth, ksplit) give a valid launch of this shape?
 static bool mid_fits(int64_t M, int64_t K, int64_t N, const MidCfg &c) {
     const int64_t G = K / 128;
     if (M < 1 || (c.mt != 1 && c.mt != 2 && c.mt != 4) || (c.wn != 1 && c.wn != 2 && c.wn != 4) || c.wk < 1 || c.wn * c.wk > 8)
         return false;
     if ((c.wk & (c.wk - 1)) || (c.depth != 1 && c.depth != 2 && c.depth != 4)) return false;
+    if (c.ksplit < 1 || c.ksplit > MID_MAX_KSPLIT || G % c.ksplit) return false;
     if (c.wn == 1 && c.mt > 2 && c.depth > 2) return false;  // direct fragments: 8 mt registers a step
     if (c.wn > 1 && c.depth == 1) return false;              // two LDS buffers alternate by step parity
-    return N % (16 * c.wn) == 0 && G % c.wk == 0 && G / c.wk >= c.depth && (G / c.wk) % c.depth == 0;
+    const int64_t gs = G / c.ksplit;  // K-groups of one split
+    return N % (16 * c.wn) == 0 && gs % c.wk == 0 && gs / c.wk >= c.depth && (gs / c.wk) % c.depth == 0;
 }
 
 // (mt, wn, wk, depth) for a shape.  The launch shapes that share activations
@@ -241,20 +249,38 @@ static bool mid_fits(int64_t M, int64_t K, int64_t N, const MidCfg &c) {
 // gives 256 CTAs (narrow N), the shape with the most CTAs, also among the
 // one-column-tile shapes that load their activations per wave.
 MidCfg mid_config(int64_t M, int64_t K, int64_t N) {
-    MidCfg c{0, 0, 0, 0};
+    MidCfg c{0, 0, 0, 0, 1};
     if (M < 1 || M > 256 || N % 16) return c;
     const int *f = tuning().mid_cfg;  // tuning override
-    if (f[0] && mid_fits(M, K, N, MidCfg{f[0], f[1], f[2], f[3]})) return MidCfg{f[0], f[1], f[2], f[3]};
+    if (f[0]) {
+        const MidCfg o{f[0], f[1], f[2], f[3], f[4] ? f[4] : 1};
+        if (mid_fits(M, K, N, o)) return o;
+    }
+    // long K at up to 64 rows: one row block (BM >= M) of 64-column blocks, K split
+    // over the fewest CTAs (2 to 8, dividing K/128) that make 256, its fp32
+    // partials summed by the reduce launch: each compute unit then reads
+    // (BM + 64) x K / S bytes instead of all of K for a narrower block (measured
+    // at N = 4096, K = 14336: 32 rows 21.1 -> 18.3 us, 64 rows 24.2 -> 22.6 us;
+    // at K = 4096 and at 128 rows the split does not pay)
+    if (M <= 64 && K >= 8192 && N % 64 == 0) {
+        const int mt = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+        const int64_t ncb = N / 64;
+        for (int ks = 2; ks <= MID_MAX_KSPLIT; ++ks) {
+            if (ncb * ks < 256) continue;
+            for (const MidCfg t : {MidCfg{mt, 4, 1, 4, ks}, MidCfg{mt, 4, 1, 2, ks}, MidCfg{mt, 4, 2, 2, ks}})
+                if (mid_fits(M, K, N, t)) return t;
+        }
+    }
     const int mtmax = (int)std::min<int64_t>((M + 15) / 16, 4);
-    MidCfg best{0, 0, 0, 0};
+    MidCfg best{0, 0, 0, 0, 1};
     int64_t best_ctas = 0, best_edge = 0;
     for (int mt : {4, 2, 1}) {
         if (mt > mtmax && mt != 1) continue;
         for (int wn : {4, 2, 1}) {
-            MidCfg t{0, 0, 0, 0};
+            MidCfg t{0, 0, 0, 0, 1};
             for (int wk = 8 / wn; wk >= 1 && !t.mt; wk /= 2)
                 for (int d : {4, 2, 1})
-                    if (!t.mt && mid_fits(M, K, N, MidCfg{mt, wn, wk, d})) t = MidCfg{mt, wn, wk, d};
+                    if (!t.mt && mid_fits(M, K, N, MidCfg{mt, wn, wk, d, 1})) t = MidCfg{mt, wn, wk, d, 1};
             if (!t.mt) continue;
             const int64_t ctas = ((M + 16 * mt - 1) / (16 * mt)) * (N / (16 * wn));
             const int64_t edge = 16 * mt + 16 * wn;
@@ -288,8 +314,9 @@ static hipError_t launch_mid_one(const MidArgs &a, const MidCfg &c, hipStream_t 
     });
     if (attr_err[dev] != hipSuccess) return attr_err[dev];
     const int64_t nblk = (a.N / (16 * WN)) * ((a.M + 16 * MT - 1) / (16 * MT));
-    hipLaunchKernelGGL((k_gemm_mid<MT, WN, WK, D, PK>), dim3((unsigned)nblk), dim3(64 * WN * WK), mid_lds(c), s,
-                       a);
+    if (c.ksplit > 1 && !a.part) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_gemm_mid<MT, WN, WK, D, PK>), dim3((unsigned)nblk, (unsigned)c.ksplit),
+                       dim3(64 * WN * WK), mid_lds(c), s, a);
     return hipGetLastError();
 }
 
@@ -335,7 +362,15 @@ static hipError_t launch_mid_mt(const MidArgs &a, const MidCfg &c, hipStream_t s
 }
 
 hipError_t launch_gemm_mid(const MidArgs &a, const MidCfg &c, hipStream_t s) {
-    return a.packed ? launch_mid_mt<true>(a, c, s) : launch_mid_mt<false>(a, c, s);
+    const hipError_t e = a.packed ? launch_mid_mt<true>(a, c, s) : launch_mid_mt<false>(a, c, s);
+    if (e != hipSuccess || c.ksplit == 1) return e;
+    return launch_splitk_reduce(a.part, a.c, a.M, a.N, c.ksplit, s);
+}
+
+// Workspace bytes of the K split's fp32 partials [ksplit][M][N] (0 without one)
+size_t mid_partial_bytes(int64_t M, int64_t K, int64_t N) {
+    const MidCfg c = mid_config(M, K, N);
+    return c.mt && c.ksplit > 1 ? align_up(sizeof(float) * (size_t)c.ksplit * M * N, 256) : 0;
 }
 
 }  // namespace r9k

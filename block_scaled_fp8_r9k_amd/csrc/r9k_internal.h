@@ -18,7 +18,7 @@ namespace r9k {
 //   R9K_SKINNY_KC, R9K_SKINNY_KSPLIT skinny kernel K batch and K split
 //   R9K_BF16A_GS                    bf16-activation variant: K-groups per wave
 //   R9K_MID                         mid-width kernel: 0 never, 1 wherever it fits (else the planner's choice)
-//   R9K_MID_CFG=mt,wn,wk,d          mid-width kernel launch shape (ignored where it does not fit)
+//   R9K_MID_CFG=mt,wn,wk,d[,ks]     mid-width kernel launch shape and K split (ignored where it does not fit)
 struct Tuning {
     int decode_wn, decode_wk;
     char tiled_cfg;
@@ -27,7 +27,7 @@ struct Tuning {
     long long skinny_ksplit;
     int bf16a_gs;
     int mid;  // -1: not set
-    int mid_cfg[4];
+    int mid_cfg[5];
 };
 const Tuning &tuning();
 
@@ -109,14 +109,18 @@ struct MidArgs {
     uint16_t *c;
     int64_t M, K, N;
     bool packed;
+    float *part;  // K split: fp32 partials [ksplit][M][N]
 };
 struct MidCfg {
-    int mt;     // row tiles of 16 per CTA (0: the shape does not fit)
-    int wn;     // column tiles of 16 per CTA
-    int wk;     // K slices per column tile (waves per CTA = wn * wk)
-    int depth;  // steps of loads in flight per wave
+    int mt;      // row tiles of 16 per CTA (0: the shape does not fit)
+    int wn;      // column tiles of 16 per CTA
+    int wk;      // K slices per column tile (waves per CTA = wn * wk)
+    int depth;   // steps of loads in flight per wave
+    int ksplit;  // CTAs along K (> 1: fp32 partials, then the ordered reduce launch)
 };
+constexpr int MID_MAX_KSPLIT = 8;
 MidCfg mid_config(int64_t M, int64_t K, int64_t N);
+size_t mid_partial_bytes(int64_t M, int64_t K, int64_t N);
 hipError_t launch_gemm_mid(const MidArgs &args, const MidCfg &cfg, hipStream_t s);
 
 // ---- LDS-tiled MFMA engine (gemm_tiled.hip) ----

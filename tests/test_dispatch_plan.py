@@ -55,9 +55,13 @@ def test_wide_shapes_go_tiled(r9k, M, K, N):
                                    (48, 4096, 16384), (32, 4096, 65536)])
 def test_mid_widths_run_in_one_launch(r9k, M, K, N):
     # 17 to 255 rows where the decode kernel would need a K split: the mid-width kernel, all of K per
-    # CTA, no partial sums and no reduction launch
+    # CTA (one launch after the activation quant), except up to 64 rows at long K, where its K split of
+    # 64-column blocks and the ordered reduce launch move fewer bytes per compute unit
+    split = M <= 64 and K >= 8192
     for packed in (False, True):
-        assert r9k.gemm_fp8_block_plan(M, K, N, packed) == (r9k.KERNEL_MID, 1)
+        kern, ks = r9k.gemm_fp8_block_plan(M, K, N, packed)
+        assert kern == r9k.KERNEL_MID, (M, K, N, kern)
+        assert (ks > 1) == split and (K // 128) % ks == 0 and (N // 64) * ks >= 256 if split else ks == 1, ks
 
 
 def test_prefill_has_no_k_split(r9k):

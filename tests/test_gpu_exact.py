@@ -73,6 +73,7 @@ ROUTES = [
     (32, 4096, 4096, "mid", False),
     (128, 4096, 4096, "mid", False),
     (255, 4096, 4096, "mid", False),
+    (32, 14336, 4096, "mid", True),
     (16, 8192, 32768, "skinny", True),
     (256, 4096, 4096, "tiled", True),
     (512, 256, 2048, "tiled", False),

@@ -1,9 +1,11 @@
-"""GPU parity for the mid-width kernel (17 to 256 rows; one launch over all of K, activations quantised
-once per call), through the C ABI.  The shapes cover every planned configuration kind: one to four row
-tiles (a last row block holding fewer rows than its tile), one column tile per CTA with K split over
-eight, four or one waves, two and four column tiles per CTA sharing staged activations, and load rings
-of one, two and four steps.  Every output is checked against the oracle; the fused call equals the
-split call, and the two weight layouts give the same bits (the same launch)."""
+"""GPU parity for the mid-width kernel (17 to 256 rows) through the C ABI: all of K per CTA on
+activations quantised once per call, or, at long K and up to 64 rows, a K split of 4 or 8 whose fp32
+partials a second launch sums in ascending split order (20 x 14336, 48 x 8192, 40 x 14336 at N = 2048,
+64 x 12288).  The shapes cover every planned configuration kind: one to four row tiles (a last row block
+holding fewer rows than its tile), one column tile per CTA with K split over eight, four or one waves,
+two and four column tiles per CTA sharing staged activations, and load rings of one, two and four steps.
+Every output is checked against the oracle; the fused call equals the split call, and the two weight
+layouts give the same bits (the same launch)."""
 import numpy as np
 import pytest
 
@@ -27,11 +29,14 @@ def r9k():
 @pytest.mark.parametrize("M,K,N", [(17, 4096, 4096), (20, 14336, 4096), (17, 1152, 4096), (33, 3072, 4096),
                                    (40, 2048, 4096), (48, 2048, 16384), (60, 4096, 4096), (64, 2048, 8192),
                                    (130, 1024, 4096), (128, 2048, 4096), (200, 1536, 4096), (255, 512, 8192),
-                                   (100, 384, 4096), (70, 640, 1024), (255, 512, 256), (255, 768, 4096)])
+                                   (100, 384, 4096), (70, 640, 1024), (255, 512, 256), (255, 768, 4096),
+                                   (48, 8192, 4096), (40, 14336, 2048), (64, 12288, 4096)])
 def test_mid_against_oracle(r9k, ora, M, K, N):
-    for packed in (False, True):
-        assert r9k.gemm_fp8_block_plan(M, K, N, packed) == (r9k.KERNEL_MID, 1)
-    say("mid", M, K, N)
+    plans = {r9k.gemm_fp8_block_plan(M, K, N, packed) for packed in (False, True)}
+    assert len(plans) == 1
+    kernel, ksplit = plans.pop()
+    assert kernel == r9k.KERNEL_MID and (K // 128) % ksplit == 0
+    say("mid", M, K, N, "ksplit", ksplit)
     a = inputs.activations(M + 1, M, K, outliers=True)
     w = inputs.weights(K // 128, N, K)
     wq_o, ws_o = ora.quant_weight(w)
