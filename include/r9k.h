@@ -123,7 +123,7 @@ int r9k_encode_e4m3(const float *x, int64_t n, uint8_t *codes, void *stream);
  * The workspace holds the activation codes and scales of a call that
  * quantises once before the GEMM (or the transposed scales the tiled and
  * mid-width kernels read), and the fp32 partial sums of a K split (decode,
- * skinny and tiled kernels); every call writes what it reads, so the contents
+ * mid-width, skinny and tiled kernels); every call writes what it reads, so the contents
  * need no initialisation.  Calls that share a workspace must not overlap in time
  * (same stream, or ordered by events).
  * Errors: NULLPTR (bytes); SHAPE as for the GEMM. */
@@ -151,8 +151,9 @@ int r9k_gemm_fp8_block(const uint8_t *aq, const float *as, int64_t M, int64_t K,
  *   enough column tiles to fill the chip) -> the decode kernel, with the
  *   activation quant in its A-load, one launch;
  *   else from 17 rows on, unless M > 128 and K >= 8192 -> the mid-width
- *   kernel (all of K per CTA, on activations quantised once per call: a quant
- *   launch, then the GEMM launch, no partial sums);
+ *   kernel on activations quantised once per call (a quant launch, then the
+ *   GEMM launch): all of K per CTA, or up to 64 rows at K >= 8192 a K split
+ *   whose fp32 partials a reduce launch sums in ascending split order;
  *   else the decode kernel with a K split (partials summed by a second launch),
  *   or where that does not fit, the tiled engine for M > 128 and K >= 8192,
  *   and the split-K skinny kernel otherwise (very wide N).
@@ -251,7 +252,7 @@ int r9k_gemm_fp8_block_bf16a_packed(const uint16_t *a, int64_t M, int64_t K, con
  * R9K_KERNEL_DECODE (the whole-row weight-streaming kernel of the decode
  * widths), R9K_KERNEL_SKINNY (the split-K skinny kernel), R9K_KERNEL_TILED
  * (the LDS-tiled MFMA GEMM), R9K_KERNEL_MID (the mid-width kernel, 17 to 255
- * rows, all of K per CTA) or R9K_KERNEL_NONE (M = 0: nothing is launched);
+ * rows) or R9K_KERNEL_NONE (M = 0: nothing is launched);
  * ksplit receives the number of CTAs that share one output tile along K
  * (1: no K split, and no reduction launch follows).  packed (0 or 1) says
  * whether the weight is in the fragment order of r9k_pack_weight; the same
