@@ -48,9 +48,10 @@ def _reference(r9k, a, w, ws, packed):
 @pytest.mark.parametrize("packed", [False, True])
 def test_noalloc_equals_workspace_entry(r9k, packed):
     import torch
-    # first a mid-width call (quantised activations in the scratch), then a smaller decode-width call with a
-    # K split (fp32 partials in the scratch, over what the first call left there)
-    shapes = [(128, 4096, 4096), (16, 14336, 2048)]
+    # first a mid-width call with a K split (quantised activations and fp32 partials in the scratch), then
+    # a smaller mid-width call without one, then a smaller decode-width call with a K split (fp32 partials
+    # in the scratch, over what the earlier calls left there)
+    shapes = [(64, 14336, 4096), (32, 4096, 4096), (16, 14336, 2048)]
     for i, (M, K, N) in enumerate(shapes):
         say("noalloc", packed, M, K, N)
         a = dev(inputs.activations(40 + i, M, K, outliers=True))
