@@ -15,6 +15,7 @@ Tensor conventions (all contiguous, on the current CUDA/HIP device):
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from ctypes import POINTER, c_char_p, c_int, c_int64, c_size_t, c_void_p
 
@@ -184,7 +185,11 @@ def encode_e4m3(x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -
 
 # ------------------------------------------------------------------- gemm ----
 
+@functools.lru_cache(maxsize=4096)
 def gemm_fp8_block_workspace(M: int, K: int, N: int) -> int:
+    """Workspace bytes for a GEMM of this shape (r9k_gemm_fp8_block_workspace).  The answer depends on the
+    shape alone (it covers every dispatch setting, and the library reads its tuning variables once), so it
+    is cached: an eager call then pays no query."""
     b = c_size_t(0)
     _check(lib().r9k_gemm_fp8_block_workspace(M, K, N, ctypes.byref(b)), "r9k_gemm_fp8_block_workspace")
     return b.value
@@ -321,6 +326,7 @@ def gemm_fp8_block_plan(M: int, K: int, N: int, packed: bool = False) -> tuple[i
 
 # -------------------------------------------------------------------- moe ----
 
+@functools.lru_cache(maxsize=1024)
 def moe_fp8_decode_workspace(T: int, H: int, E: int, I: int, topk: int) -> int:
     b = c_size_t(0)
     _check(lib().r9k_moe_fp8_decode_workspace(T, H, E, I, topk, ctypes.byref(b)), "r9k_moe_fp8_decode_workspace")
