@@ -63,7 +63,7 @@ def test_quant_act_near_ties(r9k, ora):
     _check_quant_act(r9k, ora, _near_tie_rows(5, 2000).reshape(50, -1), "near-tie groups")
 
 
-@pytest.mark.parametrize("M,K", [(1, 512), (16, 4096), (255, 14336), (4096, 4096), (3, 128)])
+@pytest.mark.parametrize("M,K", [(1, 512), (16, 4096), (255, 14336), (4096, 4096), (3, 128), (513, 16512)])
 def test_quant_act_workloads(r9k, ora, M, K):
     _check_quant_act(r9k, ora, inputs.activations(0, M, K, outliers=K > 512), f"workload {M}x{K}")
 
