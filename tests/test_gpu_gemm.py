@@ -146,35 +146,41 @@ def test_gemm_reuses_workspace_and_streams(r9k, ora):
 
 
 def test_gemm_in_hip_graph(r9k, ora):
-    """Captured decode and prefill calls replay to the eager result, several times."""
+    """Captured calls of every route replay to the eager result, several times, with eager calls on the
+    same workspaces between the replays: decode, decode with a K split (partials + reduce launch), the
+    mid-width kernel (quant launch + GEMM) with and without its K split, and prefill (tiled)."""
     import torch
     r9k.set_dispatch(255, 0)
-    pd = Problem(r9k, ora, 4, 4096, 4096, seed=8)
-    pp = Problem(r9k, ora, 512, 1024, 1024, seed=9)
-    ws_d = torch.zeros(r9k.gemm_fp8_block_workspace(4, 4096, 4096), dtype=torch.uint8, device="cuda")
-    ws_p = torch.zeros(r9k.gemm_fp8_block_workspace(512, 1024, 1024), dtype=torch.uint8, device="cuda")
-    cd = torch.empty((4, 4096), dtype=torch.bfloat16, device="cuda")
-    cp = torch.empty((512, 1024), dtype=torch.bfloat16, device="cuda")
-    eager_d = host(r9k.gemm_fp8_block_qa(pd.a_d, pd.wq_d, pd.ws_d, workspace=ws_d))
-    eager_p = host(r9k.gemm_fp8_block_qa(pp.a_d, pp.wq_d, pp.ws_d, workspace=ws_p))
+    shapes = [(4, 4096, 4096), (16, 14336, 2048), (64, 4096, 4096), (32, 14336, 4096), (512, 1024, 1024)]
+    probs = [Problem(r9k, ora, M, K, N, seed=8 + i) for i, (M, K, N) in enumerate(shapes)]
+    wss = [torch.zeros(r9k.gemm_fp8_block_workspace(M, K, N), dtype=torch.uint8, device="cuda")
+           for M, K, N in shapes]
+    outs = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for M, K, N in shapes]
+    eager = [host(r9k.gemm_fp8_block_qa(p.a_d, p.wq_d, p.ws_d, workspace=w)) for p, w in zip(probs, wss)]
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
-            r9k.gemm_fp8_block_qa(pd.a_d, pd.wq_d, pd.ws_d, c=cd, workspace=ws_d)
-            r9k.gemm_fp8_block_qa(pp.a_d, pp.wq_d, pp.ws_d, c=cp, workspace=ws_p)
+            for p, w, c in zip(probs, wss, outs):
+                r9k.gemm_fp8_block_qa(p.a_d, p.wq_d, p.ws_d, c=c, workspace=w)
     torch.cuda.current_stream().wait_stream(s)
     for rep in range(4):
         say("graph replay", rep)
-        cd.zero_()
-        cp.zero_()
+        for c in outs:
+            c.zero_()
+        # eager work on the same workspaces: each call of the next shape's problem is run on this one's
+        # workspace where it fits, leaving other contents there
+        for k, (p, w) in enumerate(zip(probs, wss)):
+            q = probs[(k + 1) % len(probs)]
+            if w.numel() >= r9k.gemm_fp8_block_workspace(q.M, q.K, q.N):
+                r9k.gemm_fp8_block_qa(q.a_d, q.wq_d, q.ws_d, workspace=w)
+        torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        assert_bits_equal(host(cd), eager_d, f"graph decode replay {rep}")
-        assert_bits_equal(host(cp), eager_p, f"graph prefill replay {rep}")
-        torch.cuda.synchronize()
+        for (M, K, N), c, e in zip(shapes, outs, eager):
+            assert_bits_equal(host(c), e, f"graph {M}x{K}x{N} replay {rep}")
 
 
 @pytest.mark.parametrize("M,K,N", [(17, 4096, 2048), (24, 4096, 1024), (32, 4096, 2048), (32, 2048, 14336),
