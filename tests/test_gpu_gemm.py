@@ -145,6 +145,23 @@ def test_gemm_reuses_workspace_and_streams(r9k, ora):
     assert_bits_equal(host(outs[1]), host(outs[3]), "p2 twice")
 
 
+def test_binding_takes_the_current_stream(r9k, ora):
+    """With no stream argument the binding launches on torch's current stream
+    (read as a raw handle): the default stream, then a side stream entered with
+    torch.cuda.stream; the call made there is correct once that stream is done."""
+    import torch
+    handle = lambda: r9k._stream(None).value or 0  # ctypes reads the null handle (the default stream) as None
+    assert handle() == torch.cuda.current_stream().cuda_stream
+    p = Problem(r9k, ora, 4, 1024, 1024, seed=7)
+    r9k.set_dispatch(255, 0)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        assert handle() == s.cuda_stream
+        out = r9k.gemm_fp8_block_qa(p.a_d, p.wq_d, p.ws_d)
+    s.synchronize()
+    assert_close(ora, host(out), p.oracle_full(ora), "current side stream")
+
+
 def test_gemm_in_hip_graph(r9k, ora):
     """Captured calls of every route replay to the eager result, several times, with eager calls on the
     same workspaces between the replays: decode, decode with a K split (partials + reduce launch), the
