@@ -18,16 +18,26 @@ namespace r9k {
 // and j + 8, so that each load instruction reads whole 128-byte lines (8 lanes
 // x 16 bytes a group) and each store writes 64 contiguous bytes of codes.
 // With `transposed`, the scale of row m, group g goes to as[g*M + m] instead
-// (the tiled engine reads the scales of 256 consecutive rows per group).  The
-// groups are walked in memory order either way: the bf16 and the codes are
-// the bulk of the traffic, and the scattered 4-byte scale stores of
-// neighbouring rows meet in L2 before they reach HBM.
+// (the GEMMs read the scales of consecutive rows per group), and block b takes
+// group g = b % G of the 32 rows from 32 (b / G) on: its 32 scales are then one
+// 128-byte line, where in memory order (one row's G groups a block) each block
+// wrote G lines 4 bytes apiece and the neighbouring rows, whose blocks run on
+// other XCDs, filled the rest of each line from another L2.  Consecutive blocks
+// take consecutive groups of the same rows, so that the loads and code stores
+// still sweep memory in order across the grid.
 __global__ __launch_bounds__(256) void k_quant_act(const uint4 *__restrict__ a, uint2 *__restrict__ aq,
                                                    float *__restrict__ as, int64_t ngroups, int64_t G, int64_t M,
                                                    bool transposed) {
-    const int64_t gid = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+    int64_t gid;
+    if (transposed) {
+        const int64_t m = (int64_t)(blockIdx.x / G) * 32 + (threadIdx.x >> 3);
+        if (m >= M) return;  // uniform across the 8 lanes of a group
+        gid = m * G + blockIdx.x % G;
+    } else {
+        gid = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+        if (gid >= ngroups) return;
+    }
     const int l = threadIdx.x & 7;
-    if (gid >= ngroups) return;  // uniform across the 8 lanes of a group
     const uint4 v0 = a[gid * 16 + l], v1 = a[gid * 16 + 8 + l];
     // maximum over the group's 8 lanes: quad_perm [1,0,3,2], [2,3,0,1], then
     // row_half_mirror (lane i of each 8-lane half row reads lane 7 - i, which
@@ -45,8 +55,8 @@ __global__ __launch_bounds__(256) void k_quant_act(const uint4 *__restrict__ a, 
 
 hipError_t launch_quant_act(const uint16_t *a, int64_t M, int64_t K, uint8_t *aq, float *as, hipStream_t s,
                             bool scales_transposed) {
-    int64_t ngroups = M * (K / 128);
-    int64_t blocks = (ngroups + 31) / 32;
+    const int64_t ngroups = M * (K / 128);
+    const int64_t blocks = scales_transposed ? (M + 31) / 32 * (K / 128) : (ngroups + 31) / 32;
     hipLaunchKernelGGL(k_quant_act, dim3((unsigned)blocks), dim3(256), 0, s, (const uint4 *)a, (uint2 *)aq, as,
                        ngroups, K / 128, M, scales_transposed);
     return hipGetLastError();
