@@ -120,7 +120,7 @@ __global__ __launch_bounds__(64 * WN * WK) void k_gemm_mid(MidArgs p) {
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) sr[slot][mt] = p.as_t[g * M + arow[mt]];
-        wsr[slot] = wsrow[g];  // a vector load of one address: it joins the ring instead of a scalar wait a step
+        wsr[slot] = wsrow[g];  // wave-uniform: a scalar load, which the next step's wait before its barrier covers
         // keep every step's loads in this order, in the prologue as in the loop, so
         // that the waits the compiler derives for the loop hold from its first trip
         // (reordered in the prologue, they forced a drain of the ring every D steps)
