@@ -32,7 +32,7 @@ The same line carries:
                 routing kernel and the fused path with a shared expert;
   single_token  M=1, K=512, N=1024 (seed 0, no outliers): microseconds a call;
   bf16a         the decode sweep on the bf16-activation variant (no quant).
-Every leg's GPU time is the median of TRIALS (3) timed trials, each over many
+Every leg's GPU time is the median of TRIALS (5) timed trials, each over many
 launches, with the trials listed; prefill, mid, moe and single_token each carry
 a `cpu_baseline` of their own (the oracle on the leg's workload, or a stated
 sample of it, median of up to 3 runs).
@@ -60,7 +60,7 @@ FP8_PEAK_TFLOPS = 5033.2        # 256 CU x 2.4 GHz x 8192 flop/CU/clk, dense fp8
 DECODE_M = (1, 2, 4, 8, 16)
 DECODE_K, DECODE_N = 4096, 14336
 ROTATE_BYTES = 512 << 20
-TRIALS = 3
+TRIALS = 5
 
 
 def log(*a):
@@ -119,7 +119,7 @@ def capture(torch, calls):
     return g
 
 
-def weight_copies(torch, r9k, dev, w_bits, min_bytes=ROTATE_BYTES, cap=16):
+def weight_copies(torch, r9k, dev, w_bits, min_bytes=ROTATE_BYTES, cap=40):
     """Quantise W once on the GPU (r9k_quant_weight) and make enough distinct
     device copies that rotating through them defeats the Infinity Cache."""
     wq, ws = r9k.quant_weight(dev(w_bits))
@@ -302,7 +302,7 @@ PREFILL_WARM_S = 0.1  # seconds of alternating prefill launches before the timed
 def bench_prefill(torch, r9k, inputs, dev, reps):
     M, K, N = 4096, 4096, 12288
     a = dev(inputs.activations(1, M, K, outliers=True))
-    copies = weight_copies(torch, r9k, dev, inputs.weights(1, N, K), min_bytes=256 << 20, cap=6)
+    copies = weight_copies(torch, r9k, dev, inputs.weights(1, N, K))
     copies = [(r9k.pack_weight(wq), ws) for wq, ws in copies]  # fragment order, packed at load
     C = len(copies)
     wsp = torch.zeros(r9k.gemm_fp8_block_workspace(M, K, N), dtype=torch.uint8, device="cuda")

@@ -59,9 +59,9 @@ def test_step_copies_never_repeat_within_the_cache_window():
 
 
 def test_median_of_trials_and_cpu_seconds():
-    vals = iter([3.0, 1.0, 2.0])
-    m, t = bench.median_of_trials(lambda: next(vals))
-    assert m == 2.0 and t == [3.0, 1.0, 2.0]
+    vals = iter([3.0, 1.0, 2.0, 5.0, 4.0])
+    m, t = bench.median_of_trials(lambda: next(vals), n=5)
+    assert m == 3.0 and t == [3.0, 1.0, 2.0, 5.0, 4.0]
     calls = []
     s, n = bench.cpu_seconds(lambda: calls.append(1), budget_s=10.0, max_runs=3)
     assert n == 3 and len(calls) == 3 and s >= 0.0
