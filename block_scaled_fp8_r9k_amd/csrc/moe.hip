@@ -14,8 +14,8 @@
 // engine: weight bytes straight into MFMA registers with 16-byte loads, the
 // pairs' activation codes in LDS, one e4m3 16x16x128 MFMA per 16x16 tile and
 // K-group, promotion acc += P * as * ws per group.
-//   gate_up: CTA = (expert, 128-column tile j); each wave holds gate columns
-//            [128 j + 32 w, +32) and the matching up columns I + the same, so
+//   gate_up: CTA = (expert, 64-column tile j); each wave holds gate columns
+//            [64 j + 16 w, +16) and the matching up columns I + the same, so
 //            its lanes own gate and up of the same (pair, column).
 //   down:    CTA = (expert, 128-column tile of H).
 // A pair p = t * topk + j is a row everywhere; intermediates are indexed by p.
@@ -27,6 +27,14 @@ namespace r9k {
 namespace {
 
 enum Mode { GATEUP_STORE = 0, GATEUP_SILU = 1, DOWN_QUANT = 2, DOWN_CODES = 3 };
+
+// gate_up: column tiles of 16 per wave (half gate, half up) and the gate
+// columns of a CTA (four waves).  A CTA of 64 gate + 64 up columns streams 256
+// KiB of an expert's weights at H = 2048; at the decode workload (16 tokens,
+// top-8 of 128 experts) its 1032 working CTAs spread over the compute units
+// evenly enough, where 128 + 128 columns (516 CTAs of 512 KiB, two or three a
+// unit) left the units with three behind: the MoE call took 75 us against 84.
+constexpr int GU_NCT = 2, GU_COLS = 4 * 16 * GU_NCT / 2;
 
 constexpr int MAX_PAIRS = 4096;
 
@@ -69,14 +77,14 @@ struct MoeSmem {
 
 }  // namespace
 
-// One expert GEMM pass.  NCT = column tiles of 16 per wave (4 for gate_up:
-// 2 gate + 2 up, 2 for down).  Rows are the expert's pairs in tiles of 16.
+// One expert GEMM pass.  NCT = column tiles of 16 per wave (GU_NCT for
+// gate_up, half gate and half up; 2 for down).  Rows are the expert's pairs in tiles of 16.
 // PK: expert weights in fragment order (r9k_pack_weight of [E * 2I][H] and
 // [E * H][I]; 16-row tiles never straddle two experts), read in 1 KiB runs.
 template <int MODE, int KC, bool PK>
 __global__ __launch_bounds__(256) void k_moe_gemm(MoeArgs p) {
     constexpr bool GATEUP = MODE == GATEUP_STORE || MODE == GATEUP_SILU;
-    constexpr int NCT = GATEUP ? 4 : 2;
+    constexpr int NCT = GATEUP ? GU_NCT : 2, HALF = NCT / 2;
     constexpr int PITCH = MoeSmem<KC, NCT>::PITCH;
     __shared__ MoeSmem<KC, NCT> sm;
     __shared__ int list[MAX_PAIRS];
@@ -87,7 +95,7 @@ __global__ __launch_bounds__(256) void k_moe_gemm(MoeArgs p) {
     const int P = (int)(p.T * topk);
     const int64_t K = GATEUP ? H : I;          // contraction length
     const int64_t G = K / 128;
-    const int64_t ntile = GATEUP ? I / 128 : H / 128;
+    const int64_t ntile = GATEUP ? I / GU_COLS : H / 128;
     const int e = (int)(blockIdx.x / ntile);
     const int64_t j = blockIdx.x % ntile;
 
@@ -103,15 +111,16 @@ __global__ __launch_bounds__(256) void k_moe_gemm(MoeArgs p) {
         wsbase = p.w13s + (int64_t)e * (2 * I / 128) * G;
 #pragma unroll
         for (int c = 0; c < NCT; ++c)
-            wrow[c] = (c < 2 ? 128 * j : I + 128 * j) + wave * 32 + 16 * (c & 1) + l16;
+            wrow[c] = (c < HALF ? 0 : I) + GU_COLS * j + wave * 16 * HALF + 16 * (c % HALF) + l16;
     } else {
         wbase = p.w2 + (int64_t)e * H * I;
         wsbase = p.w2s + (int64_t)e * (H / 128) * G;
 #pragma unroll
         for (int c = 0; c < NCT; ++c) wrow[c] = 128 * j + wave * 32 + 16 * c + l16;
     }
-    const float *ws_gate = wsbase + j * G;                       // block row of the gate / down tile
-    const float *ws_up = GATEUP ? wsbase + (I / 128 + j) * G : ws_gate;
+    const int64_t jb = GATEUP ? GU_COLS * j / 128 : j;  // block row of the gate / down tile
+    const float *ws_gate = wsbase + jb * G;
+    const float *ws_up = GATEUP ? wsbase + (I / 128 + jb) * G : ws_gate;
 
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
     const int nb = (int)(G / KC);
@@ -202,7 +211,7 @@ __global__ __launch_bounds__(256) void k_moe_gemm(MoeArgs p) {
 #pragma unroll
                 for (int c = 0; c < NCT; ++c) {
                     const v4f pr = mfma_e4m3_16x16x128(make_frag(wr[g][c][0], wr[g][c][1]), af, zero);
-                    const float sc = (GATEUP && c >= 2) ? sc_u : sc_g;
+                    const float sc = (GATEUP && c >= HALF) ? sc_u : sc_g;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) acc[c][i] = __builtin_fmaf(pr[i], sc, acc[c][i]);
                 }
@@ -222,12 +231,12 @@ __global__ __launch_bounds__(256) void k_moe_gemm(MoeArgs p) {
                 }
             } else if (MODE == GATEUP_SILU) {
 #pragma unroll
-                for (int c = 0; c < 2; ++c) {
+                for (int c = 0; c < HALF; ++c) {
                     uint32_t hb[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const float g = __uint_as_float(bf16_rne(acc[c][i]) << 16);
-                        const float u = __uint_as_float(bf16_rne(acc[c + 2][i]) << 16);
+                        const float u = __uint_as_float(bf16_rne(acc[c + HALF][i]) << 16);
                         hb[i] = silu_mul_bf16(g, u);
                     }
                     const int64_t n = wrow[c] - l16 + 4 * q;
@@ -455,9 +464,11 @@ template <int MODE>
 static hipError_t launch_gemm_mode(const MoeArgs &a, hipStream_t s) {
     constexpr bool GATEUP = MODE == GATEUP_STORE || MODE == GATEUP_SILU;
     const int64_t G = (GATEUP ? a.H : a.I) / 128;
-    const int64_t ntile = GATEUP ? a.I / 128 : a.H / 128;
+    const int64_t ntile = GATEUP ? a.I / GU_COLS : a.H / 128;
     const dim3 grid((unsigned)(a.E * ntile));
     // the largest K batch within the register budget that divides K/128
+    // (gate_up at 8: 254 VGPRs, one wave a SIMD, 10% slower; at 2: 1-2% slower;
+    // down at 2 or 3 instead of 6: the same time)
     const int kcmax = GATEUP ? 4 : 8;
     int kc = 1;
     for (int cand : {8, 6, 4, 3, 2, 1})
