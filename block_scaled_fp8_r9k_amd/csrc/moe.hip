@@ -35,6 +35,9 @@ enum Mode { GATEUP_STORE = 0, GATEUP_SILU = 1, DOWN_QUANT = 2, DOWN_CODES = 3 };
 // evenly enough, where 128 + 128 columns (516 CTAs of 512 KiB, two or three a
 // unit) left the units with three behind: the MoE call took 75 us against 84.
 constexpr int GU_NCT = 2, GU_COLS = 4 * 16 * GU_NCT / 2;
+// down: column tiles of 16 per wave and the columns of a CTA (96 KiB of weights
+// at I = 768; CTAs of 64 columns measured the same)
+constexpr int DN_NCT = 2, DN_COLS = 4 * 16 * DN_NCT;
 
 constexpr int MAX_PAIRS = 4096;
 
@@ -84,7 +87,7 @@ struct MoeSmem {
 template <int MODE, int KC, bool PK>
 __global__ __launch_bounds__(256) void k_moe_gemm(MoeArgs p) {
     constexpr bool GATEUP = MODE == GATEUP_STORE || MODE == GATEUP_SILU;
-    constexpr int NCT = GATEUP ? GU_NCT : 2, HALF = NCT / 2;
+    constexpr int NCT = GATEUP ? GU_NCT : DN_NCT, HALF = GATEUP ? NCT / 2 : NCT;
     constexpr int PITCH = MoeSmem<KC, NCT>::PITCH;
     __shared__ MoeSmem<KC, NCT> sm;
     __shared__ int list[MAX_PAIRS];
@@ -95,7 +98,7 @@ __global__ __launch_bounds__(256) void k_moe_gemm(MoeArgs p) {
     const int P = (int)(p.T * topk);
     const int64_t K = GATEUP ? H : I;          // contraction length
     const int64_t G = K / 128;
-    const int64_t ntile = GATEUP ? I / GU_COLS : H / 128;
+    const int64_t ntile = GATEUP ? I / GU_COLS : H / DN_COLS;
     const int e = (int)(blockIdx.x / ntile);
     const int64_t j = blockIdx.x % ntile;
 
@@ -116,9 +119,9 @@ __global__ __launch_bounds__(256) void k_moe_gemm(MoeArgs p) {
         wbase = p.w2 + (int64_t)e * H * I;
         wsbase = p.w2s + (int64_t)e * (H / 128) * G;
 #pragma unroll
-        for (int c = 0; c < NCT; ++c) wrow[c] = 128 * j + wave * 32 + 16 * c + l16;
+        for (int c = 0; c < NCT; ++c) wrow[c] = DN_COLS * j + wave * 16 * NCT + 16 * c + l16;
     }
-    const int64_t jb = GATEUP ? GU_COLS * j / 128 : j;  // block row of the gate / down tile
+    const int64_t jb = (GATEUP ? GU_COLS : DN_COLS) * j / 128;  // block row of the gate / down tile
     const float *ws_gate = wsbase + jb * G;
     const float *ws_up = GATEUP ? wsbase + (I / 128 + jb) * G : ws_gate;
 
@@ -464,7 +467,7 @@ template <int MODE>
 static hipError_t launch_gemm_mode(const MoeArgs &a, hipStream_t s) {
     constexpr bool GATEUP = MODE == GATEUP_STORE || MODE == GATEUP_SILU;
     const int64_t G = (GATEUP ? a.H : a.I) / 128;
-    const int64_t ntile = GATEUP ? a.I / GU_COLS : a.H / 128;
+    const int64_t ntile = GATEUP ? a.I / GU_COLS : a.H / DN_COLS;
     const dim3 grid((unsigned)(a.E * ntile));
     // the largest K batch within the register budget that divides K/128
     // (gate_up at 8: 254 VGPRs, one wave a SIMD, 10% slower; at 2: 1-2% slower;
