@@ -261,7 +261,7 @@ static bool decode_fits(int64_t M, int64_t K, int64_t N, int wn, int wk, int64_t
 // (wn, wk, gs, ksplit) for a shape, M <= 64.  Measured on the MI355X (K = 4096,
 // N = 14336): eight-wave CTAs stream fastest; the activation quant, which
 // every CTA repeats, favours fewer and wider CTAs once M is large.
-//  1. All of K in one CTA (ksplit = 1): wn = 4 from 12 rows on when that leaves
+//  1. All of K in one CTA (ksplit = 1): wn = 4 from 9 rows on when that leaves
 //     at least 192 CTAs, else wn = 2 when that leaves at least 256 CTAs, else
 //     1; then the smallest K split into waves (K-groups per wave a power of
 //     two, at most 16; the split any count up to 8, e.g. 7 for K = 14336) that
@@ -280,7 +280,10 @@ DecodeCfg decode_config(int64_t M, int64_t K, int64_t N, bool packed) {
     if (M < 1 || M > 64) return c;
     // 1. all of K per CTA
     int wn = (tiles % 2 == 0 && tiles / 2 >= 256) ? 2 : 1;
-    if (M >= 12 && tiles % 4 == 0 && tiles / 4 >= 192) wn = 4;
+    // (from 9 rows: at 9 to 11 rows and N = 14336 the half-width CTAs took 6-10%
+    // longer on packed weights, at 10 and 11 rows because their repeated quant
+    // passes the 2^24 budget below and sends the shape to a K split)
+    if (M >= 9 && tiles % 4 == 0 && tiles / 4 >= 192) wn = 4;
     if (const int v = tuning().decode_wn) {
         if (v >= 1 && v <= 4 && tiles % v == 0) wn = v;
     }

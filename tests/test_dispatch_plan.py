@@ -28,11 +28,13 @@ def test_kernel_codes_match_header(r9k):
 
 
 @pytest.mark.parametrize("packed", [False, True])
-@pytest.mark.parametrize("M", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("M", list(range(1, 17)))
 def test_decode_sweep_streams_whole_rows(r9k, M, packed):
     # single-token to 16-row decode on the 4096 -> 14336 projection: one pass
-    # over the weight, no K split
+    # over the weight, no K split (at 10 and 11 rows half-width CTAs would pass
+    # the repeated-quant budget and split K; the wide CTAs from 9 rows on do not)
     assert r9k.gemm_fp8_block_plan(M, 4096, 14336, packed) == (r9k.KERNEL_DECODE, 1)
+    assert r9k.gemm_fp8_block_plan(M, 4096, 12288, packed) == (r9k.KERNEL_DECODE, 1)
 
 
 @pytest.mark.parametrize("M,K,N", [(16, 14336, 4096), (8, 14336, 4096), (16, 14336, 2048), (1, 28672, 1024)])

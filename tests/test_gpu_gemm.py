@@ -69,9 +69,10 @@ def test_gemm_small_shapes(r9k, ora, M, K, N, engine):
     assert_bits_equal(fused, again, f"{engine} repeat {M}x{K}x{N}")
 
 
-@pytest.mark.parametrize("M", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 9, 10, 11, 16])
 def test_gemm_decode_sweep_full(r9k, ora, M):
-    """M in {1,2,4,8,16}, K=4096, N=14336, every output against the oracle."""
+    """M in {1,2,4,8,16} and the odd widths 9-11 (the first rows of the wide
+    CTAs), K=4096, N=14336, every output against the oracle."""
     say("decode sweep", M)
     p = Problem(r9k, ora, M, 4096, 14336)
     c64 = p.oracle_full(ora)
