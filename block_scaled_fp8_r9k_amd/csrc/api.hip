@@ -102,6 +102,9 @@ inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 constexpr int64_t MAX_DIM = int64_t(1) << 24;
 
+// The mid-width kernel's CTAs that one wave of the MI355X's 256 compute units holds
+constexpr int64_t MID_ONE_WAVE_CTAS = 256;
+
 int check_gemm_shape(int64_t M, int64_t K, int64_t N) {
     if (M < 0 || K <= 0 || N <= 0 || K % 128 || N % 128) return R9K_ERR_SHAPE;
     if (M > MAX_DIM || K > MAX_DIM || N > MAX_DIM) return R9K_ERR_SHAPE;
@@ -161,11 +164,16 @@ GemmRoute route_gemm(int64_t M, int64_t K, int64_t N, bool packed) {
         r.kernel = R9K_KERNEL_DECODE;
         return r;
     }
-    // above 128 rows with long K the tiled engine's K split moves fewer bytes than
-    // the mid-width kernel's all-K CTAs (measured at N = 4096, K = 14336: 255 rows
-    // 40 against 44 us; 128 rows within 3%)
-    const bool long_k_wide = M > 128 && K >= 8192;
-    if (mid != 0 && ((M >= 17 && !long_k_wide) || mid == 1)) {
+    // Above 64 rows the tiled engine (256-row tiles, a K split where they do not
+    // fill the chip) is faster than the mid-width kernel at long K (65 to 128 rows
+    // at K = 14336, N = 4096: 26.7-29.2 against 31.3-32.7 us) and wherever the mid
+    // kernel's largest blocks (64 x 64) would need more than one CTA a compute unit
+    // (at K = 4096: 65 to 255 rows at N = 14336, 23.8-32.7 against 26.9-50.4 us; 129
+    // to 255 rows at N = 6144 to 12288, 6-21% faster); with at most one such CTA a
+    // unit the mid kernel is faster (N = 4096 up to 255 rows, N = 6144 and 8192 up
+    // to 128 rows: 3-14%).
+    const bool tiled_faster = M > 64 && (K >= 8192 || ((M + 63) / 64) * (N / 64) > MID_ONE_WAVE_CTAS);
+    if (mid != 0 && ((M >= 17 && !tiled_faster) || mid == 1)) {
         r.mc = mid_config(M, K, N);
         if (r.mc.mt) {
             r.kernel = R9K_KERNEL_MID;
@@ -174,7 +182,7 @@ GemmRoute route_gemm(int64_t M, int64_t K, int64_t N, bool packed) {
     }
     if (r.dc.wn) {
         r.kernel = R9K_KERNEL_DECODE;
-    } else if (long_k_wide && g_engine.load() == R9K_ENGINE_AUTO) {
+    } else if (tiled_faster && g_engine.load() == R9K_ENGINE_AUTO) {
         r.kernel = R9K_KERNEL_TILED;
         r.tp = tiled_plan(M, K, N);
     }

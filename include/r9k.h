@@ -150,13 +150,14 @@ int r9k_gemm_fp8_block(const uint8_t *aq, const float *as, int64_t M, int64_t K,
  *   else, where the decode kernel covers all of K in each CTA (up to 64 rows,
  *   enough column tiles to fill the chip) -> the decode kernel, with the
  *   activation quant in its A-load, one launch;
- *   else from 17 rows on, unless M > 128 and K >= 8192 -> the mid-width
- *   kernel on activations quantised once per call (a quant launch, then the
- *   GEMM launch): all of K per CTA, or up to 64 rows at K >= 8192 a K split
- *   whose fp32 partials a reduce launch sums in ascending split order;
+ *   else from 17 rows on -> the mid-width kernel on activations quantised
+ *   once per call (a quant launch, then the GEMM launch): all of K per CTA,
+ *   or up to 64 rows at K >= 8192 a K split whose fp32 partials a reduce
+ *   launch sums in ascending split order; except above 64 rows where K >= 8192
+ *   or where ceil(M / 64) * (N / 64) > 256 (its 64 x 64 blocks would need
+ *   more than one CTA per compute unit), which take the tiled engine;
  *   else the decode kernel with a K split (partials summed by a second launch),
- *   or where that does not fit, the tiled engine for M > 128 and K >= 8192,
- *   and the split-K skinny kernel otherwise (very wide N).
+ *   or the split-K skinny kernel (very wide N).
  * r9k_gemm_fp8_block_plan names the kernel a shape runs.
  *   a [M][K] bf16, w [N][K] fp8, ws [N/128][K/128] fp32 -> c [M][N] bf16.
  * Errors: as r9k_gemm_fp8_block. */

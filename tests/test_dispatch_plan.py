@@ -46,19 +46,25 @@ def test_decode_k_split(r9k, M, K, N):
 
 
 @pytest.mark.parametrize("M,K,N", [(256, 4096, 4096), (300, 4096, 4096), (4096, 4096, 12288), (255, 14336, 4096),
-                                   (129, 8192, 4096)])
+                                   (129, 8192, 4096), (65, 14336, 4096), (128, 14336, 4096), (65, 8192, 4096),
+                                   (65, 4096, 14336), (255, 4096, 14336), (129, 4096, 8192), (129, 4096, 6144),
+                                   (255, 512, 8192)])
 def test_wide_shapes_go_tiled(r9k, M, K, N):
+    # above 255 rows; and above 64 rows at long K or where the mid-width kernel's 64 x 64 blocks would
+    # need more than one CTA per compute unit (ceil(M / 64) * N / 64 > 256)
     kern, ks = r9k.gemm_fp8_block_plan(M, K, N)
     assert kern == r9k.KERNEL_TILED and ks >= 1
 
 
 @pytest.mark.parametrize("M,K,N", [(17, 4096, 4096), (32, 4096, 4096), (64, 4096, 4096), (128, 4096, 4096),
-                                   (255, 4096, 4096), (32, 14336, 4096), (64, 14336, 4096), (128, 14336, 4096),
-                                   (48, 4096, 16384), (32, 4096, 65536)])
+                                   (255, 4096, 4096), (32, 14336, 4096), (64, 14336, 4096), (48, 4096, 16384),
+                                   (32, 4096, 65536), (64, 4096, 14336), (33, 4096, 14336), (128, 4096, 8192),
+                                   (128, 4096, 6144), (200, 4096, 4096), (255, 512, 4096)])
 def test_mid_widths_run_in_one_launch(r9k, M, K, N):
     # 17 to 255 rows where the decode kernel would need a K split: the mid-width kernel, all of K per
     # CTA (one launch after the activation quant), except up to 64 rows at long K, where its K split of
-    # 64-column blocks and the ordered reduce launch move fewer bytes per compute unit
+    # 64-column blocks and the ordered reduce launch move fewer bytes per compute unit; above 64 rows
+    # only at K < 8192 and where its 64 x 64 blocks fit one CTA per compute unit
     split = M <= 64 and K >= 8192
     for packed in (False, True):
         kern, ks = r9k.gemm_fp8_block_plan(M, K, N, packed)

@@ -100,6 +100,23 @@ def test_gemm_mid_sweep_sampled(r9k, ora, M, K):
     assert_bits_equal(got, p.run(r9k, 0, fused=False), f"mid M={M} fused vs split")
 
 
+@pytest.mark.parametrize("M,K,N", [(65, 4096, 14336), (255, 4096, 14336), (129, 4096, 6144), (65, 14336, 4096),
+                                   (100, 8192, 4096)])
+def test_gemm_wide_mid_rows_go_tiled(r9k, ora, M, K, N):
+    """65 to 255 rows where the tiled engine is the automatic choice (long K, or the mid-width kernel's
+    64 x 64 blocks more than one CTA per compute unit): sampled rows and points against the oracle,
+    and the fused call equal to the split call."""
+    for packed in (False, True):
+        assert r9k.gemm_fp8_block_plan(M, K, N, packed)[0] == r9k.KERNEL_TILED
+    say("wide mid rows", M, K, N)
+    p = Problem(r9k, ora, M, K, N, seed=11)
+    rows = np.unique(np.array([0, 1, M // 2, M - 1]))
+    ms, ns, c64 = _sampled(ora, p, rows)
+    got = p.run(r9k, 0, fused=True)
+    assert_close(ora, got[ms, ns], c64, f"tiled route {M}x{K}x{N}")
+    assert_bits_equal(got, p.run(r9k, 0, fused=False), f"tiled route {M}x{K}x{N} fused vs split")
+
+
 def test_gemm_boundary_both_engines(r9k, ora):
     """M = 255 and 256 at K=4096, N=4096, each engine forced."""
     for M in (255, 256):
