@@ -21,8 +21,9 @@ from ctypes import POINTER, c_char_p, c_int, c_int64, c_size_t, c_void_p
 
 import torch
 
-ABI_VERSION = 7
+ABI_VERSION = 8
 ENGINE_AUTO, ENGINE_SKINNY, ENGINE_TILED = 0, 1, 2
+TILE_AUTO, TILE_256X256, TILE_256X128, TILE_128X64, TILE_256X64 = 0, 1, 2, 3, 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libr9k.so")
@@ -58,6 +59,8 @@ def lib() -> ctypes.CDLL:
         L.r9k_gemm_fp8_block_qa_packed.argtypes = L.r9k_gemm_fp8_block_qa.argtypes
         L.r9k_pack_weight.argtypes = [c_void_p, c_int64, c_int64, c_void_p, c_void_p]
         L.r9k_set_dispatch.argtypes = [c_int, c_int]
+        L.r9k_set_tiled_plan.argtypes = [c_int, c_int]
+        L.r9k_get_tiled_plan.argtypes = [POINTER(c_int), POINTER(c_int)]
         L.r9k_get_dispatch.argtypes = [POINTER(c_int), POINTER(c_int)]
         L.r9k_gemm_fp8_block_plan.argtypes = [c_int64, c_int64, c_int64, c_int, POINTER(c_int), POINTER(c_int)]
         L.r9k_moe_fp8_decode_workspace.argtypes = [c_int64] * 5 + [POINTER(c_size_t)]
@@ -196,8 +199,9 @@ def encode_e4m3(x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -
 @functools.lru_cache(maxsize=4096)
 def gemm_fp8_block_workspace(M: int, K: int, N: int) -> int:
     """Workspace bytes for a GEMM of this shape (r9k_gemm_fp8_block_workspace).  The answer depends on the
-    shape alone (it covers every dispatch setting, and the library reads its tuning variables once), so it
-    is cached: an eager call then pays no query."""
+    shape (it covers every dispatch setting, and the library reads its tuning variables once) and on a
+    forced tiled plan, which set_tiled_plan changes and then clears this cache; so it is cached: an eager
+    call then pays no query."""
     b = c_size_t(0)
     _check(lib().r9k_gemm_fp8_block_workspace(M, K, N, ctypes.byref(b)), "r9k_gemm_fp8_block_workspace")
     return b.value
@@ -313,6 +317,20 @@ def gemm_fp8_block_qa_packed(a, wp, ws, c=None, workspace=None, stream=None) -> 
 
 def set_dispatch(skinny_max_m: int = 255, engine: int = ENGINE_AUTO) -> None:
     _check(lib().r9k_set_dispatch(skinny_max_m, engine), "r9k_set_dispatch")
+
+
+def set_tiled_plan(shape: int = TILE_AUTO, ksplit: int = 0) -> None:
+    """Force the tiled engine's tile shape (TILE_*) and K split (0: the planner's) for later calls
+    (r9k_set_tiled_plan).  A forced split changes the workspace a shape needs, so the cached
+    workspace sizes are dropped."""
+    _check(lib().r9k_set_tiled_plan(shape, ksplit), "r9k_set_tiled_plan")
+    gemm_fp8_block_workspace.cache_clear()
+
+
+def get_tiled_plan() -> tuple[int, int]:
+    sh, ks = c_int(0), c_int(0)
+    _check(lib().r9k_get_tiled_plan(ctypes.byref(sh), ctypes.byref(ks)), "r9k_get_tiled_plan")
+    return sh.value, ks.value
 
 
 def get_dispatch() -> tuple[int, int]:

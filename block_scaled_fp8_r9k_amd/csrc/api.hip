@@ -435,6 +435,28 @@ int r9k_set_dispatch(int skinny_max_m, int engine) {
     return R9K_OK;
 }
 
+int r9k_set_tiled_plan(int shape, int ksplit) {
+    static constexpr int to_internal[] = {-1, TILE_C, TILE_B, TILE_M1, TILE_M2};
+    if (shape < R9K_TILE_AUTO || shape > R9K_TILE_256X64 || ksplit < 0) return R9K_ERR_ARG;
+    set_tiled_override(to_internal[shape], ksplit);
+    return R9K_OK;
+}
+
+int r9k_get_tiled_plan(int *shape, int *ksplit) {
+    if (!shape || !ksplit) return R9K_ERR_NULLPTR;
+    int sh = -1, ks = 0;
+    get_tiled_override(&sh, &ks);
+    switch (sh) {
+        case TILE_C: *shape = R9K_TILE_256X256; break;
+        case TILE_B: *shape = R9K_TILE_256X128; break;
+        case TILE_M1: *shape = R9K_TILE_128X64; break;
+        case TILE_M2: *shape = R9K_TILE_256X64; break;
+        default: *shape = R9K_TILE_AUTO; break;
+    }
+    *ksplit = ks;
+    return R9K_OK;
+}
+
 int r9k_get_dispatch(int *skinny_max_m, int *engine) {
     if (!skinny_max_m || !engine) return R9K_ERR_NULLPTR;
     read_env();

@@ -31,6 +31,7 @@
 // so the 16 rows a fragment read touches in one LDS cycle fall on distinct
 // banks.
 #include <algorithm>
+#include <atomic>
 #include <cstdlib>
 #include <mutex>
 
@@ -434,9 +435,89 @@ static int64_t ctas_of(int64_t M, int64_t N) {
     return ((N + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM);
 }
 
+// Above 256 rows: the tile shape and K split of the least estimated time.  A
+// launch runs in rounds of up to 256 CTAs (one a compute unit); a round costs
+// about the same whether it is full or not, per 128-K group (fused calls at K =
+// 4096 on the MI355X, rounds of 168-256 CTAs): 256 x 256 1.875 us, 256 x 128
+// 1.31 us, 256 x 64 1.02 us, 128 x 64 0.78 us.  Where a shape other than 256 x
+// 256 leaves the chip partly idle, K is split so that about 256 CTAs run, and
+// the split pays its fp32 partials at about 5 TB/s (written, then read with the
+// output written by the reduce launch) and that launch, about 2 us.  The
+// estimates matched the measured calls within about 10% (768 to 3072 rows at N
+// = 4096 to 28672, and 1024 x 14336 x 4096) and picked the fastest shape at
+// each: e.g. 1024 x 4096 x 14336 in one round of 256 x 256 tiles (224 CTAs)
+// 63 us, where two rounds of 256 x 128 took 84 us.
+struct TileCost {
+    TileShape shape;
+    double us_per_group;
+    bool splits;
+};
+static int64_t ctas_for(TileShape shape, int64_t M, int64_t N) {
+    switch (shape) {
+        case TILE_C: return ctas_of<CfgC>(M, N);
+        case TILE_B: return ctas_of<CfgB>(M, N);
+        case TILE_M1: return ctas_of<CfgM1>(M, N);
+        case TILE_M2: return ctas_of<CfgM2>(M, N);
+    }
+    return 0;
+}
+static TiledPlan tiled_plan_wide(int64_t M, int64_t K, int64_t N) {
+    static constexpr TileCost costs[] = {
+        {TILE_C, 1.875, false}, {TILE_B, 1.31, true}, {TILE_M2, 1.02, true}, {TILE_M1, 0.78, true}};
+    const int64_t G = K / 128;
+    TiledPlan best{TILE_C, 1};
+    double best_us = 0.0;
+    for (const TileCost &c : costs) {
+        const int64_t ctas = ctas_for(c.shape, M, N);
+        int64_t s = 1;
+        if (c.splits && ctas < 256) s = std::max<int64_t>(std::min<int64_t>(256 / ctas, G / 2), 1);
+        const int64_t rounds = (ctas * s + 255) / 256;
+        double us = (double)rounds * c.us_per_group * (double)G / (double)s;
+        if (s > 1) us += (8.0 * (double)s * (double)M * (double)N + 2.0 * (double)M * (double)N) / 5.0e6 + 2.0;
+        if (best_us == 0.0 || us < best_us) {
+            best_us = us;
+            best = TiledPlan{c.shape, (int)s};
+        }
+    }
+    return best;
+}
+
+namespace {
+std::atomic<int> g_tile_shape{-1}, g_tile_ksplit{0};
+std::once_flag g_tile_once;
+void tile_override_init() {
+    std::call_once(g_tile_once, [] {
+        int sh = -1;
+        switch (tuning().tiled_cfg) {  // b|c|1|2
+            case 'b': sh = TILE_B; break;
+            case 'c': sh = TILE_C; break;
+            case '1': sh = TILE_M1; break;
+            case '2': sh = TILE_M2; break;
+        }
+        g_tile_shape = sh;
+        g_tile_ksplit = std::max(tuning().tiled_ksplit, 0);
+    });
+}
+}  // namespace
+
+void set_tiled_override(int shape, int ksplit) {
+    tile_override_init();
+    g_tile_shape = shape;
+    g_tile_ksplit = ksplit;
+}
+
+void get_tiled_override(int *shape, int *ksplit) {
+    tile_override_init();
+    *shape = g_tile_shape.load();
+    *ksplit = g_tile_ksplit.load();
+}
+
 TiledPlan tiled_plan(int64_t M, int64_t K, int64_t N) {
     TiledPlan t{TILE_B, 1};
     const int64_t G = K / 128;
+    tile_override_init();
+    const int force_shape = g_tile_shape.load(), force_ksplit = g_tile_ksplit.load();
+    if (M > 256 && force_shape < 0 && force_ksplit == 0) return tiled_plan_wide(M, K, N);
     if (ctas_of<CfgC>(M, N) >= 256) t.shape = TILE_C;
     else if (ctas_of<CfgB>(M, N) >= 256) t.shape = TILE_B;
     else if (M <= 256) {
@@ -446,12 +527,7 @@ TiledPlan tiled_plan(int64_t M, int64_t K, int64_t N) {
         if (M > 128 && G >= 64) t.shape = TILE_B;
         else t.shape = M <= 128 ? TILE_M1 : TILE_M2;
     }
-    switch (tuning().tiled_cfg) {  // b|c|1|2 forces the tile shape (tuning)
-        case 'b': t.shape = TILE_B; break;
-        case 'c': t.shape = TILE_C; break;
-        case '1': t.shape = TILE_M1; break;
-        case '2': t.shape = TILE_M2; break;
-    }
+    if (force_shape >= 0) t.shape = (TileShape)force_shape;
     int64_t ctas = 0;
     switch (t.shape) {
         case TILE_C: ctas = ctas_of<CfgC>(M, N); break;
@@ -461,9 +537,7 @@ TiledPlan tiled_plan(int64_t M, int64_t K, int64_t N) {
     }
     // split K so that about 256 CTAs run, each with at least two groups
     if (t.shape != TILE_C && ctas > 0 && ctas < 256) t.ksplit = (int)std::max<int64_t>(std::min<int64_t>(256 / ctas, G / 2), 1);
-    if (const int v = tuning().tiled_ksplit) {  // tuning
-        if (v >= 1 && v <= G && t.shape != TILE_C) t.ksplit = v;
-    }
+    if (force_ksplit >= 1 && t.shape != TILE_C) t.ksplit = (int)std::min<int64_t>(force_ksplit, G);
     return t;
 }
 

@@ -146,6 +146,11 @@ struct TiledPlan {
     int ksplit;
 };
 TiledPlan tiled_plan(int64_t M, int64_t K, int64_t N);
+// The forced tiled plan (r9k_set_tiled_plan; R9K_TILED_CFG and R9K_TILED_KSPLIT
+// give the initial values): shape -1 = the planner's, else a TileShape; ksplit
+// 0 = the planner's.
+void set_tiled_override(int shape, int ksplit);
+void get_tiled_override(int *shape, int *ksplit);
 size_t tiled_partial_bytes(const TiledPlan &t, int64_t M, int64_t N);
 hipError_t launch_gemm_tiled(const TiledArgs &args, const TiledPlan &plan, hipStream_t s);
 hipError_t launch_splitk_reduce(const float *part, uint16_t *c, int64_t M, int64_t N, int ksplit, hipStream_t s);

@@ -60,7 +60,7 @@ extern "C" {
 #pragma GCC visibility push(default)
 #endif
 
-#define R9K_ABI_VERSION 7
+#define R9K_ABI_VERSION 8
 
 /* Return codes: 0 or negative, as the pages' kernels return them (release
  * v0.3.0, its validation record: a test failing "with the kernel's -7").
@@ -76,7 +76,8 @@ extern "C" {
 
 /* The ABI version this library implements (R9K_ABI_VERSION; 4 added the MoE
  * routing and the shared-expert fold, 5 the bf16-activation variant, 6 the
- * mid-width kernel in the plan query, 7 the allocation-free GEMM entry point).  Callers refuse
+ * mid-width kernel in the plan query, 7 the allocation-free GEMM entry point, 8 the tiled-plan
+ * control).  Callers refuse
  * a library whose version differs from the header they were built against:
  * the convention of the pages' plugin, which refuses an older libr9k.so
  * (release v0.2.2, "Upgrading").  Host only; cannot fail. */
@@ -226,6 +227,26 @@ int r9k_gemm_fp8_block_qa_packed(const uint16_t *a, int64_t M, int64_t K, const 
 #define R9K_ENGINE_TILED 2
 int r9k_set_dispatch(int skinny_max_m, int engine);
 int r9k_get_dispatch(int *skinny_max_m, int *engine);
+
+/* Tiled-engine plan control (release v0.3.0, "What changed for someone
+ * running it": the tiled fp8 GEMMs of prefill widths), for tuning and tests:
+ * every later call that runs the tiled engine uses this tile shape and K
+ * split.  shape: R9K_TILE_AUTO (the planner's choice) or one of the CTA tiles
+ * rows x columns below; ksplit: 0 (the planner's) or the number of CTAs that
+ * share one output tile along K (clamped to K/128 by the call; the 256 x 256
+ * tile takes none, and a forced split is ignored for it).  The environment
+ * variables R9K_TILED_CFG (c, b, 1, 2 for the four tiles) and R9K_TILED_KSPLIT
+ * give the initial values.  The setting is process-wide, changes the
+ * workspace a shape needs (query again after a change), and must change only
+ * while no GEMM call is being issued.
+ * Errors: ARG for an unknown shape or a negative ksplit; NULLPTR (get). */
+#define R9K_TILE_AUTO 0
+#define R9K_TILE_256X256 1
+#define R9K_TILE_256X128 2
+#define R9K_TILE_128X64 3
+#define R9K_TILE_256X64 4
+int r9k_set_tiled_plan(int shape, int ksplit);
+int r9k_get_tiled_plan(int *shape, int *ksplit);
 
 /* The bf16-activation variant at decode widths (release v0.3.1, "What changed
  * for someone running it": the decode GEMMs of fp8 weights run as bf16

@@ -77,6 +77,12 @@ def _ws(L, M, K, N):
     return rc, b.value
 
 
+def _plan(L, M, K, N, packed=1):
+    k, s = c_int(0), c_int(0)
+    assert L.r9k_gemm_fp8_block_plan(M, K, N, packed, ctypes.byref(k), ctypes.byref(s)) == 0
+    return k.value, s.value
+
+
 def test_gemm_workspace_query(L):
     rc, b = _ws(L, 16, 4096, 14336)
     assert rc == 0 and b > 0 and b % 256 == 0
@@ -121,6 +127,32 @@ def test_dispatch_settings(L):
     finally:
         L.r9k_set_dispatch(*old)
     assert L.r9k_get_dispatch(None, ctypes.byref(e)) == -1
+
+
+def test_tiled_plan_control(L):
+    """r9k_set_tiled_plan forces the tiled engine's tile shape and K split; the plan query and the
+    workspace query follow it (host only), and R9K_TILE_AUTO restores the planner's choice."""
+    sh, ks = c_int(-1), c_int(-1)
+    assert L.r9k_get_tiled_plan(ctypes.byref(sh), ctypes.byref(ks)) == 0
+    old = (sh.value, ks.value)
+    plan = lambda M, K, N: _plan(L, M, K, N)
+    auto = plan(512, 4096, 4096)
+    ws_auto = _ws(L, 512, 4096, 4096)[1]
+    try:
+        assert L.r9k_set_tiled_plan(5, 0) == -7 and L.r9k_set_tiled_plan(-1, 0) == -7
+        assert L.r9k_set_tiled_plan(0, -1) == -7
+        assert L.r9k_set_tiled_plan(2, 3) == 0                       # 256 x 128, split 3
+        assert L.r9k_get_tiled_plan(ctypes.byref(sh), ctypes.byref(ks)) == 0 and (sh.value, ks.value) == (2, 3)
+        assert plan(512, 4096, 4096) == (3, 3)
+        assert plan(512, 256, 4096) == (3, 2)                        # the split clamped to K/128
+        # the workspace follows: three fp32 partials of M x N beside the codes
+        assert _ws(L, 512, 4096, 4096)[1] >= 3 * 4 * 512 * 4096
+        assert L.r9k_set_tiled_plan(1, 4) == 0                       # 256 x 256 takes no split
+        assert plan(512, 4096, 4096) == (3, 1)
+    finally:
+        assert L.r9k_set_tiled_plan(*old) == 0
+    assert plan(512, 4096, 4096) == auto and _ws(L, 512, 4096, 4096)[1] == ws_auto
+    assert L.r9k_get_tiled_plan(None, ctypes.byref(ks)) == -1
 
 
 def test_moe_checks(L):

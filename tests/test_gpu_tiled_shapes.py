@@ -4,8 +4,6 @@ Shapes cover ragged M, a last column tile half full (N % 256 == 128), K
 splits that divide the group count unevenly (K = 896: 7 groups), and both
 weight layouts; every output is compared with the oracle to the GEMM bar.
 """
-import os
-
 import numpy as np
 import pytest
 
@@ -23,8 +21,7 @@ def r9k():
     r9k.lib()
     yield r9k
     r9k.set_dispatch(255, r9k.ENGINE_AUTO)
-    os.environ.pop("R9K_TILED_CFG", None)
-    os.environ.pop("R9K_TILED_KSPLIT", None)
+    r9k.set_tiled_plan(r9k.TILE_AUTO, 0)
 
 
 @pytest.fixture(scope="module")
@@ -41,13 +38,18 @@ def problems(r9k, ora):
     return out
 
 
-@pytest.mark.parametrize("shape", ["b", "c", "1", "2"])
-@pytest.mark.parametrize("ksplit", ["1", "3", "7"])
+@pytest.mark.parametrize("shape", ["256x128", "256x256", "128x64", "256x64"])
+@pytest.mark.parametrize("ksplit", [1, 3, 7])
 def test_tiled_shape_and_split(r9k, ora, problems, shape, ksplit):
-    os.environ["R9K_TILED_CFG"] = shape
-    os.environ["R9K_TILED_KSPLIT"] = ksplit
+    code = {"256x256": r9k.TILE_256X256, "256x128": r9k.TILE_256X128, "128x64": r9k.TILE_128X64,
+            "256x64": r9k.TILE_256X64}[shape]
+    r9k.set_tiled_plan(code, ksplit)
     r9k.set_dispatch(255, r9k.ENGINE_TILED)
     try:
+        for (M, K, N) in problems:
+            # the plan the call runs: the forced split (none for the 256 x 256 tile), clamped to K/128
+            want = 1 if shape == "256x256" else min(ksplit, K // 128)
+            assert r9k.gemm_fp8_block_plan(M, K, N) == (r9k.KERNEL_TILED, want), (shape, ksplit, M, K, N)
         for (M, K, N), (a, wq, wp, ws, c64) in problems.items():
             say("tiled", shape, ksplit, M, K, N)
             got = host(r9k.gemm_fp8_block_qa(a, wq, ws))
@@ -56,6 +58,5 @@ def test_tiled_shape_and_split(r9k, ora, problems, shape, ksplit):
             aq, as_ = r9k.quant_act(a)
             assert_bits_equal(host(r9k.gemm_fp8_block(aq, as_, wq, ws)), got, "split == fused")
     finally:
-        os.environ.pop("R9K_TILED_CFG", None)
-        os.environ.pop("R9K_TILED_KSPLIT", None)
+        r9k.set_tiled_plan(r9k.TILE_AUTO, 0)
         r9k.set_dispatch(255, r9k.ENGINE_AUTO)
