@@ -521,11 +521,17 @@ TiledPlan tiled_plan(int64_t M, int64_t K, int64_t N) {
     if (ctas_of<CfgC>(M, N) >= 256) t.shape = TILE_C;
     else if (ctas_of<CfgB>(M, N) >= 256) t.shape = TILE_B;
     else if (M <= 256) {
-        // 64-column tiles, except for long K above 128 rows, where the 256 x 128
-        // tile split about 8 ways takes 10-12% less time (measured on the MI355X
-        // at N = 4096, K = 14336, M = 192 and 255)
-        if (M > 128 && G >= 64) t.shape = TILE_B;
-        else t.shape = M <= 128 ? TILE_M1 : TILE_M2;
+        // 64-column tiles: 128 rows a tile up to 128 rows, and above 128 rows too
+        // where those tiles fill most of one round of the chip by themselves (no
+        // split; 255 x 4096 x 8192 24.0 against 26.4 us for 256-row tiles split two
+        // ways, 192 x 4096 x 8192 23.7 against 24.4), else 256 rows a tile; except
+        // at K >= 12288 above 128 rows, where the 256 x 128 tile split about 8 ways
+        // is faster (N = 4096, K = 14336: 35.3-37.9 against 36.0-39.6 us at 192 and
+        // 255 rows; at K = 8192 the 256 x 64 tile split 4 ways is: 25.2 against 31.6)
+        const int64_t m1 = ctas_of<CfgM1>(M, N);
+        if (M > 128 && G >= 96) t.shape = TILE_B;
+        else if (M <= 128 || (m1 >= 192 && m1 <= 256)) t.shape = TILE_M1;
+        else t.shape = TILE_M2;
     }
     if (force_shape >= 0) t.shape = (TileShape)force_shape;
     int64_t ctas = 0;
