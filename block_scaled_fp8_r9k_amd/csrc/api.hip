@@ -64,6 +64,7 @@ const Tuning &tuning() {
         t.skinny_ksplit = num("R9K_SKINNY_KSPLIT");
         t.bf16a_gs = (int)num("R9K_BF16A_GS");
         t.mid = getenv("R9K_MID") ? (int)num("R9K_MID") : -1;
+        t.moe_mtr = (int)num("R9K_MOE_MTR");
         if (const char *e = getenv("R9K_MID_CFG"))
             if (sscanf(e, "%d,%d,%d,%d,%d", &t.mid_cfg[0], &t.mid_cfg[1], &t.mid_cfg[2], &t.mid_cfg[3],
                        &t.mid_cfg[4]) < 4)

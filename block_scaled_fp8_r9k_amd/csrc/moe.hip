@@ -71,25 +71,27 @@ __device__ int gather_pairs(const int32_t *ids, int P, int e, int *list, int *wa
     return base;
 }
 
-template <int KC, int NCT>
+template <int KC, int MTR>
 struct MoeSmem {
     static constexpr int PITCH = KC * 128 + 16;
-    uint8_t codes[16 * PITCH];
-    float scales[KC * 16];
+    uint8_t codes[16 * MTR * PITCH];
+    float scales[KC * 16 * MTR];
 };
 
 }  // namespace
 
 // One expert GEMM pass.  NCT = column tiles of 16 per wave (GU_NCT for
-// gate_up, half gate and half up; 2 for down).  Rows are the expert's pairs in tiles of 16.
+// gate_up, half gate and half up; 2 for down).  Rows are the expert's pairs in
+// tiles of 16, MTR of them a pass: the weight tile streams once per pass, so
+// an expert with up to 16 MTR pairs reads its weights once.
 // PK: expert weights in fragment order (r9k_pack_weight of [E * 2I][H] and
 // [E * H][I]; 16-row tiles never straddle two experts), read in 1 KiB runs.
-template <int MODE, int KC, bool PK>
+template <int MODE, int KC, int MTR, bool PK>
 __global__ __launch_bounds__(256) void k_moe_gemm(MoeArgs p) {
     constexpr bool GATEUP = MODE == GATEUP_STORE || MODE == GATEUP_SILU;
     constexpr int NCT = GATEUP ? GU_NCT : DN_NCT, HALF = GATEUP ? NCT / 2 : NCT;
-    constexpr int PITCH = MoeSmem<KC, NCT>::PITCH;
-    __shared__ MoeSmem<KC, NCT> sm;
+    constexpr int PITCH = MoeSmem<KC, MTR>::PITCH, ROWS = 16 * MTR;
+    __shared__ MoeSmem<KC, MTR> sm;
     __shared__ int list[MAX_PAIRS];
     __shared__ int wave_cnt[4];
 
@@ -127,11 +129,13 @@ __global__ __launch_bounds__(256) void k_moe_gemm(MoeArgs p) {
 
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
     const int nb = (int)(G / KC);
-    for (int r0 = 0; r0 < cnt; r0 += 16) {
-        const int rows = min(16, cnt - r0);
-        v4f acc[NCT];
+    for (int r0 = 0; r0 < cnt; r0 += ROWS) {
+        const int rows = min(ROWS, cnt - r0);
+        v4f acc[MTR][NCT];
 #pragma unroll
-        for (int c = 0; c < NCT; ++c) acc[c] = zero;
+        for (int rt = 0; rt < MTR; ++rt)
+#pragma unroll
+            for (int c = 0; c < NCT; ++c) acc[rt][c] = zero;
 
         for (int b = 0; b < nb; ++b) {
             const int64_t g0 = (int64_t)b * KC;
@@ -139,11 +143,11 @@ __global__ __launch_bounds__(256) void k_moe_gemm(MoeArgs p) {
 
             // activation side: QA modes quantise a bf16 row group per 16 lanes
             constexpr bool QA = MODE != DOWN_CODES;
-            const int task = tid >> 4;  // 16 row groups per pass, KC passes cover 16 rows x KC groups
-            uint4 avs[KC];
+            const int task = tid >> 4;  // 16 row groups per pass, KC MTR passes cover 16 MTR rows x KC groups
+            uint4 avs[KC * MTR];
             if (QA) {
 #pragma unroll
-                for (int it = 0; it < KC; ++it) {
+                for (int it = 0; it < KC * MTR; ++it) {
                     const int tk = task + 16 * it;  // tk = row * KC + g
                     if (tk < rows * KC) {
                         const int r = tk / KC, g = tk % KC;
@@ -173,21 +177,21 @@ __global__ __launch_bounds__(256) void k_moe_gemm(MoeArgs p) {
                 }
 
             // zero rows past the pair count, then fill the valid rows
-            for (int i = tid; i < (16 - rows) * KC * 8; i += 256) {
+            for (int i = tid; i < (ROWS - rows) * KC * 8; i += 256) {
                 const int r = rows + i / (KC * 8), c16 = i % (KC * 8);
                 *(uint4 *)&sm.codes[r * PITCH + c16 * 16] = make_uint4(0, 0, 0, 0);
             }
-            for (int i = tid; i < (16 - rows) * KC; i += 256) sm.scales[(i % KC) * 16 + rows + i / KC] = 0.0f;
+            for (int i = tid; i < (ROWS - rows) * KC; i += 256) sm.scales[(i % KC) * ROWS + rows + i / KC] = 0.0f;
             if (QA) {
 #pragma unroll
-                for (int it = 0; it < KC; ++it) {
+                for (int it = 0; it < KC * MTR; ++it) {
                     const int tk = task + 16 * it;
                     if (tk < rows * KC) {
                         const int r = tk / KC, g = tk % KC;
                         float s;
                         const uint2 codes = quant_group16(avs[it], s);
                         *(uint2 *)&sm.codes[r * PITCH + g * 128 + l16 * 8] = codes;
-                        if (l16 == 0) sm.scales[g * 16 + r] = s;
+                        if (l16 == 0) sm.scales[g * ROWS + r] = s;
                     }
                 }
             } else {
@@ -199,38 +203,47 @@ __global__ __launch_bounds__(256) void k_moe_gemm(MoeArgs p) {
                 }
                 for (int i = tid; i < rows * KC; i += 256) {
                     const int r = i / KC, g = i % KC;
-                    sm.scales[g * 16 + r] = p.hs[(int64_t)list[r0 + r] * G + g0 + g];
+                    sm.scales[g * ROWS + r] = p.hs[(int64_t)list[r0 + r] * G + g0 + g];
                 }
             }
             __syncthreads();
 
 #pragma unroll
             for (int g = 0; g < KC; ++g) {
-                const uint8_t *ap = &sm.codes[l16 * PITCH + g * 128 + 16 * q];
-                const v8i af = make_frag(*(const uint4 *)ap, *(const uint4 *)(ap + 64));
-                const float sa = sm.scales[g * 16 + l16];
-                const float sc_g = sa * ws_gate[g0 + g];
-                const float sc_u = sa * ws_up[g0 + g];
+                const float wsg = ws_gate[g0 + g], wsu = ws_up[g0 + g];
 #pragma unroll
-                for (int c = 0; c < NCT; ++c) {
-                    const v4f pr = mfma_e4m3_16x16x128(make_frag(wr[g][c][0], wr[g][c][1]), af, zero);
-                    const float sc = (GATEUP && c >= HALF) ? sc_u : sc_g;
+                for (int rt = 0; rt < MTR; ++rt) {
+                    const uint8_t *ap = &sm.codes[(16 * rt + l16) * PITCH + g * 128 + 16 * q];
+                    const v8i af = make_frag(*(const uint4 *)ap, *(const uint4 *)(ap + 64));
+                    const float sa = sm.scales[g * ROWS + 16 * rt + l16];
+                    const float sc_g = sa * wsg;
+                    const float sc_u = sa * wsu;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[c][i] = __builtin_fmaf(pr[i], sc, acc[c][i]);
+                    for (int c = 0; c < NCT; ++c) {
+                        const v4f pr = mfma_e4m3_16x16x128(make_frag(wr[g][c][0], wr[g][c][1]), af, zero);
+                        const float sc = (GATEUP && c >= HALF) ? sc_u : sc_g;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[rt][c][i] = __builtin_fmaf(pr[i], sc, acc[rt][c][i]);
+                    }
                 }
             }
         }
 
 #pragma unroll
-        for (int c = 0; c < NCT; ++c) pin_acc(acc[c]);  // the MFMAs run with every lane enabled
-        // epilogue: lane holds rows (pairs) list[r0 + l16], columns 4q + i of each tile c
-        if (l16 < rows) {
-            const int64_t pr = list[r0 + l16];
+        for (int rt = 0; rt < MTR; ++rt)
+#pragma unroll
+            for (int c = 0; c < NCT; ++c) pin_acc(acc[rt][c]);  // the MFMAs run with every lane enabled
+        // epilogue: lane holds rows (pairs) list[r0 + 16 rt + l16], columns 4q + i of each tile c
+#pragma unroll
+        for (int rt = 0; rt < MTR; ++rt) {
+            if (16 * rt + l16 >= rows) continue;
+            const int64_t pr = list[r0 + 16 * rt + l16];
             if (MODE == GATEUP_STORE) {
 #pragma unroll
                 for (int c = 0; c < NCT; ++c) {
                     const int64_t n = wrow[c] - l16 + 4 * q;  // first of the lane's 4 columns
-                    *(uint2 *)(p.gu + pr * 2 * I + n) = bf16x4_rne(acc[c][0], acc[c][1], acc[c][2], acc[c][3]);
+                    *(uint2 *)(p.gu + pr * 2 * I + n) =
+                        bf16x4_rne(acc[rt][c][0], acc[rt][c][1], acc[rt][c][2], acc[rt][c][3]);
                 }
             } else if (MODE == GATEUP_SILU) {
 #pragma unroll
@@ -238,8 +251,8 @@ __global__ __launch_bounds__(256) void k_moe_gemm(MoeArgs p) {
                     uint32_t hb[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float g = __uint_as_float(bf16_rne(acc[c][i]) << 16);
-                        const float u = __uint_as_float(bf16_rne(acc[c + HALF][i]) << 16);
+                        const float g = __uint_as_float(bf16_rne(acc[rt][c][i]) << 16);
+                        const float u = __uint_as_float(bf16_rne(acc[rt][c + HALF][i]) << 16);
                         hb[i] = silu_mul_bf16(g, u);
                     }
                     const int64_t n = wrow[c] - l16 + 4 * q;
@@ -249,7 +262,7 @@ __global__ __launch_bounds__(256) void k_moe_gemm(MoeArgs p) {
 #pragma unroll
                 for (int c = 0; c < NCT; ++c) {
                     const int64_t n = wrow[c] - l16 + 4 * q;
-                    *(v4f *)(p.y + pr * H + n) = acc[c];
+                    *(v4f *)(p.y + pr * H + n) = acc[rt][c];
                 }
             }
         }
@@ -447,20 +460,35 @@ MoeLayout moe_layout(int64_t T, int64_t H, int64_t E, int64_t I, int64_t topk) {
     return L;
 }
 
-template <int MODE, bool PK>
+template <int MODE, int MTR, bool PK>
 static hipError_t launch_kc(const MoeArgs &a, int kc, dim3 grid, hipStream_t s) {
     constexpr bool GATEUP = MODE == GATEUP_STORE || MODE == GATEUP_SILU;
     switch (kc) {
-        case 8: if constexpr (!GATEUP) { hipLaunchKernelGGL((k_moe_gemm<MODE, 8, PK>), grid, dim3(256), 0, s, a); break; }
+        // (two row tiles a pass take K batches of at most 3)
+        case 8: if constexpr (!GATEUP && MTR == 1) { hipLaunchKernelGGL((k_moe_gemm<MODE, 8, MTR, PK>), grid, dim3(256), 0, s, a); break; }
                 return hipErrorInvalidValue;
-        case 6: if constexpr (!GATEUP) { hipLaunchKernelGGL((k_moe_gemm<MODE, 6, PK>), grid, dim3(256), 0, s, a); break; }
+        case 6: if constexpr (!GATEUP && MTR == 1) { hipLaunchKernelGGL((k_moe_gemm<MODE, 6, MTR, PK>), grid, dim3(256), 0, s, a); break; }
                 return hipErrorInvalidValue;
-        case 4: hipLaunchKernelGGL((k_moe_gemm<MODE, 4, PK>), grid, dim3(256), 0, s, a); break;
-        case 3: hipLaunchKernelGGL((k_moe_gemm<MODE, 3, PK>), grid, dim3(256), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((k_moe_gemm<MODE, 2, PK>), grid, dim3(256), 0, s, a); break;
-        default: hipLaunchKernelGGL((k_moe_gemm<MODE, 1, PK>), grid, dim3(256), 0, s, a); break;
+        case 4: if constexpr (MTR == 1) { hipLaunchKernelGGL((k_moe_gemm<MODE, 4, MTR, PK>), grid, dim3(256), 0, s, a); break; }
+                return hipErrorInvalidValue;
+        case 3: hipLaunchKernelGGL((k_moe_gemm<MODE, 3, MTR, PK>), grid, dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((k_moe_gemm<MODE, 2, MTR, PK>), grid, dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL((k_moe_gemm<MODE, 1, MTR, PK>), grid, dim3(256), 0, s, a); break;
     }
     return hipGetLastError();
+}
+
+// Row tiles a pass: two once an expert gets 10 pairs on average (the launch
+// cannot see the routing), with smaller K batches to keep two waves a SIMD.
+// H = 2048, 128 experts of 768, top-8, fused call: 256 tokens 148.5 against
+// 180.4 us, 192 tokens 136-139 against 145.6; 128 tokens (8 on average) the
+// same; with the one-pass K batches two row tiles were slower below 256 tokens,
+// and four row tiles slower everywhere.  R9K_MOE_MTR overrides (tuning).
+static int moe_row_tiles(const MoeArgs &a) {
+    if (const int v = tuning().moe_mtr) {
+        if (v == 1 || v == 2) return v;
+    }
+    return a.T * a.topk >= 10 * a.E ? 2 : 1;
 }
 
 template <int MODE>
@@ -472,12 +500,15 @@ static hipError_t launch_gemm_mode(const MoeArgs &a, hipStream_t s) {
     // the largest K batch within the register budget that divides K/128
     // (gate_up at 8: 254 VGPRs, one wave a SIMD, 10% slower; at 2: 1-2% slower;
     // down at 2 or 3 instead of 6: the same time)
-    const int kcmax = GATEUP ? 4 : 8;
+    const int mtr = moe_row_tiles(a);
+    const int kcmax = mtr > 1 ? (GATEUP ? 2 : 3) : GATEUP ? 4 : 8;
     int kc = 1;
     for (int cand : {8, 6, 4, 3, 2, 1})
         if (cand <= kcmax && G % cand == 0) { kc = cand; break; }
-    if (a.packed) return launch_kc<MODE, true>(a, kc, grid, s);
-    return launch_kc<MODE, false>(a, kc, grid, s);
+    switch (mtr) {
+        case 2: return a.packed ? launch_kc<MODE, 2, true>(a, kc, grid, s) : launch_kc<MODE, 2, false>(a, kc, grid, s);
+        default: return a.packed ? launch_kc<MODE, 1, true>(a, kc, grid, s) : launch_kc<MODE, 1, false>(a, kc, grid, s);
+    }
 }
 
 hipError_t launch_moe_decode(const MoeArgs &a, bool fused, hipStream_t s) {

@@ -19,6 +19,7 @@ namespace r9k {
 //   R9K_BF16A_GS                    bf16-activation variant: K-groups per wave
 //   R9K_MID                         mid-width kernel: 0 never, 1 wherever it fits (else the planner's choice)
 //   R9K_MID_CFG=mt,wn,wk,d[,ks]     mid-width kernel launch shape and K split (ignored where it does not fit)
+//   R9K_MOE_MTR                     MoE expert GEMMs: row tiles of 16 pairs a pass (1 or 2)
 struct Tuning {
     int decode_wn, decode_wk;
     char tiled_cfg;
@@ -28,6 +29,7 @@ struct Tuning {
     int bf16a_gs;
     int mid;  // -1: not set
     int mid_cfg[5];
+    int moe_mtr;  // MoE row tiles a pass (1 or 2; 0 = by the average pairs an expert gets)
 };
 const Tuning &tuning();
 
