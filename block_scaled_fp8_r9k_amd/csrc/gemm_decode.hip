@@ -266,8 +266,15 @@ static bool decode_fits(int64_t M, int64_t K, int64_t N, int wn, int wk, int64_t
 //     1; then the smallest K split into waves (K-groups per wave a power of
 //     two, at most 16; the split any count up to 8, e.g. 7 for K = 14336) that
 //     gives at least 8 waves per compute unit (4 on row-major weights, whose
-//     16-row load pattern does better with fewer).  Taken when it fits and the
-//     CTAs together quantise at most 2^24 activation values.
+//     16-row load pattern does better with fewer); on fragment-order weights
+//     also at least as many slices as keep a wave's slab at 8 K-groups or fewer
+//     (at 8 to 16 thousand column tiles two slices of 16 groups streamed 3-6%
+//     slower than four of 8).  Taken when it fits and the CTAs together quantise
+//     at most 2^24 activation values or a quarter of the weight bytes, whichever
+//     is more: an LM head over a large vocabulary repeats the quant across
+//     thousands of CTAs, but each CTA's share stays small next to its stream
+//     (4 x 4096 x 128256 80 against 87 us with the K split, 8 rows 86.5 against
+//     94.7 us on the skinny kernel; row-major 91 against 119 us).
 //  2. Else a K split across CTAs: CTAs of 4 x 2 waves (fewer column tiles if
 //     N is narrow), the largest K-groups per wave that still gives at least
 //     256 CTAs, with the split's partial sums reduced by a second kernel.
@@ -295,9 +302,10 @@ DecodeCfg decode_config(int64_t M, int64_t K, int64_t N, bool packed) {
         DecodeCfg t;
         if (!decode_fits(M, K, N, wn, cand, G / cand, 1, t)) continue;
         best = t;
-        if ((tiles / wn) * wn * cand >= (packed ? 8 : 4) * 256) break;
+        if ((tiles / wn) * wn * cand >= (packed ? 8 : 4) * 256 && (!packed || G / cand <= 8)) break;
     }
-    if (best.wn && ((tiles / best.wn) * M * K <= (int64_t(1) << 24) || force_wk)) return best;
+    if (best.wn && ((tiles / best.wn) * M * K <= std::max<int64_t>(int64_t(1) << 24, N * K / 4) || force_wk))
+        return best;
     // 2. a K split across CTAs
     const int wn2 = tiles % 4 == 0 && tiles / 4 >= 64 ? 4 : tiles % 2 == 0 && tiles / 2 >= 64 ? 2 : 1;
     const int wk2 = 8 / wn2 >= 2 ? 2 : 1;

@@ -122,11 +122,20 @@ def test_plan_argument_checks(r9k):
     assert L.r9k_gemm_fp8_block_plan(1, 4096, 4096, 2, byref(k), byref(s)) == -7
 
 
-@pytest.mark.parametrize("M,K,N", [(16, 4096, 151936), (8, 4096, 151936), (16, 8192, 32768), (4, 16384, 65536)])
+@pytest.mark.parametrize("M,K,N", [(1, 4096, 128256), (4, 4096, 128256), (8, 4096, 151936), (16, 4096, 151936),
+                                   (8, 4096, 32768), (16, 4096, 28672)])
+def test_wide_n_decode_streams_whole_rows(r9k, M, K, N):
+    # very wide outputs (an LM head over a large vocabulary) at decode widths: every CTA repeats the
+    # activation quant, but at most a quarter as many values as the weight bytes it streams, so the decode
+    # kernel covers all of K in one launch
+    for packed in (False, True):
+        assert r9k.gemm_fp8_block_plan(M, K, N, packed) == (r9k.KERNEL_DECODE, 1), (M, K, N, packed)
+
+
+@pytest.mark.parametrize("M,K,N", [(16, 8192, 32768), (4, 16384, 65536)])
 def test_wide_n_goes_to_the_skinny_kernel(r9k, M, K, N):
-    # very wide outputs (an LM head over a large vocabulary) at decode widths (up to 16 rows): the decode
-    # kernel's every-CTA activation quant would be repeated across too many column tiles, so the skinny
-    # kernel, with its quant in the A-load, takes them
+    # wide outputs at decode widths where the decode kernel does not fit all of K per CTA (its LDS holds
+    # M x K codes): the skinny kernel, with its quant in the A-load
     for packed in (False, True):
         kern, ks = r9k.gemm_fp8_block_plan(M, K, N, packed)
         assert kern == r9k.KERNEL_SKINNY and ks >= 1, (packed, kern, ks)

@@ -270,6 +270,24 @@ def test_gemm_wide_n_skinny_inload_quant(r9k, ora):
     assert_bits_equal(host(r9k.gemm_fp8_block_qa_packed(p.a_d, wp, p.ws_d)), got, "wide-N skinny packed")
 
 
+def test_gemm_lm_head_width_decode(r9k, ora):
+    """An LM-head-wide output at decode widths (8 rows of a 4096 -> 65536 projection) on the decode kernel
+    over all of K: sampled outputs against the oracle on both weight layouts (which may slice K
+    differently, so each is checked on its own), fused == split bit for bit."""
+    M, K, N = 8, 4096, 65536
+    for packed in (False, True):
+        assert r9k.gemm_fp8_block_plan(M, K, N, packed) == (r9k.KERNEL_DECODE, 1)
+    say("lm-head width decode", M, K, N)
+    p = Problem(r9k, ora, M, K, N, seed=23)
+    ms, ns, c64 = _sampled(ora, p, np.arange(M), n_random=4000)
+    got = p.run(r9k, 0, fused=True)
+    assert_close(ora, got[ms, ns], c64, "lm-head width decode")
+    assert_bits_equal(got, p.run(r9k, 0, fused=False), "lm-head width decode fused vs split")
+    wp = r9k.pack_weight(p.wq_d)
+    gotp = host(r9k.gemm_fp8_block_qa_packed(p.a_d, wp, p.ws_d))
+    assert_close(ora, gotp[ms, ns], c64, "lm-head width decode packed")
+
+
 def test_gemm_empty_batch(r9k):
     """M = 0 through the binding returns an empty output without a launch, for every GEMM form."""
     import torch
