@@ -22,7 +22,7 @@ from ctypes import POINTER, c_char_p, c_int, c_int64, c_size_t, c_void_p
 import torch
 
 ABI_VERSION = 8
-ENGINE_AUTO, ENGINE_SKINNY, ENGINE_TILED = 0, 1, 2
+ENGINE_AUTO, ENGINE_SKINNY, ENGINE_TILED, ENGINE_SPLITK = 0, 1, 2, 3
 TILE_AUTO, TILE_256X256, TILE_256X128, TILE_128X64, TILE_256X64 = 0, 1, 2, 3, 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

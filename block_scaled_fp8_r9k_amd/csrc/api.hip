@@ -115,6 +115,7 @@ int check_gemm_shape(int64_t M, int64_t K, int64_t N) {
 int engine_for(int64_t M) {
     read_env();
     const int e = g_engine.load();
+    if (e == R9K_ENGINE_SPLITK) return M <= g_skinny_max_m.load() ? R9K_ENGINE_SPLITK : R9K_ENGINE_TILED;
     if (e != R9K_ENGINE_AUTO) return e;
     return M <= g_skinny_max_m.load() ? R9K_ENGINE_SKINNY : R9K_ENGINE_TILED;
 }
@@ -159,6 +160,7 @@ GemmRoute route_gemm(int64_t M, int64_t K, int64_t N, bool packed) {
         r.tp = tiled_plan(M, K, N);
         return r;
     }
+    if (engine == R9K_ENGINE_SPLITK) return r;  // the split-K skinny kernel, forced
     r.dc = decode_config(M, K, N, packed);
     const int mid = tuning().mid;
     if (r.dc.wn && r.dc.ksplit == 1 && mid != 1) {
@@ -186,6 +188,18 @@ GemmRoute route_gemm(int64_t M, int64_t K, int64_t N, bool packed) {
     } else if (tiled_faster && g_engine.load() == R9K_ENGINE_AUTO) {
         r.kernel = R9K_KERNEL_TILED;
         r.tp = tiled_plan(M, K, N);
+    } else if (mid != 0 && M >= 8) {
+        // from 8 rows, where the decode kernel fits neither way (large K and N: its
+        // LDS cannot hold M x K codes), the mid-width kernel with its K split streams
+        // faster than the split-K skinny kernel: 8 x 16384 x 32768 89.3 against 97.4 us,
+        // 12 and 16 x 8192 x 32768 50.0 / 51.0 against 54.4 / 57.5, 16 x 16384 x 16384
+        // 49.4 against 53.6; below 8 rows the skinny kernel streams at the chip's
+        // plain-read rate (4 x 16384 x 65536: 6.36 TB/s)
+        const MidCfg mc = mid_config(M, K, N);
+        if (mc.mt) {
+            r.kernel = R9K_KERNEL_MID;
+            r.mc = mc;
+        }
     }
     return r;
 }
@@ -430,7 +444,9 @@ int r9k_gemm_fp8_block_plan(int64_t M, int64_t K, int64_t N, int packed, int *ke
 int r9k_set_dispatch(int skinny_max_m, int engine) {
     read_env();
     if (skinny_max_m < 0) return R9K_ERR_SHAPE;
-    if (engine != R9K_ENGINE_AUTO && engine != R9K_ENGINE_SKINNY && engine != R9K_ENGINE_TILED) return R9K_ERR_ARG;
+    if (engine != R9K_ENGINE_AUTO && engine != R9K_ENGINE_SKINNY && engine != R9K_ENGINE_TILED &&
+        engine != R9K_ENGINE_SPLITK)
+        return R9K_ERR_ARG;
     g_skinny_max_m = skinny_max_m;
     g_engine = engine;
     return R9K_OK;

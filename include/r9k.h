@@ -157,8 +157,9 @@ int r9k_gemm_fp8_block(const uint8_t *aq, const float *as, int64_t M, int64_t K,
  *   launch sums in ascending split order; except above 64 rows where K >= 8192
  *   or where ceil(M / 64) * (N / 64) > 256 (its 64 x 64 blocks would need
  *   more than one CTA per compute unit), which take the tiled engine;
- *   else the decode kernel with a K split (partials summed by a second launch),
- *   or the split-K skinny kernel (very wide N).
+ *   else the decode kernel with a K split (partials summed by a second launch);
+ *   else, from 8 rows, the mid-width kernel with its K split; else the split-K
+ *   skinny kernel (large K and N below 8 rows).
  * r9k_gemm_fp8_block_plan names the kernel a shape runs.
  *   a [M][K] bf16, w [N][K] fp8, ws [N/128][K/128] fp32 -> c [M][N] bf16.
  * Errors: as r9k_gemm_fp8_block. */
@@ -219,12 +220,16 @@ int r9k_gemm_fp8_block_qa_packed(const uint16_t *a, int64_t M, int64_t K, const 
  * largest M the skinny engine takes (default 255, the pages' boundary; env
  * R9K_FP8_SKINNY_MAXM).  engine:
  * R9K_ENGINE_AUTO (by M), R9K_ENGINE_SKINNY or R9K_ENGINE_TILED (forced, for
- * tests; env R9K_FP8_ENGINE=auto|skinny|tiled).  The setting is process-wide;
+ * tests; env R9K_FP8_ENGINE=auto|skinny|tiled), or R9K_ENGINE_SPLITK: up to
+ * skinny_max_m rows, the split-K skinny kernel itself, which the weight-
+ * streaming engine otherwise takes only where neither the decode nor the
+ * mid-width kernel fits (tests and tuning).  The setting is process-wide;
  * change it only while no GEMM call is being issued.
  * Errors: SHAPE if skinny_max_m < 0; ARG for an unknown engine. */
 #define R9K_ENGINE_AUTO 0
 #define R9K_ENGINE_SKINNY 1
 #define R9K_ENGINE_TILED 2
+#define R9K_ENGINE_SPLITK 3
 int r9k_set_dispatch(int skinny_max_m, int engine);
 int r9k_get_dispatch(int *skinny_max_m, int *engine);
 

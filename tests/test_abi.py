@@ -120,7 +120,8 @@ def test_dispatch_settings(L):
     old = (m.value, e.value)
     try:
         assert L.r9k_set_dispatch(-1, 0) == -2
-        assert L.r9k_set_dispatch(255, 7) == -7
+        assert L.r9k_set_dispatch(255, 7) == -7 and L.r9k_set_dispatch(255, 4) == -7
+        assert L.r9k_set_dispatch(255, 3) == 0                      # the split-K skinny kernel, forced
         assert L.r9k_set_dispatch(31, 2) == 0
         assert L.r9k_get_dispatch(ctypes.byref(m), ctypes.byref(e)) == 0
         assert (m.value, e.value) == (31, 2)

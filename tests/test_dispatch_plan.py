@@ -132,9 +132,29 @@ def test_wide_n_decode_streams_whole_rows(r9k, M, K, N):
         assert r9k.gemm_fp8_block_plan(M, K, N, packed) == (r9k.KERNEL_DECODE, 1), (M, K, N, packed)
 
 
-@pytest.mark.parametrize("M,K,N", [(16, 8192, 32768), (4, 16384, 65536)])
+@pytest.mark.parametrize("M,K,N", [(8, 16384, 32768), (12, 8192, 32768), (16, 8192, 32768), (16, 16384, 16384)])
+def test_large_k_and_n_from_8_rows_go_mid(r9k, M, K, N):
+    # large K and N at 8 to 16 rows, where the decode kernel fits neither way: the mid-width kernel with
+    # its K split
+    for packed in (False, True):
+        kern, ks = r9k.gemm_fp8_block_plan(M, K, N, packed)
+        assert kern == r9k.KERNEL_MID and ks > 1, (packed, kern, ks)
+
+
+def test_forced_split_k_engine(r9k):
+    # R9K_ENGINE_SPLITK: the split-K skinny kernel up to the boundary, the tiled engine above it
+    r9k.set_dispatch(255, r9k.ENGINE_SPLITK)
+    try:
+        assert r9k.gemm_fp8_block_plan(16, 2048, 4096)[0] == r9k.KERNEL_SKINNY
+        assert r9k.gemm_fp8_block_plan(255, 1024, 1024)[0] == r9k.KERNEL_SKINNY
+        assert r9k.gemm_fp8_block_plan(256, 1024, 1024)[0] == r9k.KERNEL_TILED
+    finally:
+        r9k.set_dispatch(255, r9k.ENGINE_AUTO)
+
+
+@pytest.mark.parametrize("M,K,N", [(4, 16384, 65536), (2, 16384, 131072)])
 def test_wide_n_goes_to_the_skinny_kernel(r9k, M, K, N):
-    # wide outputs at decode widths where the decode kernel does not fit all of K per CTA (its LDS holds
+    # large K and N below 8 rows, where the decode kernel does not fit all of K per CTA (its LDS holds
     # M x K codes): the skinny kernel, with its quant in the A-load
     for packed in (False, True):
         kern, ks = r9k.gemm_fp8_block_plan(M, K, N, packed)

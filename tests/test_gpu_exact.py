@@ -74,15 +74,25 @@ ROUTES = [
     (128, 4096, 4096, "mid", False),
     (255, 4096, 4096, "mid", False),
     (32, 14336, 4096, "mid", True),
-    (16, 8192, 32768, "skinny", True),
+    (16, 8192, 32768, "mid", True),
     (256, 4096, 4096, "tiled", True),
     (512, 256, 2048, "tiled", False),
 ]
 KERNELS = {"decode": 1, "skinny": 2, "tiled": 3, "mid": 4}
 
 
-@pytest.mark.parametrize("M,K,N,kern,split", ROUTES)
+@pytest.mark.parametrize("M,K,N,kern,split", ROUTES + [(16, 2048, 4096, "skinny", True), (4, 4096, 2048, "skinny", True)])
 def test_exact_sums_round_to_nearest_even(r9k, ora, M, K, N, kern, split):
+    # the split-K skinny kernel is taken by the dispatcher only for large K and N below 8 rows; here it
+    # is forced (R9K_ENGINE_SPLITK) at shapes the oracle handles quickly
+    r9k.set_dispatch(255, r9k.ENGINE_SPLITK if kern == "skinny" else r9k.ENGINE_AUTO)
+    try:
+        _exact_sums(r9k, ora, M, K, N, kern, split)
+    finally:
+        r9k.set_dispatch(255, r9k.ENGINE_AUTO)
+
+
+def _exact_sums(r9k, ora, M, K, N, kern, split):
     for packed in (False, True):
         k, ks = r9k.gemm_fp8_block_plan(M, K, N, packed)
         assert k == KERNELS[kern] and (ks > 1) == split, (packed, k, ks)
@@ -137,11 +147,19 @@ def edge_rows(M, K):
 
 
 @pytest.mark.parametrize("M,K,N,kern", [(12, 1536, 2048, "decode"), (40, 1536, 1024, "decode"),
-                                        (16, 15360, 2048, "decode"), (16, 8192, 32768, "skinny")])
+                                        (16, 15360, 2048, "decode"), (16, 2048, 4096, "skinny")])
 def test_inload_quant_edge_groups(r9k, ora, M, K, N, kern):
     """Every in-load quant (the decode kernel's four lanes a group, with and without a K split, and the
-    skinny kernel's sixteen) on the adversarial groups: fused == split bit for bit on both weight layouts,
-    each row to the tolerance."""
+    skinny kernel's sixteen, forced) on the adversarial groups: fused == split bit for bit on both weight
+    layouts, each row to the tolerance."""
+    r9k.set_dispatch(255, r9k.ENGINE_SPLITK if kern == "skinny" else r9k.ENGINE_AUTO)
+    try:
+        _edge_groups(r9k, ora, M, K, N, kern)
+    finally:
+        r9k.set_dispatch(255, r9k.ENGINE_AUTO)
+
+
+def _edge_groups(r9k, ora, M, K, N, kern):
     for packed in (False, True):
         assert r9k.gemm_fp8_block_plan(M, K, N, packed)[0] == KERNELS[kern]
     say("edge groups", M, K, N, kern)

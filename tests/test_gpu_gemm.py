@@ -253,10 +253,20 @@ def test_gemm_decode_k_split(r9k, ora, M, K, N):
 
 
 def test_gemm_wide_n_skinny_inload_quant(r9k, ora):
-    """A wide output at a decode width (16 rows of an 8192 -> 32768 projection) runs the skinny kernel with
-    the activation quant in its A-load and a K split: sampled outputs against the oracle, fused == split bit
-    for bit, both weight layouts."""
+    """A wide output at a decode width (16 rows of an 8192 -> 32768 projection) on the split-K skinny
+    kernel (forced: the dispatcher gives this shape to the mid-width kernel) with the activation quant in
+    its A-load and a K split: sampled outputs against the oracle, fused == split bit for bit, both weight
+    layouts."""
     M, K, N = 16, 8192, 32768
+    assert r9k.gemm_fp8_block_plan(M, K, N)[0] == r9k.KERNEL_MID
+    r9k.set_dispatch(255, r9k.ENGINE_SPLITK)
+    try:
+        _wide_n_skinny(r9k, ora, M, K, N)
+    finally:
+        r9k.set_dispatch(255, r9k.ENGINE_AUTO)
+
+
+def _wide_n_skinny(r9k, ora, M, K, N):
     for packed in (False, True):
         assert r9k.gemm_fp8_block_plan(M, K, N, packed)[0] == r9k.KERNEL_SKINNY
     say("wide-N skinny", M, K, N)
