@@ -77,7 +77,7 @@ extern "C" {
 /* The ABI version this library implements (R9K_ABI_VERSION; 4 added the MoE
  * routing and the shared-expert fold, 5 the bf16-activation variant, 6 the
  * mid-width kernel in the plan query, 7 the allocation-free GEMM entry point, 8 the tiled-plan
- * control).  Callers refuse
+ * control and R9K_ENGINE_SPLITK).  Callers refuse
  * a library whose version differs from the header they were built against:
  * the convention of the pages' plugin, which refuses an older libr9k.so
  * (release v0.2.2, "Upgrading").  Host only; cannot fail. */
