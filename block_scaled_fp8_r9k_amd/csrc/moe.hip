@@ -462,12 +462,11 @@ MoeLayout moe_layout(int64_t T, int64_t H, int64_t E, int64_t I, int64_t topk) {
 
 template <int MODE, int MTR, bool PK>
 static hipError_t launch_kc(const MoeArgs &a, int kc, dim3 grid, hipStream_t s) {
-    constexpr bool GATEUP = MODE == GATEUP_STORE || MODE == GATEUP_SILU;
     switch (kc) {
         // (two row tiles a pass take K batches of at most 3)
-        case 8: if constexpr (!GATEUP && MTR == 1) { hipLaunchKernelGGL((k_moe_gemm<MODE, 8, MTR, PK>), grid, dim3(256), 0, s, a); break; }
+        case 8: if constexpr (MTR == 1) { hipLaunchKernelGGL((k_moe_gemm<MODE, 8, MTR, PK>), grid, dim3(256), 0, s, a); break; }
                 return hipErrorInvalidValue;
-        case 6: if constexpr (!GATEUP && MTR == 1) { hipLaunchKernelGGL((k_moe_gemm<MODE, 6, MTR, PK>), grid, dim3(256), 0, s, a); break; }
+        case 6: if constexpr (MTR == 1) { hipLaunchKernelGGL((k_moe_gemm<MODE, 6, MTR, PK>), grid, dim3(256), 0, s, a); break; }
                 return hipErrorInvalidValue;
         case 4: if constexpr (MTR == 1) { hipLaunchKernelGGL((k_moe_gemm<MODE, 4, MTR, PK>), grid, dim3(256), 0, s, a); break; }
                 return hipErrorInvalidValue;
@@ -491,6 +490,9 @@ static int moe_row_tiles(const MoeArgs &a) {
     return a.T * a.topk >= 10 * a.E ? 2 : 1;
 }
 
+// compute units of the chip: a grid up to this many CTAs runs in one wave, one CTA each
+constexpr int64_t MOE_ONE_PER_CU_CTAS = 256;
+
 template <int MODE>
 static hipError_t launch_gemm_mode(const MoeArgs &a, hipStream_t s) {
     constexpr bool GATEUP = MODE == GATEUP_STORE || MODE == GATEUP_SILU;
@@ -499,9 +501,14 @@ static hipError_t launch_gemm_mode(const MoeArgs &a, hipStream_t s) {
     const dim3 grid((unsigned)(a.E * ntile));
     // the largest K batch within the register budget that divides K/128
     // (gate_up at 8: 254 VGPRs, one wave a SIMD, 10% slower; at 2: 1-2% slower;
-    // down at 2 or 3 instead of 6: the same time)
+    // down at 2 or 3 instead of 6: the same time).  When the CTAs that hold
+    // pairs fit one a compute unit, occupancy buys nothing and gate_up takes 8
+    // too: twice the bytes in flight a round trip (1-2 tokens over 128 experts
+    // of 768: 4-6% faster; at 3 CTAs in 2 compute units, 6% slower).
     const int mtr = moe_row_tiles(a);
-    const int kcmax = mtr > 1 ? (GATEUP ? 2 : 3) : GATEUP ? 4 : 8;
+    const int64_t busy_ctas = std::min<int64_t>(a.E, a.T * a.topk) * ntile;  // at most
+    const bool one_per_cu = mtr == 1 && busy_ctas <= MOE_ONE_PER_CU_CTAS;
+    const int kcmax = mtr > 1 ? (GATEUP ? 2 : 3) : (GATEUP && !one_per_cu) ? 4 : 8;
     int kc = 1;
     for (int cand : {8, 6, 4, 3, 2, 1})
         if (cand <= kcmax && G % cand == 0) { kc = cand; break; }
