@@ -79,15 +79,34 @@ def _dump(name, **arrays):
     np.savez_compressed(os.path.join("gpurun_out", name), **arrays)
 
 
+def _drawn_shapes(seed=2027, n=16):
+    """Seeded (T, H, E, I, topk) draws beside the hand-picked shapes: 1-8, 9-64 or 65-256 tokens, up to
+    64 experts, top-1 to top-6, H/128 from 1 to 24 and I/128 from 1 to 8, with E * H * I at most 2^24 so
+    that the oracle's quant of every expert stays quick.  Seed 2027 gives one and two row tiles a pass,
+    K batches of 1, 2, 3, 4, 6 and 8 groups, and launches with their busy CTAs under and over one a
+    compute unit."""
+    g = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        T = int(g.choice([g.integers(1, 9), g.integers(9, 65), g.integers(65, 257)]))
+        E = int(g.integers(1, 65))
+        k = int(g.integers(1, min(E, 6) + 1))
+        H, I = 128 * int(g.integers(1, 25)), 128 * int(g.integers(1, 9))
+        if E * H * I <= 1 << 24:
+            out.append((T, H, E, I, k))
+    return out
+
+
 # Shapes: the workload's, and small and wide ones that give K batches of 1, 2,
 # 3, 4, 6 and 8 groups (K/128 from 1 to 56), single- and multi-batch K loops,
 # experts with more than 16 pairs (several row tiles), and the largest token
-# count the decode path takes (255 tokens, 2040 pairs over 32 experts).
+# count the decode path takes (255 tokens, 2040 pairs over 32 experts); then
+# the seeded draws.
 @pytest.mark.parametrize("shape", [(16, 2048, 128, 768, 8), (2, 256, 4, 128, 2), (40, 256, 4, 256, 2),
                                    (40, 256, 4, 128, 2), (20, 256, 2, 128, 1), (1, 128, 3, 128, 3),
                                    (40, 1024, 4, 384, 2), (24, 512, 3, 512, 3), (40, 2048, 4, 256, 2),
                                    (8, 512, 2, 2048, 2), (4, 4096, 2, 256, 2), (2, 7168, 2, 256, 2),
-                                   (255, 1024, 32, 256, 8)])
+                                   (255, 1024, 32, 256, 8)] + _drawn_shapes())
 def test_moe_decode(r9k, ora, shape):
     """Stage by stage on the three-launch path, then the fused path against it."""
     import torch
