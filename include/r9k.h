@@ -150,7 +150,9 @@ int r9k_gemm_fp8_block(const uint8_t *aq, const float *as, int64_t M, int64_t K,
  *   M > skinny_max_m (default 255)       -> the LDS-tiled MFMA engine;
  *   else, where the decode kernel covers all of K in each CTA (up to 64 rows,
  *   enough column tiles to fill the chip) -> the decode kernel, with the
- *   activation quant in its A-load, one launch;
+ *   activation quant in its A-load, one launch; from 17 rows only where its
+ *   estimated time (the busiest compute unit's weight bytes and repeated
+ *   quant) is below the mid-width kernel's (that unit's bytes of codes);
  *   else from 17 rows on -> the mid-width kernel on activations quantised
  *   once per call (a quant launch, then the GEMM launch): all of K per CTA,
  *   or up to 64 rows at K >= 8192 a K split whose fp32 partials a reduce

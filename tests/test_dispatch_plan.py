@@ -132,6 +132,20 @@ def test_wide_n_decode_streams_whole_rows(r9k, M, K, N):
         assert r9k.gemm_fp8_block_plan(M, K, N, packed) == (r9k.KERNEL_DECODE, 1), (M, K, N, packed)
 
 
+@pytest.mark.parametrize("M,K,N,kern", [(17, 4096, 14336, 1), (32, 2048, 14336, 1), (64, 512, 14336, 1),
+                                        (32, 1024, 4096, 1), (17, 512, 1024, 1),
+                                        (17, 4096, 2048, 4), (32, 4096, 2048, 4), (64, 2048, 2048, 4),
+                                        (48, 1024, 4096, 4), (32, 4096, 28672, 4), (64, 2048, 28672, 4)])
+def test_whole_k_decode_against_mid_from_17_rows(r9k, M, K, N, kern):
+    # from 17 rows, where the decode kernel covers all of K per CTA, the lower of the two estimated
+    # times: the decode kernel keeps shapes whose busiest compute unit streams many weight bytes next to
+    # the activations it re-quantises (N = 14336, or short K); with few column tiles a CTA, or two CTAs
+    # a compute unit at K >= 2048, the mid-width kernel on activations quantised once is faster
+    want = r9k.KERNEL_DECODE if kern == 1 else r9k.KERNEL_MID
+    for packed in (False, True):
+        assert r9k.gemm_fp8_block_plan(M, K, N, packed) == (want, 1), (M, K, N, packed)
+
+
 @pytest.mark.parametrize("M,K,N", [(8, 16384, 32768), (12, 8192, 32768), (16, 8192, 32768), (16, 16384, 16384)])
 def test_large_k_and_n_from_8_rows_go_mid(r9k, M, K, N):
     # large K and N at 8 to 16 rows, where the decode kernel fits neither way: the mid-width kernel with
