@@ -218,12 +218,14 @@ def test_gemm_in_hip_graph(r9k, ora):
             assert_bits_equal(host(c), e, f"graph {M}x{K}x{N} replay {rep}")
 
 
-@pytest.mark.parametrize("M,K,N", [(17, 4096, 2048), (24, 4096, 1024), (32, 4096, 2048), (32, 2048, 14336),
-                                   (8, 14336, 1024)])
+@pytest.mark.parametrize("M,K,N", [(17, 4096, 14336), (24, 1024, 4096), (20, 1536, 3072), (24, 2048, 8192),
+                                   (32, 2048, 14336), (8, 14336, 1024)])
 def test_gemm_decode_two_row_tiles(r9k, ora, M, K, N):
     """The decode kernel's widths past 16 rows (two row tiles) and K=14336 at 8 rows, full output, both
     weight layouts (which may slice K differently: equal up to the fp32 summation order)."""
     say("decode widths", M, K, N)
+    for packed in (False, True):
+        assert r9k.gemm_fp8_block_plan(M, K, N, packed) == (r9k.KERNEL_DECODE, 1), (M, K, N, packed)
     p = Problem(r9k, ora, M, K, N, seed=M + 3)
     c64 = p.oracle_full(ora)
     got = p.run(r9k, 0, fused=True)
