@@ -262,8 +262,9 @@ static bool decode_fits(int64_t M, int64_t K, int64_t N, int wn, int wk, int64_t
 // N = 14336): eight-wave CTAs stream fastest; the activation quant, which
 // every CTA repeats, favours fewer and wider CTAs once M is large.
 //  1. All of K in one CTA (ksplit = 1): wn = 4 from 9 rows on when that leaves
-//     at least 192 CTAs, else wn = 2 when that leaves at least 256 CTAs, else
-//     1; then the smallest K split into waves (K-groups per wave a power of
+//     at least 168 CTAs, else wn = 2 when that leaves at least 256 CTAs (168
+//     from 5 rows on), else 1, and up to 4 rows wn = 1 where it gives the
+//     busiest compute unit a fifth fewer tiles; then the smallest K split into waves (K-groups per wave a power of
 //     two, at most 16; the split any count up to 8, e.g. 7 for K = 14336) that
 //     gives at least 8 waves per compute unit (4 on row-major weights, whose
 //     16-row load pattern does better with fewer); on fragment-order weights
@@ -286,11 +287,15 @@ DecodeCfg decode_config(int64_t M, int64_t K, int64_t N, bool packed) {
     const int64_t G = K / 128, tiles = N / 16;
     if (M < 1 || M > 64) return c;
     // 1. all of K per CTA
-    int wn = (tiles % 2 == 0 && tiles / 2 >= 256) ? 2 : 1;
+    int wn = (tiles % 2 == 0 && tiles / 2 >= (M <= 4 ? 256 : 168)) ? 2 : 1;
     // (from 9 rows: at 9 to 11 rows and N = 14336 the half-width CTAs took 6-10%
     // longer on packed weights, at 10 and 11 rows because their repeated quant
     // passes the 2^24 budget below and sends the shape to a K split)
-    if (M >= 9 && tiles % 4 == 0 && tiles / 4 >= 192) wn = 4;
+    if (M >= 9 && tiles % 4 == 0 && tiles / 4 >= 168) wn = 4;
+    // up to 4 rows the repeated quant is small, and the busiest compute unit's
+    // share of the column tiles sets the time: one tile a CTA where that cuts
+    // the share by a fifth or more (640 to 768 tiles: 3 against 4)
+    if (M <= 4 && wn == 2 && 5 * ((tiles + 255) / 256) <= 4 * (2 * ((tiles / 2 + 255) / 256))) wn = 1;
     if (const int v = tuning().decode_wn) {
         if (v >= 1 && v <= 4 && tiles % v == 0) wn = v;
     }

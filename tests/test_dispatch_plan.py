@@ -132,6 +132,15 @@ def test_wide_n_decode_streams_whole_rows(r9k, M, K, N):
         assert r9k.gemm_fp8_block_plan(M, K, N, packed) == (r9k.KERNEL_DECODE, 1), (M, K, N, packed)
 
 
+@pytest.mark.parametrize("M,K,N", [(12, 4096, 6144), (16, 4096, 6144), (12, 4096, 11008), (16, 4096, 11008),
+                                   (16, 2048, 6144)])
+def test_decode_wide_ctas_keep_whole_rows(r9k, M, K, N):
+    # from 5 rows two or four column tiles a CTA down to 168 CTAs: the CTAs repeat the activation quant
+    # fewer times, which keeps these shapes under the quant budget and off the K split
+    for packed in (False, True):
+        assert r9k.gemm_fp8_block_plan(M, K, N, packed) == (r9k.KERNEL_DECODE, 1), (M, K, N, packed)
+
+
 @pytest.mark.parametrize("M,K,N,kern", [(17, 4096, 14336, 1), (32, 2048, 14336, 1), (64, 512, 14336, 1),
                                         (32, 1024, 4096, 1), (17, 512, 1024, 1),
                                         (17, 4096, 2048, 4), (32, 4096, 2048, 4), (64, 2048, 2048, 4),
