@@ -221,6 +221,11 @@ Bf16aCfg bf16a_config(int64_t M, int64_t K, int64_t N) {
         const int wk = (int)(G / gs);
         int wn = 1;
         while (wn * 2 * wk <= 8 && tiles % (wn * 2) == 0 && (wide || tiles / (wn * 2) >= 256)) wn *= 2;
+        // up to 4 rows the busiest compute unit's share of the column tiles sets
+        // the time: one tile a CTA where that cuts the share by a fifth or more
+        // (576 to 768 tiles: 3 against 4; 1 to 4 rows 3.5-12% faster, at 8 rows,
+        // where every CTA stages more of A, 15-23% slower)
+        if (!wide && M <= 4 && wn == 2 && 5 * ((tiles + 255) / 256) <= 4 * (2 * ((tiles / 2 + 255) / 256))) wn = 1;
         return Bf16aCfg{wn, wk, gs};
     }
     return c;
