@@ -151,21 +151,21 @@ struct GemmRoute {
 // unit of the decode launch streams W weight bytes and re-quantises Q activation
 // values (every CTA quantises all of A); that of the mid-width launch reads B
 // bytes of codes, quantised once by a launch of its own.  Fitted over 112 shapes
-// (17 to 64 rows, K = 512 to 4096, N = 1024 to 28672, fused calls on fragment-order
-// weights in graphs, same box): decode 2.6 us + W / (35.4 KiB/us) + Q / (14.2
-// K values/us), mid-width 4.6 us + B / (39.2 KiB/us), each within about 0.4-0.7 us.
-// Taking the lower estimate loses 9.8 us summed over those shapes against the
-// faster kernel of each, where taking the decode kernel lost 89.6 us (32 x 4096 x
-// 2048: 7.4 against 12.4 us; 32 x 4096 x 28672: 25.4 against 35.1 us; the decode
-// kernel stays at N = 14336 and at short K).
+// (17 to 64 rows, K = 512 to 4096, N = 1024 to 28672, each kernel forced, fused
+// calls on fragment-order weights in graphs, same box): decode 2.6 us + W /
+// (36.2 KiB/us) + Q / (13.9 K values/us), mid-width 4.7 us + B / (38.6 KiB/us),
+// within about 0.4-0.7 us.  Taking the lower estimate loses 9.7 us summed over
+// those shapes against the faster kernel of each, where taking the decode kernel
+// always lost 91.6 us (32 x 4096 x 2048: 7.4 against 12.4 us; 32 x 4096 x 28672:
+// 25.4 against 35.1 us; the decode kernel keeps N = 14336 and short K).
 bool mid_beats_decode(const DecodeCfg &d, int64_t M, int64_t K, int64_t N) {
     const MidCfg m = mid_config(M, K, N);
     if (!m.mt || m.ksplit != 1) return false;
     const int64_t dctas = N / 16 / d.wn, mctas = (M + 16 * m.mt - 1) / (16 * m.mt) * (N / (16 * m.wn));
     const double dc = double((dctas + 255) / 256), mc = double((mctas + 255) / 256);
     const double W = dc * 16 * d.wn * K, Q = dc * M * K, B = mc * (16 * m.mt + 16 * m.wn) * K;
-    const double t_decode = 2.6 + W / (35.4 * 1024) + Q / (14.2 * 1024);
-    const double t_mid = 4.6 + B / (39.2 * 1024);
+    const double t_decode = 2.6 + W / (36.2 * 1024) + Q / (13.9 * 1024);
+    const double t_mid = 4.7 + B / (38.6 * 1024);
     return t_mid < t_decode;
 }
 

@@ -141,7 +141,7 @@ def test_decode_wide_ctas_keep_whole_rows(r9k, M, K, N):
         assert r9k.gemm_fp8_block_plan(M, K, N, packed) == (r9k.KERNEL_DECODE, 1), (M, K, N, packed)
 
 
-@pytest.mark.parametrize("M,K,N,kern", [(17, 4096, 14336, 1), (32, 2048, 14336, 1), (64, 512, 14336, 1),
+@pytest.mark.parametrize("M,K,N,kern", [(17, 4096, 14336, 1), (24, 2048, 14336, 1), (64, 512, 14336, 1),
                                         (32, 1024, 4096, 1), (17, 512, 1024, 1),
                                         (17, 4096, 2048, 4), (32, 4096, 2048, 4), (64, 2048, 2048, 4),
                                         (48, 1024, 4096, 4), (32, 4096, 28672, 4), (64, 2048, 28672, 4)])

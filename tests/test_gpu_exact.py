@@ -146,7 +146,7 @@ def edge_rows(M, K):
     return rows
 
 
-@pytest.mark.parametrize("M,K,N,kern", [(12, 1536, 2048, "decode"), (40, 1536, 3072, "decode"),
+@pytest.mark.parametrize("M,K,N,kern", [(12, 1536, 2048, "decode"), (40, 1536, 6144, "decode"),
                                         (16, 15360, 2048, "decode"), (16, 2048, 4096, "skinny")])
 def test_inload_quant_edge_groups(r9k, ora, M, K, N, kern):
     """Every in-load quant (the decode kernel's four lanes a group, with and without a K split, and the
