@@ -198,7 +198,12 @@ GemmRoute route_gemm(int64_t M, int64_t K, int64_t N, bool packed) {
     // to 255 rows at N = 6144 to 12288, 6-21% faster); with at most one such CTA a
     // unit the mid kernel is faster (N = 4096 up to 255 rows, N = 6144 and 8192 up
     // to 128 rows: 3-14%).
-    const bool tiled_faster = M > 64 && (K >= 8192 || ((M + 63) / 64) * (N / 64) > MID_ONE_WAVE_CTAS);
+    // (at long K only for weights past 2^24 bytes: narrower ones need the tiled
+    // engine to split K 8 to 32 ways, and the mid-width kernel was faster, 65 to 255
+    // rows at K = 8192, N = 1024 and 2048 by 8-27%, at K = 14336, N = 1024 by up to
+    // 11%; at K = 8192, N = 3072 and K = 14336, N = 2048 the tiled engine by 6-34%)
+    const bool tiled_faster =
+        M > 64 && ((K >= 8192 && N * K > (int64_t(1) << 24)) || ((M + 63) / 64) * (N / 64) > MID_ONE_WAVE_CTAS);
     if (mid != 0 && ((M >= 17 && !tiled_faster) || mid == 1)) {
         r.mc = mid_config(M, K, N);
         if (r.mc.mt) {

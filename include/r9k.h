@@ -157,8 +157,9 @@ int r9k_gemm_fp8_block(const uint8_t *aq, const float *as, int64_t M, int64_t K,
  *   once per call (a quant launch, then the GEMM launch): all of K per CTA,
  *   or up to 64 rows at K >= 8192 a K split whose fp32 partials a reduce
  *   launch sums in ascending split order; except above 64 rows where K >= 8192
- *   or where ceil(M / 64) * (N / 64) > 256 (its 64 x 64 blocks would need
- *   more than one CTA per compute unit), which take the tiled engine;
+ *   with N * K > 2^24, or where ceil(M / 64) * (N / 64) > 256 (its 64 x 64
+ *   blocks would need more than one CTA per compute unit), which take the
+ *   tiled engine;
  *   else the decode kernel with a K split (partials summed by a second launch);
  *   else, from 8 rows, the mid-width kernel with its K split; else the split-K
  *   skinny kernel (large K and N below 8 rows).

@@ -132,6 +132,15 @@ def test_wide_n_decode_streams_whole_rows(r9k, M, K, N):
         assert r9k.gemm_fp8_block_plan(M, K, N, packed) == (r9k.KERNEL_DECODE, 1), (M, K, N, packed)
 
 
+@pytest.mark.parametrize("M,K,N,kern", [(128, 8192, 2048, 4), (255, 8192, 1024, 4), (192, 14336, 1024, 4),
+                                        (128, 14336, 2048, 3), (128, 8192, 3072, 3), (255, 8192, 4096, 3)])
+def test_long_k_above_64_rows(r9k, M, K, N, kern):
+    # above 64 rows at K >= 8192 the tiled engine only for weights past 2^24 bytes; narrower weights would
+    # need its K split 8 to 32 ways, and the mid-width kernel streams them faster
+    for packed in (False, True):
+        assert r9k.gemm_fp8_block_plan(M, K, N, packed)[0] == kern, (M, K, N, packed)
+
+
 @pytest.mark.parametrize("M,K,N", [(12, 4096, 6144), (16, 4096, 6144), (12, 4096, 11008), (16, 4096, 11008),
                                    (16, 2048, 6144)])
 def test_decode_wide_ctas_keep_whole_rows(r9k, M, K, N):
