@@ -30,7 +30,7 @@ def r9k():
                                    (40, 2048, 4096), (48, 2048, 16384), (60, 4096, 4096), (64, 2048, 8192),
                                    (130, 1024, 4096), (128, 2048, 4096), (200, 1536, 4096), (255, 512, 4096),
                                    (100, 384, 4096), (70, 640, 1024), (255, 512, 256), (255, 768, 4096),
-                                   (48, 8192, 4096), (40, 14336, 2048), (64, 12288, 4096)])
+                                   (48, 8192, 4096), (40, 14336, 2048), (64, 12288, 4096), (130, 8192, 1024)])
 def test_mid_against_oracle(r9k, ora, M, K, N):
     plans = {r9k.gemm_fp8_block_plan(M, K, N, packed) for packed in (False, True)}
     assert len(plans) == 1
