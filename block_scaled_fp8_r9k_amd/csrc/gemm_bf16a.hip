@@ -196,7 +196,8 @@ static size_t bf16a_lds(int64_t M, int64_t K, const Bf16aCfg &c, bool *alds) {
 }
 
 // (wn, wk, gs): K-groups per wave preferably 8 (else 16, 4, 2, 1) in at most 8
-// slices, then tiles per CTA while at least 256 CTAs remain.  When a CTA's
+// slices, then tiles per CTA while at least 256 CTAs remain (up to 4 rows, one
+// tile a CTA where that evens out the compute units' shares).  When a CTA's
 // staged rows take more than 72 KiB only one CTA fits on a compute unit, so the
 // widest CTA is taken instead (16 groups a wave if that allows it): a single
 // round of CTAs (measured at M = 16, K = 4096, N = 14336).
