@@ -309,7 +309,14 @@ DecodeCfg decode_config(int64_t M, int64_t K, int64_t N, bool packed) {
         best = t;
         if ((tiles / wn) * wn * cand >= (packed ? 8 : 4) * 256 && (!packed || G / cand <= 8)) break;
     }
-    if (best.wn && ((tiles / best.wn) * M * K <= std::max<int64_t>(int64_t(1) << 24, N * K / 4) || force_wk))
+    // (a whole-K grid of fewer than 192 CTAs leaves compute units idle; where each
+    // CTA also re-quantises 12 x 8192 activation values or more, the K split below,
+    // which spreads the stream and divides the quant, was faster: N = 1024 and 2048
+    // at 12-16 rows and K = 8192, 8 rows and K = 14336-16384, 4-17%; with less
+    // quant a CTA it lost up to 22%, its reduce launch costing more than it saved)
+    const bool few_ctas = best.wn && tiles / best.wn < 192 && M * K >= 12 * 8192 && K >= 8192 && N >= 1024;
+    if (best.wn && (force_wk || (!few_ctas && (tiles / best.wn) * M * K <=
+                                                  std::max<int64_t>(int64_t(1) << 24, N * K / 4))))
         return best;
     // 2. a K split across CTAs
     const int wn2 = tiles % 4 == 0 && tiles / 4 >= 64 ? 4 : tiles % 2 == 0 && tiles / 2 >= 64 ? 2 : 1;

@@ -141,6 +141,16 @@ def test_long_k_above_64_rows(r9k, M, K, N, kern):
         assert r9k.gemm_fp8_block_plan(M, K, N, packed)[0] == kern, (M, K, N, packed)
 
 
+@pytest.mark.parametrize("M,K,N,split", [(8, 14336, 2048, True), (12, 8192, 1024, True), (6, 16384, 2048, True),
+                                         (4, 14336, 2048, False), (8, 8192, 2048, False), (16, 4096, 2048, False)])
+def test_decode_few_ctas_split_at_long_k(r9k, M, K, N, split):
+    # a whole-K grid of fewer than 192 CTAs at K >= 8192 takes the K split once each CTA would
+    # re-quantise 12 x 8192 activation values or more
+    for packed in (False, True):
+        kern, ks = r9k.gemm_fp8_block_plan(M, K, N, packed)
+        assert kern == r9k.KERNEL_DECODE and (ks > 1) == split, (M, K, N, packed, kern, ks)
+
+
 @pytest.mark.parametrize("M,K,N", [(12, 4096, 6144), (16, 4096, 6144), (12, 4096, 11008), (16, 4096, 11008),
                                    (16, 2048, 6144)])
 def test_decode_wide_ctas_keep_whole_rows(r9k, M, K, N):
