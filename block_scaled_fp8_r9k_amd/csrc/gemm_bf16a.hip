@@ -196,8 +196,8 @@ static size_t bf16a_lds(int64_t M, int64_t K, const Bf16aCfg &c, bool *alds) {
 }
 
 // (wn, wk, gs): K-groups per wave preferably 8 (else 16, 4, 2, 1) in at most 8
-// slices, then tiles per CTA while at least 256 CTAs remain (up to 4 rows, one
-// tile a CTA where that evens out the compute units' shares).  When a CTA's
+// slices, then tiles per CTA while at least 256 CTAs remain (168 from 5 rows on;
+// up to 4 rows, one tile a CTA where that evens out the compute units' shares).  When a CTA's
 // staged rows take more than 72 KiB only one CTA fits on a compute unit, so the
 // widest CTA is taken instead (16 groups a wave if that allows it): a single
 // round of CTAs (measured at M = 16, K = 4096, N = 14336).
@@ -221,7 +221,10 @@ Bf16aCfg bf16a_config(int64_t M, int64_t K, int64_t N) {
         if (G % gs || G / gs > 8) continue;
         const int wk = (int)(G / gs);
         int wn = 1;
-        while (wn * 2 * wk <= 8 && tiles % (wn * 2) == 0 && (wide || tiles / (wn * 2) >= 256)) wn *= 2;
+        // (from 5 rows each CTA stages more of A, and wider CTAs pay down to 168:
+        // 5-8 rows at N = 5376-8064, K = 2048 and 4096, 5-26% faster than one tile a CTA)
+        const int64_t min_ctas = M > 4 ? 168 : 256;
+        while (wn * 2 * wk <= 8 && tiles % (wn * 2) == 0 && (wide || tiles / (wn * 2) >= min_ctas)) wn *= 2;
         // up to 4 rows the busiest compute unit's share of the column tiles sets
         // the time: one tile a CTA where that cuts the share by a fifth or more
         // (576 to 768 tiles: 3 against 4; 1 to 4 rows 3.5-12% faster, at 8 rows,

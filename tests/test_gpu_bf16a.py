@@ -46,7 +46,9 @@ def _weights(ora, r9k, N, K, seed):
                                    (16, 4096, 14336), (5, 14336, 4096), (16, 14336, 4096), (3, 7168, 1024),
                                    (1, 128, 128), (7, 384, 256), (13, 640, 384), (9, 1280, 512), (16, 2048, 2048),
                                    # long staged rows whose K/1024 does not divide sixteen (three slices)
-                                   (16, 3072, 4096), (12, 3072, 4096), (16, 6144, 2048)])
+                                   (16, 3072, 4096), (12, 3072, 4096), (16, 6144, 2048),
+                                   # from 5 rows two tiles a CTA down to 168 CTAs
+                                   (8, 2048, 6144), (6, 4096, 5376)])
 def test_bf16a_against_oracle(r9k, ora, M, K, N):
     say("bf16a", M, K, N)
     a = inputs.activations(M + K // 128, M, K, outliers=True)
