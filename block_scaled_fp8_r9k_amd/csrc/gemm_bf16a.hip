@@ -214,8 +214,16 @@ Bf16aCfg bf16a_config(int64_t M, int64_t K, int64_t N) {
     // runs the slices side by side (measured at M = 16, K = 4096, N = 14336)
     // (taken only where the slice count divides sixteen and the CTA's column
     // tiles divide N's, so that the grid covers every column)
-    if (wide && !force && G % 8 == 0 && 16 % (G / 8) == 0 && tiles % (16 / (G / 8)) == 0)
-        return Bf16aCfg{(int)(16 / (G / 8)), (int)(G / 8), 8};
+    if (wide && !force && G % 8 == 0 && 16 % (G / 8) == 0 && tiles % (16 / (G / 8)) == 0) {
+        const int wn16 = (int)(16 / (G / 8));
+        // (where that leaves fewer than 168 CTAs, eight waves of half the column
+        // tiles, twice the CTAs, as long as they still run in one round of one CTA
+        // a compute unit: 6-16 rows at K = 4096 and 8192, N = 2048-8192, 12-42%
+        // faster; at N = 10240, K = 4096 the 320 CTAs of two rounds were up to
+        // 26% slower, and from 168 CTAs the sixteen-wave CTAs won by up to 27%)
+        if (tiles / wn16 < 168 && wn16 >= 2 && tiles / (wn16 / 2) <= 256) return Bf16aCfg{wn16 / 2, (int)(G / 8), 8};
+        return Bf16aCfg{wn16, (int)(G / 8), 8};
+    }
     for (int gs : wide ? pref_wide : pref) {
         if (force && gs != force) continue;
         if (G % gs || G / gs > 8) continue;

@@ -48,7 +48,9 @@ def _weights(ora, r9k, N, K, seed):
                                    # long staged rows whose K/1024 does not divide sixteen (three slices)
                                    (16, 3072, 4096), (12, 3072, 4096), (16, 6144, 2048),
                                    # from 5 rows two tiles a CTA down to 168 CTAs
-                                   (8, 2048, 6144), (6, 4096, 5376)])
+                                   (8, 2048, 6144), (6, 4096, 5376),
+                                   # wide rows with few sixteen-wave CTAs: eight waves of half the tiles
+                                   (9, 4096, 4096), (16, 8192, 2048)])
 def test_bf16a_against_oracle(r9k, ora, M, K, N):
     say("bf16a", M, K, N)
     a = inputs.activations(M + K // 128, M, K, outliers=True)
