@@ -111,6 +111,34 @@ def test_workspace_covers_partials(r9k, M, K, N):
             assert ws >= M * K + 4 * M * (K // 128), (M, K, N, packed, ws)
 
 
+def test_random_shapes_plan_valid_splits(r9k):
+    """Seeded random shapes (1-600 rows, K up to 32768, N up to 65536) through every planner: the plan
+    query succeeds on both layouts, a K split fits K/128, and the workspace the library asks for holds
+    the split's fp32 partials and, for the kernels that read codes quantised once a call, the codes and
+    scales."""
+    import numpy as np
+    g = np.random.default_rng(11)
+    for _ in range(3000):
+        M = int(g.integers(1, 601))
+        K = 128 * int(g.choice([g.integers(1, 33), g.integers(33, 257)]))
+        N = 128 * int(g.choice([g.integers(1, 65), g.integers(65, 513)]))
+        ws = r9k.gemm_fp8_block_workspace(M, K, N)
+        for packed in (False, True):
+            kern, ks = r9k.gemm_fp8_block_plan(M, K, N, packed)
+            assert kern in (r9k.KERNEL_DECODE, r9k.KERNEL_SKINNY, r9k.KERNEL_TILED, r9k.KERNEL_MID), (M, K, N)
+            # the tiled kernel hands split s the groups [s G / S, (s + 1) G / S), so any S up to G
+            # will do; the other kernels' splits take equal K ranges
+            assert 1 <= ks <= K // 128, (M, K, N, packed, kern, ks)
+            if kern != r9k.KERNEL_TILED:
+                assert (K // 128) % ks == 0, (M, K, N, packed, kern, ks)
+            if M > 255:
+                assert kern == r9k.KERNEL_TILED, (M, K, N, packed, kern)
+            if ks > 1:
+                assert ws >= 4 * ks * M * N, (M, K, N, packed, kern, ks, ws)
+            if kern in (r9k.KERNEL_MID, r9k.KERNEL_TILED):
+                assert ws >= M * K + 4 * M * (K // 128), (M, K, N, packed, ws)
+
+
 def test_plan_argument_checks(r9k):
     L = r9k.lib()
     from ctypes import byref, c_int
