@@ -234,7 +234,12 @@ def bench_decode(torch, r9k, inputs, dev, steps, warmup, packed=True):
     for M in DECODE_M:
         reps_per_graph = 2 * C
         g = capture(torch, [call(M, i % C) for i in range(reps_per_graph)])
-        tm.run(lambda i: g.replay(), 2)
+        # replays of this graph alone for DECODE_WARM_S first: right after the step loop the first
+        # width's launches run about 5% slow for several milliseconds (the kernel trace of the same
+        # run shows them steady and fastest at M = 1), which two replays did not cover
+        t_end = time.perf_counter() + DECODE_WARM_S
+        while time.perf_counter() < t_end:
+            tm.run(lambda i: g.replay(), 2)
         ms, tr = median_of_trials(lambda: tm.run(lambda i: g.replay(), max(3, steps // 4)) / reps_per_graph)
         b = gemm_bytes(M, K, N)
         per_m[M] = dict(us=ms * 1e3, GBs=b / (ms * 1e-3) / 1e9, trials_us=[t * 1e3 for t in tr])
@@ -296,6 +301,7 @@ def cpu_baseline(ora, a_bits, w_bits, step_bytes):
                        f"median of {len(times)}")
 
 
+DECODE_WARM_S = 0.05  # seconds of one width's graph replays before its timed trials
 PREFILL_WARM_S = 0.1  # seconds of alternating prefill launches before the timed trials
 
 
