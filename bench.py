@@ -90,6 +90,15 @@ class Timer:
         return s.elapsed_time(e) / reps  # ms
 
 
+def warm_graph(tm, g):
+    """Replays of one graph alone for GRAPH_WARM_S before its timed trials: right after a heavy phase
+    (the decode step loop) the next launches run about 5% slow for several milliseconds, which the kernel
+    trace of the same run does not show and a couple of replays did not cover."""
+    t_end = time.perf_counter() + GRAPH_WARM_S
+    while time.perf_counter() < t_end:
+        tm.run(lambda i: g.replay(), 2)
+
+
 def median_of_trials(run_once, n=TRIALS):
     """Median of n timed trials (run_once() -> ms) and the trials themselves."""
     t = [run_once() for _ in range(n)]
@@ -234,12 +243,7 @@ def bench_decode(torch, r9k, inputs, dev, steps, warmup, packed=True):
     for M in DECODE_M:
         reps_per_graph = 2 * C
         g = capture(torch, [call(M, i % C) for i in range(reps_per_graph)])
-        # replays of this graph alone for DECODE_WARM_S first: right after the step loop the first
-        # width's launches run about 5% slow for several milliseconds (the kernel trace of the same
-        # run shows them steady and fastest at M = 1), which two replays did not cover
-        t_end = time.perf_counter() + DECODE_WARM_S
-        while time.perf_counter() < t_end:
-            tm.run(lambda i: g.replay(), 2)
+        warm_graph(tm, g)
         ms, tr = median_of_trials(lambda: tm.run(lambda i: g.replay(), max(3, steps // 4)) / reps_per_graph)
         b = gemm_bytes(M, K, N)
         per_m[M] = dict(us=ms * 1e3, GBs=b / (ms * 1e-3) / 1e9, trials_us=[t * 1e3 for t in tr])
@@ -270,7 +274,7 @@ def bench_bf16a(torch, r9k, inputs, dev, reps):
             f()
         g = capture(torch, calls)
         tm = Timer(torch)
-        tm.run(lambda i: g.replay(), 2)
+        warm_graph(tm, g)
         ms, tr = median_of_trials(lambda: tm.run(lambda i: g.replay(), reps) / len(calls))
         res[str(M)] = dict(us=ms * 1e3, GBs=gemm_bytes(M, K, N) / (ms * 1e-3) / 1e9, trials_us=[t * 1e3 for t in tr])
         log(f"bf16a M={M}: {ms * 1e3:.2f} us/launch, {res[str(M)]['GBs']:.0f} GB/s")
@@ -301,7 +305,7 @@ def cpu_baseline(ora, a_bits, w_bits, step_bytes):
                        f"median of {len(times)}")
 
 
-DECODE_WARM_S = 0.05  # seconds of one width's graph replays before its timed trials
+GRAPH_WARM_S = 0.05  # seconds of one graph's replays before its timed trials (all legs but prefill)
 PREFILL_WARM_S = 0.1  # seconds of alternating prefill launches before the timed trials
 
 
@@ -385,7 +389,7 @@ def bench_mid(torch, r9k, inputs, dev, reps, points=MID_POINTS):
                 f()
             g = capture(torch, calls)
             tm = Timer(torch)
-            tm.run(lambda i: g.replay(), 1)
+            warm_graph(tm, g)
             ms, tr = median_of_trials(lambda: tm.run(lambda i: g.replay(), reps) / C)
             gbs = gemm_bytes(M, K, N) / (ms * 1e-3) / 1e9
             tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
@@ -423,7 +427,7 @@ def bench_moe(torch, r9k, inputs, dev, reps):
     rcalls = [lambda: r9k.moe_route(logits_d, k, ids=ids_d, w=tw_d)] * 20
     g = capture(torch, rcalls)
     tm = Timer(torch)
-    tm.run(lambda i: g.replay(), 1)
+    warm_graph(tm, g)
     ms, tr = median_of_trials(lambda: tm.run(lambda i: g.replay(), reps) / len(rcalls))
     res["route"] = dict(us=ms * 1e3, T=T, E=E, topk=k, trials_us=[t * 1e3 for t in tr])
     log(f"moe route T={T} E={E} top-{k}: {res['route']['us']:.2f} us")
@@ -436,7 +440,7 @@ def bench_moe(torch, r9k, inputs, dev, reps):
             f()
         g = capture(torch, calls)
         tm = Timer(torch)
-        tm.run(lambda i: g.replay(), 1)
+        warm_graph(tm, g)
         ms, tr = median_of_trials(lambda: tm.run(lambda i: g.replay(), reps) / len(sets))
         gbs = nbytes / (ms * 1e-3) / 1e9
         log(f"moe fused={fused}: {ms * 1e3:.1f} us, {gbs:.0f} GB/s over {touched} touched experts")
@@ -451,7 +455,7 @@ def bench_moe(torch, r9k, inputs, dev, reps):
         f()
     g = capture(torch, calls)
     tm = Timer(torch)
-    tm.run(lambda i: g.replay(), 1)
+    warm_graph(tm, g)
     ms, tr = median_of_trials(lambda: tm.run(lambda i: g.replay(), reps) / len(sets))
     res["fused_shared"] = dict(us=ms * 1e3, GBs=nbytes / (ms * 1e-3) / 1e9, trials_us=[t * 1e3 for t in tr])
     log(f"moe fused with the shared expert's term: {ms * 1e3:.1f} us")
@@ -474,7 +478,7 @@ def bench_single_token(torch, r9k, inputs, dev, reps):
     calls = [one] * 50
     g = capture(torch, calls)
     tm = Timer(torch)
-    tm.run(lambda i: g.replay(), 2)
+    warm_graph(tm, g)
     ms, tr = median_of_trials(lambda: tm.run(lambda i: g.replay(), reps) / len(calls))
     ems, etr = median_of_trials(lambda: tm.run(lambda i: one(), 200))
     log(f"single token {M}x{K}x{N}: {ms * 1e3:.2f} us a call in a graph, {ems * 1e3:.2f} us eager")
@@ -574,7 +578,7 @@ def hbm_read_ceiling(torch, reps, nbytes=DECODE_K * DECODE_N):
             f()
         g = capture(torch, calls)
         tm = Timer(torch)
-        tm.run(lambda i: g.replay(), 2)
+        warm_graph(tm, g)
         ms, tr = median_of_trials(lambda: tm.run(lambda i: g.replay(), reps) / len(calls))
         res[name] = dict(us=ms * 1e3, GBs=nbytes / (ms * 1e-3) / 1e9, trials_us=[t * 1e3 for t in tr])
         log(f"plain read of {nbytes / 1e6:.1f} MB ({name}): {ms * 1e3:.2f} us, {res[name]['GBs']:.0f} GB/s")
