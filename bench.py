@@ -487,7 +487,7 @@ def bench_single_token(torch, r9k, inputs, dev, reps):
                 kernel=KERNEL_NAMES.get(r9k.gemm_fp8_block_plan(M, K, N)[0]))
 
 
-# ---- the oracle beside each leg (CPU, the machine's host cores) ----
+# ---- the oracle beside each leg (CPU, the host's cores) ----
 
 def cpu_prefill(ora, inputs, rows=512):
     M, K, N = 4096, 4096, 12288

@@ -152,7 +152,7 @@ struct GemmRoute {
 // values (every CTA quantises all of A); that of the mid-width launch reads B
 // bytes of codes, quantised once by a launch of its own.  Fitted over 112 shapes
 // (17 to 64 rows, K = 512 to 4096, N = 1024 to 28672, each kernel forced, fused
-// calls on fragment-order weights in graphs, same box): decode 2.6 us + W /
+// calls on fragment-order weights in graphs, one GPU): decode 2.6 us + W /
 // (36.2 KiB/us) + Q / (13.9 K values/us), mid-width 4.7 us + B / (38.6 KiB/us),
 // within about 0.4-0.7 us.  Taking the lower estimate loses 9.7 us summed over
 // those shapes against the faster kernel of each, where taking the decode kernel

@@ -249,7 +249,7 @@ static bool mid_fits(int64_t M, int64_t K, int64_t N, const MidCfg &c) {
 // the fewest CTAs that still give 256, ran 448 CTAs of 32 x 32 at 32 x 4096 x
 // 14336, two on most units, where 224 of 32 x 64 move a quarter fewer bytes a
 // unit: 15.2 against 18.2 us; over 17 such shapes at K = 4096, N = 2048-14336
-// and 24-192 rows, 8-29% faster, same box.)
+// and 24-192 rows, 8-29% faster, one GPU, interleaved runs.)
 MidCfg mid_config(int64_t M, int64_t K, int64_t N) {
     MidCfg c{0, 0, 0, 0, 1};
     if (M < 1 || M > 256 || N % 16) return c;
